@@ -1,0 +1,233 @@
+"""Seeded synthetic inputs for the KDA mixer.
+
+This module draws inputs and nothing else.  It holds none of the mixer's
+arithmetic, so both the HIP path and the CPU oracle may consume what it
+produces.  It imports neither of them.
+
+Distributions, following the workloads the mixer is measured on:
+  * raw q, k, v          N(0, 1)
+  * decay alpha          exp(-softplus(a)), a ~ N(0, 1), one per key channel
+  * write strength beta  sigmoid(b), b ~ N(0, 1), one per head
+  * output gate g        N(0, 1), one per value channel
+  * conv weights         N(0, 0.5) (second argument = standard deviation)
+  * initial state        N(0, 0.1) where a workload starts from a random state
+  * conv history         N(0, 1)   where a workload starts mid-sequence
+
+Draws are fp64 from numpy's PCG64 and are then rounded to the activation
+dtype: float32 (round to nearest even), or bfloat16 (round to float32, then
+to nearest even on the upper 16 bits).  Conv and norm weights stay float32.
+Every array here holds values that are exact in its dtype, stored as float32
+(bfloat16 values are float32 values with 16 zero low bits); ``bf16_bits``
+gives the 16-bit patterns the device buffers hold.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+ACT_DTYPES = ("f32", "bf16")
+STATE_DTYPES = ("f32", "bf16")
+
+
+def round_f32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 of the float32 rounding of x, as float32 values."""
+    u = round_f32(x).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return (u.astype(np.uint32) << 16).view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return round_f32(x)
+    if dtype == "bf16":
+        return round_bf16(x)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float32 arrays that hold bfloat16 values."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    if np.any(u & 0xFFFF):
+        raise ValueError("array holds values that are not bfloat16")
+    return (u >> 16).astype(np.uint16)
+
+
+def _softplus(a: np.ndarray) -> np.ndarray:
+    return np.logaddexp(0.0, a)
+
+
+def _sigmoid(b: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-b))
+
+
+@dataclass
+class Weights:
+    """Per-layer parameters: depthwise conv taps and the norm weight."""
+    conv_q: np.ndarray  # [H, dk, W] float32
+    conv_k: np.ndarray  # [H, dk, W] float32
+    conv_v: np.ndarray  # [H, dv, W] float32
+    norm_w: np.ndarray  # [dv] float32
+
+
+@dataclass
+class TokenInputs:
+    """Per-token mixer inputs; leading dims are whatever the caller asked."""
+    q: np.ndarray      # [..., H, dk]
+    k: np.ndarray      # [..., H, dk]
+    v: np.ndarray      # [..., H, dv]
+    alpha: np.ndarray  # [..., H, dk]
+    beta: np.ndarray   # [..., H]
+    g: np.ndarray      # [..., H, dv]
+
+
+@dataclass
+class Case:
+    """One workload: shapes, weights, starting state and the token stream."""
+    name: str
+    mode: str               # "decode" | "verify" | "prefill"
+    H: int
+    dk: int
+    dv: int
+    width: int
+    act: str
+    state: str
+    weights: Weights
+    batch: int
+    S0: np.ndarray          # [batch, H, dk, dv] logical, exact in `state`
+    hist0: np.ndarray       # [batch, width-1, H, 2dk+dv] raw, oldest first
+    pos0: np.ndarray        # [batch] int64 tokens already consumed
+    steps: int = 0          # decode
+    n_draft: int = 0        # verify
+    tokens: TokenInputs | None = None  # decode [steps,B,...]; verify [B,n,...]
+    active: np.ndarray | None = None   # decode [steps, B] bool
+    accepted: np.ndarray | None = None  # verify [B] int32
+    lens: list = field(default_factory=list)   # prefill lengths
+    cu_seqlens: np.ndarray | None = None       # prefill [B+1] int32
+    chunk: int = 64
+    slice_seq: int = -1    # prefill: sequence and start of the checked slice
+    slice_start: int = -1
+    slice_len: int = 0
+
+
+def _weights(rng, H, dk, dv, W):
+    cq = round_f32(rng.normal(0.0, 0.5, size=(H, dk, W)))
+    ck = round_f32(rng.normal(0.0, 0.5, size=(H, dk, W)))
+    cv = round_f32(rng.normal(0.0, 0.5, size=(H, dv, W)))
+    return Weights(cq, ck, cv, np.ones(dv, dtype=np.float32))
+
+
+def _tokens(rng, lead, H, dk, dv, act) -> TokenInputs:
+    q = round_to(rng.standard_normal(lead + (H, dk)), act)
+    k = round_to(rng.standard_normal(lead + (H, dk)), act)
+    v = round_to(rng.standard_normal(lead + (H, dv)), act)
+    alpha = round_to(np.exp(-_softplus(rng.standard_normal(lead + (H, dk)))), act)
+    beta = round_to(_sigmoid(rng.standard_normal(lead + (H,))), act)
+    g = round_to(rng.standard_normal(lead + (H, dv)), act)
+    return TokenInputs(q, k, v, alpha, beta, g)
+
+
+def _start(rng, B, H, dk, dv, W, act, state, init):
+    C = 2 * dk + dv
+    if init == "zero":
+        S0 = np.zeros((B, H, dk, dv), dtype=np.float32)
+        hist0 = np.zeros((B, W - 1, H, C), dtype=np.float32)
+        pos0 = np.zeros(B, dtype=np.int64)
+    elif init == "random":
+        S0 = round_to(rng.normal(0.0, 0.1, size=(B, H, dk, dv)), state)
+        hist0 = round_to(rng.standard_normal((B, W - 1, H, C)), act)
+        pos0 = (W - 1) + (np.arange(B, dtype=np.int64) % 4)
+    else:
+        raise ValueError(init)
+    return S0, hist0, pos0
+
+
+def make_decode(seed, *, B, H, dk, dv, steps, act, state, init,
+                active_per_step=None, width=4, name="decode", norm_w=None):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = _weights(rng, H, dk, dv, width)
+    if norm_w is not None:
+        w.norm_w = round_f32(norm_w)
+    S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
+    toks = _tokens(rng, (steps, B), H, dk, dv, act)
+    active = np.ones((steps, B), dtype=bool)
+    if active_per_step is not None:
+        active[:] = False
+        for s in range(steps):
+            active[s, rng.permutation(B)[:active_per_step]] = True
+    return Case(name=name, mode="decode", H=H, dk=dk, dv=dv, width=width,
+                act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
+                pos0=pos0, steps=steps, tokens=toks, active=active)
+
+
+def make_verify(seed, *, B, H, dk, dv, n_draft, act, state, init, width=4,
+                name="verify"):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = _weights(rng, H, dk, dv, width)
+    S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
+    toks = _tokens(rng, (B, n_draft), H, dk, dv, act)
+    accepted = rng.integers(0, n_draft + 1, size=B).astype(np.int32)
+    return Case(name=name, mode="verify", H=H, dk=dk, dv=dv, width=width,
+                act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
+                pos0=pos0, n_draft=n_draft, tokens=toks, accepted=accepted)
+
+
+def make_prefill(seed, *, lens, H, dk, dv, act, state, init="zero", width=4,
+                 chunk=64, slice_len=512, name="prefill"):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w = _weights(rng, H, dk, dv, width)
+    B = len(lens)
+    S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
+    total = int(sum(lens))
+    toks = _tokens(rng, (total,), H, dk, dv, act)
+    cu = np.zeros(B + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    # a slice of consecutive outputs to check at full size
+    fits = [i for i, n in enumerate(lens) if n >= slice_len]
+    if fits:
+        s = int(fits[rng.integers(0, len(fits))])
+        start = int(rng.integers(0, lens[s] - slice_len + 1))
+    else:
+        s, start, slice_len = 0, 0, int(lens[0])
+    return Case(name=name, mode="prefill", H=H, dk=dk, dv=dv, width=width,
+                act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
+                pos0=pos0, tokens=toks, lens=list(lens), cu_seqlens=cu,
+                chunk=chunk, slice_seq=s, slice_start=start,
+                slice_len=slice_len)
+
+
+# The five measured workloads.  The seed of each is its index.
+CONFIG_NAMES = {
+    0: "tiny_decode_B1_H4_d64_fp32",
+    1: "batched_decode_B64_H32_d128_bf16act_f32state",
+    2: "spec_verify_B16_H32_d128_n4_f32state",
+    3: "large_batch_decode_B256_active192_H32_d128_bf16state",
+    4: "chunked_prefill_lens8192_4096_2048_1024_H32_d128_C64",
+}
+
+
+def config(i: int) -> Case:
+    if i == 0:
+        return make_decode(0, B=1, H=4, dk=64, dv=64, steps=16, act="f32",
+                           state="f32", init="zero", name=CONFIG_NAMES[0])
+    if i == 1:
+        return make_decode(1, B=64, H=32, dk=128, dv=128, steps=32,
+                           act="bf16", state="f32", init="random",
+                           name=CONFIG_NAMES[1])
+    if i == 2:
+        return make_verify(2, B=16, H=32, dk=128, dv=128, n_draft=4,
+                           act="bf16", state="f32", init="random",
+                           name=CONFIG_NAMES[2])
+    if i == 3:
+        return make_decode(3, B=256, H=32, dk=128, dv=128, steps=16,
+                           act="bf16", state="bf16", init="random",
+                           active_per_step=192, name=CONFIG_NAMES[3])
+    if i == 4:
+        return make_prefill(4, lens=[8192, 4096, 2048, 1024], H=32, dk=128,
+                            dv=128, act="bf16", state="f32", init="zero",
+                            chunk=64, name=CONFIG_NAMES[4])
+    raise ValueError(f"no config {i}")
