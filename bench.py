@@ -1,0 +1,317 @@
+"""Benchmark of the KDA mixer on one MI355X.
+
+The timed step is one batched decode call (conv, L2 norms, decay, delta-rule
+write, read-out, gated RMSNorm and the typed state store) over the
+batched-decode workload: 64 sequences x 32 heads, dk = dv = 128, bf16
+activations, FP32 state (64 KiB per head).  Eight independent state pools
+("layers") are rotated so the working set (1 GiB) is far larger than the
+256 MB Infinity Cache and every step streams its state from HBM.
+
+Printed: one JSON line with the throughput (token-head state updates per
+second), the roofline of the decode kernel (algorithmic bytes per launch over
+its average launch time, HIP events on the launch stream), the CPU oracle's
+throughput on a bounded sample of the same workload, and the same figures for
+the other modes (large-batch BF16-state decode, speculative verify + commit).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--layers", type=int, default=8,
+                    help="state pools rotated to defeat the Infinity Cache")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-modes", action="store_true",
+                    help="time only the headline decode workload")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------ byte models
+# Algorithmic bytes: every tensor the step must touch, counted once.
+
+def decode_bytes_per_th(dk, dv, act_b, state_b):
+    C = 2 * dk + dv
+    return (2 * dk * dv * state_b          # state read + write
+            + C * act_b                    # raw q, k, v
+            + dk * act_b + act_b           # alpha, beta
+            + dv * act_b                   # g
+            + 3 * C * act_b                # conv history read (3 ring entries)
+            + C * act_b                    # new ring entry
+            + dv * 4)                      # y (FP32)
+
+
+def per_call_bytes(H, dk, dv, rows):
+    return H * (2 * dk + dv) * 4 * 4 + dv * 4 + rows * 8   # conv taps, norm_w, ids
+
+
+def verify_bytes_per_head(n, dk, dv, act_b, state_b):
+    C = 2 * dk + dv
+    return (dk * dv * state_b              # state read
+            + n * dk * dv * 4              # FP32 records
+            + n * (C + dk + 1 + dv) * act_b  # q, k, v, alpha, beta, g
+            + 3 * C * act_b                # conv history
+            + n * C * act_b                # raw drafts kept
+            + n * dv * 4)                  # y
+
+
+# ------------------------------------------------------------ helpers
+
+def timed_loop(torch, launch, K, W):
+    """W warm-up launches, then K timed launches bracketed by synchronize.
+    Returns (total seconds, mean per-launch kernel seconds)."""
+    for i in range(W):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(K):
+        ev[i][0].record()
+        launch(W + i)
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total = t0.elapsed_time(t1) / 1e3
+    per = [a.elapsed_time(b) / 1e3 for a, b in ev]
+    return total, float(np.mean(per)), float(np.median(per)), wall
+
+
+def rel_err(got, ref):
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+# ------------------------------------------------------------ decode
+
+def run_decode_mode(torch, case, K, W, layers):
+    from hybrid_linear_attention_rule_amd import device as dev
+    from hybrid_linear_attention_rule_amd import kda
+    import oracle
+
+    pools = [dev.make_state(case, spare_slots=0, fill_nan=False) for _ in range(layers)]
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    B, H, dk, dv, S = case.batch, case.H, case.dk, case.dv, case.steps
+    y = torch.empty((B, H, dv), device="cuda")
+    slot_steps = [torch.from_numpy(np.where(case.active[s], pools[0].slots, -1)
+                                   .astype(np.int32)).cuda() for s in range(S)]
+    pos = np.zeros((S, B), dtype=np.int64)
+    pos[0] = case.pos0
+    for s in range(1, S):
+        pos[s] = pos[s - 1] + case.active[s - 1]
+    pos_steps = [torch.from_numpy(pos[s].astype(np.int32)).cuda() for s in range(S)]
+    ds0 = pools[0]
+
+    def launch(i):
+        layer = i % layers
+        s = (i // layers) % S
+        d = pools[layer]
+        kda.decode(d.shape, d.params, slot_steps[s], pos_steps[s], tok["q"][s],
+                   tok["k"][s], tok["v"][s], tok["alpha"][s], tok["beta"][s],
+                   tok["g"][s], d.pool, d.ring, y)
+
+    # parity of the first step on layer 0 before any timing
+    launch(0)
+    torch.cuda.synchronize()
+    y_ref, S_ref, _ = oracle.decode_case(case, steps=1)
+    act0 = case.active[0]
+    tol = 2e-5 if case.state == "f32" else 1e-2
+    e_y = rel_err(y.cpu().numpy()[act0], y_ref[0][act0])
+    e_s = rel_err(dev.read_states(ds0)[act0], S_ref[act0])
+    assert e_y <= tol and e_s <= tol, f"parity failed before timing: {e_y} {e_s}"
+    # restore layer 0 so that every layer starts from the same state
+    pools[0] = dev.make_state(case, spare_slots=0, fill_nan=False)
+
+    total, mean_k, med_k, wall = timed_loop(torch, launch, K, W)
+    act_b = 2 if case.act == "bf16" else 4
+    st_b = 2 if case.state == "bf16" else 4
+    n_active = int(case.active.sum(axis=1).mean())
+    th_per_step = n_active * H
+    bytes_launch = th_per_step * decode_bytes_per_th(dk, dv, act_b, st_b) + \
+        per_call_bytes(H, dk, dv, B)
+    return dict(
+        workload=case.name, rows=B, active_rows=n_active, heads=H, dk=dk, dv=dv,
+        act=case.act, state=case.state, layers=layers, steps=K, warmup=W,
+        ms_per_step=total / K * 1e3, kernel_us=mean_k * 1e6, kernel_us_median=med_k * 1e6,
+        th_per_s=th_per_step * K / total, bytes_per_launch=bytes_launch,
+        hbm_gbs=bytes_launch / mean_k / 1e9,
+        hbm_frac=bytes_launch / mean_k / 1e9 / HBM_PEAK_GBS,
+        parity_rel_err={"y": e_y, "state": e_s}, wall_s=wall)
+
+
+# ------------------------------------------------------------ verify
+
+def run_verify_mode(torch, case, K, W, layers):
+    from hybrid_linear_attention_rule_amd import device as dev
+    from hybrid_linear_attention_rule_amd import kda
+    import oracle
+
+    pools = [dev.make_state(case, spare_slots=0, fill_nan=False) for _ in range(layers)]
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    B, n, H, dk, dv = case.batch, case.n_draft, case.H, case.dk, case.dv
+    C = 2 * dk + dv
+    recs = [torch.empty((B, n, H, dv, dk), device="cuda") for _ in range(2)]
+    dconv = torch.empty((B, n, H, C), device="cuda", dtype=pools[0].shape.act_dtype)
+    y = torch.empty((B, n, H, dv), device="cuda")
+    slot_t = pools[0].slot_ids
+    pos_t = torch.from_numpy(case.pos0.astype(np.int32)).cuda()
+    acc_t = torch.from_numpy(case.accepted.astype(np.int32)).cuda()
+
+    def verify(i):
+        d = pools[i % layers]
+        kda.verify(d.shape, d.params, slot_t, pos_t, tok["q"], tok["k"], tok["v"],
+                   tok["alpha"], tok["beta"], tok["g"], d.pool, d.ring, recs[i % 2],
+                   dconv, y)
+
+    verify(0)
+    torch.cuda.synchronize()
+    y_ref, rec_ref, _, _ = oracle.verify_case(case)
+    e_y = rel_err(y.cpu().numpy(), y_ref)
+    e_r = rel_err(np.swapaxes(recs[0].cpu().numpy(), 3, 4), rec_ref)
+    assert e_y <= 2e-5 and e_r <= 2e-5, f"verify parity failed: {e_y} {e_r}"
+    total, mean_k, med_k, _ = timed_loop(torch, verify, K, W)
+    act_b = 2 if case.act == "bf16" else 4
+    st_b = 2 if case.state == "bf16" else 4
+    per_head = verify_bytes_per_head(n, dk, dv, act_b, st_b)
+    bytes_launch = B * H * per_head + per_call_bytes(H, dk, dv, B)
+
+    # commit: copies record m-1 of rows with m >= 1 (m = accepted)
+    def commit(i):
+        d = pools[i % layers]
+        kda.commit_accepted(d.shape, slot_t, pos_t, acc_t, recs[0], dconv, d.pool,
+                            d.ring)
+    c_total, c_mean, _, _ = timed_loop(torch, commit, K, W)
+    m = case.accepted
+    commit_bytes = int((m > 0).sum()) * H * (dk * dv * 4 + dk * dv * st_b) + \
+        int(np.minimum(m, 4).sum()) * H * 2 * C * act_b
+    return dict(
+        workload=case.name, rows=B, heads=H, n_draft=n, state=case.state,
+        verify_kernel_us=mean_k * 1e6, verify_ms_per_call=total / K * 1e3,
+        th_per_s=B * H * n * K / total, bytes_per_launch=bytes_launch,
+        hbm_gbs=bytes_launch / mean_k / 1e9,
+        hbm_frac=bytes_launch / mean_k / 1e9 / HBM_PEAK_GBS,
+        commit_kernel_us=c_mean * 1e6, commit_bytes=commit_bytes,
+        commit_hbm_gbs=commit_bytes / c_mean / 1e9,
+        parity_rel_err={"y": e_y, "records": e_r})
+
+
+# ------------------------------------------------------------ CPU oracle
+
+def cpu_baseline(case, seconds):
+    """The oracle as it stands, threaded over (sequence, head), on the same
+    workload: whole passes over its decode steps until `seconds` elapse."""
+    import oracle
+    from oracle.ref import default_threads
+    th = default_threads()
+    done = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.decode_case(case, threads=th)
+        passes += 1
+        done += int(case.active.sum()) * case.H
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "token-head updates/s", "cores": th,
+            "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the {case.name} workload "
+                      f"({case.steps} decode steps x {case.batch} rows x {case.H} heads), "
+                      f"fp64 C oracle on {th} threads, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the mixer shards over heads and sequences with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from hybrid_linear_attention_rule_amd import kda
+    from hybrid_linear_attention_rule_amd import workloads as wl
+
+    if not os.path.exists(kda.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    kda.load()
+    torch.cuda.init()
+
+    case1 = wl.config(1)
+    print(f"# decode {case1.name}: steps={args.steps} warmup={args.warmup} "
+          f"layers={args.layers}", file=sys.stderr, flush=True)
+    head = run_decode_mode(torch, case1, args.steps, args.warmup, args.layers)
+    print(f"# decode kernel {head['kernel_us']:.2f} us, {head['hbm_gbs']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
+    modes = {}
+    if not args.no_modes:
+        case3 = wl.config(3)
+        print(f"# decode {case3.name}", file=sys.stderr, flush=True)
+        modes["large_batch_decode_bf16_state"] = run_decode_mode(
+            torch, case3, args.steps, args.warmup, 4)
+        case2 = wl.config(2)
+        print(f"# verify {case2.name}", file=sys.stderr, flush=True)
+        modes["spec_verify_commit"] = run_verify_mode(torch, case2, args.steps,
+                                                      args.warmup, 8)
+
+    cpu = None
+    if not args.no_cpu:
+        print("# cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(case1, args.cpu_seconds)
+
+    line = {
+        "metric": "KDA decode token-head state updates/s (batched decode, 1 GPU)",
+        "value": head["th_per_s"],
+        "unit": "token-head updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; distributions of the batched-decode workload)",
+        "config": {"workload": case1.name, "batch": case1.batch, "heads": case1.H,
+                   "head_k": case1.dk, "head_v": case1.dv, "act": case1.act,
+                   "state": case1.state, "state_pools_rotated": args.layers,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["hbm_frac"], "traffic": None,
+                     "kernel": "kda::token_kernel<128,128,bf16,f32,decode>",
+                     "kernel_us": head["kernel_us"],
+                     "bytes_per_launch": head["bytes_per_launch"]},
+        "cpu_baseline": cpu,
+        "parity_rel_err": head["parity_rel_err"],
+        "modes": modes,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

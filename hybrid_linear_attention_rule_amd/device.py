@@ -1,0 +1,105 @@
+"""Place a synthetic workload (workloads.Case) on the device, in the
+library's physical layouts, and read results back in logical layouts.
+
+Layout conversion only: no arithmetic of the mixer.  The state pool is
+[num_slots, H, dv, dk] (a logical S[i][j] sits at [j][i]); the conv ring is
+[num_slots, 4, H, 2dk+dv] with the raw token of position p in entry p mod 4.
+Rows are mapped to a shuffled set of slots, and spare slots are filled with
+NaN so that any stray access shows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import kda
+from .workloads import Case
+
+RING = 4
+
+
+def _act(x: np.ndarray, act: str, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device=device, dtype=torch.bfloat16 if act == "bf16" else torch.float32)
+
+
+def shape_of(case: Case, gate: str = "sigmoid", q_scale=1.0) -> kda.KdaShape:
+    return kda.KdaShape(case.H, case.dk, case.dv, act=case.act, state=case.state,
+                        gate={"sigmoid": kda.GATE_SIGMOID, "silu": kda.GATE_SILU}[gate],
+                        q_scale=q_scale)
+
+
+def params_of(case: Case, device="cuda") -> kda.KdaParams:
+    w = case.weights
+    f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    return kda.KdaParams(f(w.conv_q.reshape(-1, w.conv_q.shape[-1])),
+                         f(w.conv_k.reshape(-1, w.conv_k.shape[-1])),
+                         f(w.conv_v.reshape(-1, w.conv_v.shape[-1])),
+                         f(w.norm_w))
+
+
+@dataclass
+class DeviceState:
+    shape: kda.KdaShape
+    params: kda.KdaParams
+    pool: torch.Tensor
+    ring: torch.Tensor
+    slot_ids: torch.Tensor   # [B] int32 on device
+    slots: np.ndarray        # [B] host copy
+    num_slots: int
+
+
+def make_state(case: Case, *, spare_slots=3, seed=0, device="cuda", gate="sigmoid",
+               q_scale=1.0, fill_nan=True) -> DeviceState:
+    """Pool and ring holding the case's start state and history."""
+    B, H, dk, dv = case.batch, case.H, case.dk, case.dv
+    C = 2 * dk + dv
+    num_slots = B + spare_slots
+    rng = np.random.default_rng(1000 + seed)
+    slots = rng.permutation(num_slots)[:B].astype(np.int32)
+    shape = shape_of(case, gate, q_scale)
+
+    pool_h = np.full((num_slots, H, dv, dk), np.nan if fill_nan else 0.0,
+                     dtype=np.float32)
+    pool_h[slots] = np.swapaxes(case.S0, 2, 3)
+    ring_h = np.full((num_slots, RING, H, C), np.nan if fill_nan else 0.0,
+                     dtype=np.float32)
+    for b in range(B):
+        p = int(case.pos0[b])
+        for j in range(RING - 1):
+            pp = p - (RING - 1) + j
+            if pp >= 0:
+                ring_h[slots[b], pp % RING] = case.hist0[b, j]
+    pool = torch.from_numpy(pool_h).to(device=device, dtype=shape.state_dtype)
+    ring = _act(ring_h, case.act, device)
+    return DeviceState(shape, params_of(case, device), pool, ring,
+                       torch.from_numpy(slots).to(device), slots, num_slots)
+
+
+def read_states(ds: DeviceState, slots=None) -> np.ndarray:
+    """Logical float64 states [B, H, dk, dv] of the given slots (host copy)."""
+    slots = ds.slots if slots is None else slots
+    phys = ds.pool.float().cpu().numpy()[slots]
+    return np.swapaxes(phys, 2, 3).astype(np.float64)
+
+
+def read_window(ds: DeviceState, positions: np.ndarray, slots=None) -> np.ndarray:
+    """Logical float64 history [B, 3, H, C] (oldest first) at `positions`."""
+    slots = ds.slots if slots is None else slots
+    ring = ds.ring.float().cpu().numpy()
+    B = len(slots)
+    out = np.zeros((B, RING - 1) + ring.shape[2:])
+    for b in range(B):
+        for j in range(RING - 1):
+            pp = int(positions[b]) - (RING - 1) + j
+            if pp >= 0:
+                out[b, j] = ring[slots[b], pp % RING]
+    return out
+
+
+def tokens_to_device(toks, act: str, device="cuda"):
+    """TokenInputs arrays -> dict of device tensors in the activation dtype."""
+    return {name: _act(getattr(toks, name), act, device)
+            for name in ("q", "k", "v", "alpha", "beta", "g")}

@@ -1,0 +1,161 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, sizes buffers exactly, and rejects bad arguments before any launch
+(host-detected errors write nothing, so these calls are safe without a GPU:
+every pointer below is a dummy that must never be dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hybrid_linear_attention_rule_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_UNSUP = 0, -1, -2, -3, -4, -5
+BOGUS = ctypes.c_void_p(0x1000)     # never dereferenced: errors come first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def shape(**kw):
+    base = dict(num_heads=32, head_k=128, head_v=128, act="bf16", state="f32")
+    base.update(kw)
+    return kda.KdaShape(**base)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = header_functions()
+    assert len(names) == 14, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
+    assert sorted(kda.SIGNATURES) == names
+
+
+def test_library_links_no_torch():
+    import subprocess
+    out = subprocess.run(["ldd", kda.LIB_PATH], capture_output=True, text=True).stdout
+    assert "libtorch" not in out and "libc10" not in out
+
+
+def test_sizes(lib):
+    s = shape()
+    assert kda.state_bytes(s, 64) == 64 * 32 * 128 * 128 * 4
+    assert kda.state_bytes(shape(state="bf16"), 256) == 256 * 32 * 128 * 128 * 2
+    assert kda.conv_bytes(s, 64) == 64 * 4 * 32 * 384 * 2
+    assert kda.conv_bytes(shape(act="f32"), 3) == 3 * 4 * 32 * 384 * 4
+    assert kda.draft_state_bytes(s, 16, 4) == 16 * 4 * 32 * 128 * 128 * 4
+    assert kda.draft_state_bytes(shape(state="bf16"), 16, 4) == 16 * 4 * 32 * 128 * 128 * 4
+    assert kda.draft_conv_bytes(s, 16, 4) == 16 * 4 * 32 * 384 * 2
+    assert kda.state_bytes(shape(head_k=96, head_v=96), 1) == 0   # unsupported
+    assert kda.state_bytes(s, -1) == 0
+
+
+def test_status_strings(lib):
+    for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_UNSUP, -6):
+        assert lib.kda_status_str(code)
+    assert lib.kda_status_str(123) == b"unknown status code"
+
+
+def _decode(lib, sh, params, batch=4, num_slots=8, ptrs=None):
+    p = [BOGUS] * 11 if ptrs is None else ptrs
+    return lib.kda_decode(None if sh is None else ctypes.byref(sh.c()),
+                          None if params is None else ctypes.byref(params),
+                          batch, num_slots, *p, None, None)
+
+
+def _params():
+    return kda._Params(0x1000, 0x1000, 0x1000, None)
+
+
+def test_decode_host_errors(lib):
+    assert _decode(lib, None, _params()) == E_NULL
+    assert _decode(lib, shape(), None) == E_NULL
+    assert _decode(lib, shape(act="f32"), kda._Params(0, 0x1000, 0x1000, None)) == E_NULL
+    bad = shape()
+    c = bad.c()
+    c.act_dtype = 7
+    assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                          *([BOGUS] * 11), None, None) == E_DTYPE
+    c = shape().c()
+    c.gate = 5
+    assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                          *([BOGUS] * 11), None, None) == E_DTYPE
+    assert _decode(lib, shape(head_k=96, head_v=96), _params()) == E_UNSUP
+    assert _decode(lib, shape(head_k=64, head_v=128), _params()) == E_UNSUP
+    assert _decode(lib, shape(conv_width=3), _params()) == E_UNSUP
+    assert _decode(lib, shape(num_heads=0), _params()) == E_SHAPE
+    assert _decode(lib, shape(), _params(), batch=-1) == E_SHAPE
+    for i in range(11):        # each required pointer
+        p = [BOGUS] * 11
+        p[i] = None
+        assert _decode(lib, shape(), _params(), ptrs=p) == E_NULL, i
+    # batch 0 is a no-op success that launches nothing
+    assert _decode(lib, shape(), _params(), batch=0, ptrs=[None] * 11) == OK
+
+
+def test_verify_and_commit_host_errors(lib):
+    sh = shape()
+
+    def verify(n, ptrs=None):
+        p = [BOGUS] * 13 if ptrs is None else ptrs
+        return lib.kda_verify(ctypes.byref(sh.c()), ctypes.byref(_params()), 4, n, 8,
+                              *p, None, None)
+    assert verify(0) == E_SHAPE
+    assert verify(17) == E_SHAPE
+    for i in range(13):
+        p = [BOGUS] * 13
+        p[i] = None
+        assert verify(4, p) == E_NULL, i
+
+    def commit(n, ptrs=None, batch=4):
+        p = [BOGUS] * 7 if ptrs is None else ptrs
+        return lib.kda_commit_accepted(ctypes.byref(sh.c()), batch, n, 8, *p, None, None)
+    assert commit(0) == E_SHAPE
+    assert commit(4, batch=-2) == E_SHAPE
+    for i in range(7):
+        p = [BOGUS] * 7
+        p[i] = None
+        assert commit(4, p) == E_NULL, i
+    assert commit(4, [None] * 7, batch=0) == OK
+
+
+def test_prefill_host_errors(lib):
+    sh = shape()
+
+    def prefill(num_seqs=2, total=100, max_len=60, ptrs=None, ws=None, ws_bytes=0):
+        p = [BOGUS] * 12 if ptrs is None else ptrs
+        return lib.kda_prefill(ctypes.byref(sh.c()), ctypes.byref(_params()), num_seqs,
+                               p[0], total, max_len, 8, *p[1:], ws, ws_bytes, None, None)
+    need = kda.prefill_workspace_bytes(sh, 2, 100)
+    assert prefill(num_seqs=-1) == E_SHAPE
+    assert prefill(total=-5) == E_SHAPE
+    for i in range(12):
+        p = [BOGUS] * 12
+        p[i] = None
+        assert prefill(ptrs=p, ws=BOGUS, ws_bytes=need) == E_NULL, i
+    if need > 0:
+        assert prefill(ws=None, ws_bytes=0) == E_WS
+        assert prefill(ws=BOGUS, ws_bytes=need - 1) == E_WS
+    assert prefill(num_seqs=0, ptrs=[None] * 12) == OK
+
+
+def test_state_io_host_errors(lib):
+    sh = shape()
+    c = sh.c()
+    assert lib.kda_state_write(ctypes.byref(c), None, 8, BOGUS, 2, BOGUS, None, None) == E_NULL
+    assert lib.kda_state_read(ctypes.byref(c), BOGUS, 8, BOGUS, -1, BOGUS, None, None) == E_SHAPE
+    assert lib.kda_state_read(ctypes.byref(c), None, 8, None, 0, None, None, None) == OK
+    assert lib.kda_conv_write(ctypes.byref(c), BOGUS, 8, BOGUS, None, 2, BOGUS, None,
+                              None) == E_NULL
+    assert lib.kda_conv_read(None, BOGUS, 8, BOGUS, BOGUS, 2, BOGUS, None, None) == E_NULL
