@@ -84,6 +84,12 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Recursive-halving reduction over groups of G consecutive lanes, for
 // N == G values per lane.  On return lane (lane % G) == i of the group holds
 // the group's sum of value i.  N - 1 shuffles per lane, fixed order.
+//
+// At each level the upper lane of a pair first swaps the two halves of its
+// values, so that every lane keeps v[0..half) and sends v[half..2*half).
+// The swap reads each element twice, which keeps the selects on values: a
+// select between two element addresses would turn the register array into a
+// dynamically indexed one (compare-and-select chains).
 template <int G>
 __device__ __forceinline__ float group_transpose_sum(float (&v)[G], int lane_in_group) {
 #pragma unroll
@@ -91,10 +97,12 @@ __device__ __forceinline__ float group_transpose_sum(float (&v)[G], int lane_in_
         const bool upper = (lane_in_group & half) != 0;
 #pragma unroll
         for (int i = 0; i < half; ++i) {
-            const float send = upper ? v[i] : v[i + half];
-            const float keep = upper ? v[i + half] : v[i];
-            v[i] = keep + __shfl_xor(send, half, kWave);
+            const float a = v[i], b = v[i + half];
+            v[i] = upper ? b : a;
+            v[i + half] = upper ? a : b;
         }
+#pragma unroll
+        for (int i = 0; i < half; ++i) v[i] += __shfl_xor(v[i + half], half, kWave);
     }
     return v[0];
 }

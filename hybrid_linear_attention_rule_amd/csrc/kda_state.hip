@@ -8,7 +8,8 @@
 
 namespace kda {
 
-// One workgroup per (row, head); logical [dk][dv] <-> physical [dv][dk].
+// One workgroup per (row, head); the pool stores each head's state in the
+// logical [dk][dv] order, so import/export is a typed copy.
 template <int ST>
 __global__ __launch_bounds__(256) void state_io_kernel(StateIoArgs a, int DK, int DV) {
     const int H = a.H;
@@ -24,10 +25,8 @@ __global__ __launch_bounds__(256) void state_io_kernel(StateIoArgs a, int DK, in
     const size_t phys0 = ((size_t)slot * H + h) * elems;
     float* logical = a.logical + ((size_t)b * H + h) * elems;
     for (int e = threadIdx.x; e < (int)elems; e += blockDim.x) {
-        const int j = e / DK, i = e % DK;     // physical [j][i]
-        const size_t li = (size_t)i * DV + j;
         if (a.write) {
-            const float x = logical[li];
+            const float x = logical[e];
             if constexpr (ST == kF32)
                 static_cast<float*>(a.pool)[phys0 + e] = x;
             else
@@ -38,7 +37,7 @@ __global__ __launch_bounds__(256) void state_io_kernel(StateIoArgs a, int DK, in
                 x = static_cast<const float*>(a.pool)[phys0 + e];
             else
                 x = bf16_to_f32(static_cast<const uint16_t*>(a.pool)[phys0 + e]);
-            logical[li] = x;
+            logical[e] = x;
         }
     }
 }

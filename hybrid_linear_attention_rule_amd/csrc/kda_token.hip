@@ -23,52 +23,47 @@
 //   y        = norm_w * o / sqrt(mean(o^2) + eps) * gate(g)
 // so a single pass over S serves both dk-reductions.
 //
-// Thread map: the physical state of a head is [dv][dk] (dk contiguous).  A
-// thread owns VEC consecutive dk entries (16 bytes of storage) of PASSES
-// rows j = r + ROWS * p.  LANES = dk / VEC lanes cover one row, and the two
-// dk-reductions of all PASSES rows (2 * PASSES == LANES values per lane) are
-// finished with one recursive-halving shuffle pass per lane group, which
-// leaves lane i of the group holding reduced value i.  Workgroup size is
-// 2 * dv threads, so every reduction, load and store is fixed in order and
-// the result is bitwise reproducible.
+// Thread map: the state of a head is stored [dk][dv] (dv contiguous).  A
+// thread owns VEC consecutive dv entries (16 bytes of storage) of RPT
+// consecutive key rows; LJ = dv / VEC lanes span a row and RG = 2 * VEC row
+// groups span dk.  The dk-reductions run in-thread over the thread's RPT
+// rows, then over the RG row groups through LDS in a fixed order, so every
+// result is bitwise reproducible.  Workgroup size is 2 * dv threads.
 #include "kda_device.h"
 #include "kda_internal.h"
+
+#include <hip/hip_bf16.h>
 
 namespace kda {
 
 template <int DK, int DV, int VEC>
 struct TileMap {
-    static constexpr int LANES = DK / VEC;      // lanes per state row
-    static constexpr int NT = 2 * DV;           // threads per workgroup
-    static constexpr int ROWS = NT / LANES;     // rows per pass
-    static constexpr int PASSES = DV / ROWS;    // rows per thread
-    static_assert(2 * PASSES == LANES, "reduction needs 2*PASSES == LANES");
-    static_assert(kWave % LANES == 0, "lane groups must tile a wave");
+    static constexpr int NT = 2 * DV;          // threads per workgroup
+    static constexpr int LJ = DV / VEC;        // lanes along one dv row
+    static constexpr int RG = NT / LJ;         // row groups (= 2 * VEC)
+    static constexpr int RPT = DK / RG;        // consecutive rows per thread
+    static_assert(kWave % LJ == 0, "a dv row must tile a wave");
+    static_assert(RPT >= 4 && DK % RG == 0 && RPT % 4 == 0, "rows per thread");
     static_assert(NT >= DK + DV, "conv needs one thread per q/k and v channel");
 };
 
-// Load the thread's state slice as raw 128-bit words (issued early).
-template <int ST, int DK, int PASSES, int ROWS, int VEC>
-__device__ __forceinline__ void load_state_raw(const void* head_base, int r,
-                                               int l, uint4 (&raw)[PASSES]) {
+// Raw 128-bit words of the thread's state slice (issued early).
+template <int ST, int DV, int RPT, int VEC>
+__device__ __forceinline__ void load_state_raw(const void* head_base, int r, int c,
+                                               uint4 (&raw)[RPT]) {
+    const size_t esz = (ST == kF32) ? 4 : 2;
+    const char* base = static_cast<const char*>(head_base) +
+                       ((size_t)(r * RPT) * DV + (size_t)c * VEC) * esz;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int j = r + ROWS * p;
-        if constexpr (ST == kF32) {
-            raw[p] = *reinterpret_cast<const uint4*>(
-                static_cast<const float*>(head_base) + j * DK + l * VEC);
-        } else {
-            raw[p] = *reinterpret_cast<const uint4*>(
-                static_cast<const uint16_t*>(head_base) + j * DK + l * VEC);
-        }
-    }
+    for (int p = 0; p < RPT; ++p)
+        raw[p] = *reinterpret_cast<const uint4*>(base + (size_t)p * DV * esz);
 }
 
-template <int ST, int PASSES, int VEC>
-__device__ __forceinline__ void unpack_state(const uint4 (&raw)[PASSES],
-                                             float (&s)[PASSES][VEC]) {
+template <int ST, int RPT, int VEC>
+__device__ __forceinline__ void unpack_state(const uint4 (&raw)[RPT],
+                                             float (&s)[RPT][VEC]) {
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
+    for (int p = 0; p < RPT; ++p) {
         const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
         if constexpr (ST == kF32) {
 #pragma unroll
@@ -83,133 +78,138 @@ __device__ __forceinline__ void unpack_state(const uint4 (&raw)[PASSES],
     }
 }
 
-// Typed store of the thread's state slice into [dv][dk] storage.
-template <int ST, int DK, int PASSES, int ROWS, int VEC>
-__device__ __forceinline__ void store_state(void* head_base, int r, int l,
-                                            const float (&s)[PASSES][VEC]) {
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __hip_bfloat162 p = __float22bfloat162_rn(make_float2(lo, hi));
+    return *reinterpret_cast<uint32_t*>(&p);
+}
+
+// Typed store of the thread's state slice into [dk][dv] storage.
+template <int ST, int DV, int RPT, int VEC>
+__device__ __forceinline__ void store_state(void* head_base, int r, int c,
+                                            const float (&s)[RPT][VEC]) {
+    const size_t esz = (ST == kF32) ? 4 : 2;
+    char* base = static_cast<char*>(head_base) +
+                 ((size_t)(r * RPT) * DV + (size_t)c * VEC) * esz;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int j = r + ROWS * p;
+    for (int p = 0; p < RPT; ++p) {
+        uint4 x;
         if constexpr (ST == kF32) {
-            float4 x = make_float4(s[p][0], s[p][1], s[p][2], s[p][3]);
-            *reinterpret_cast<float4*>(static_cast<float*>(head_base) + j * DK +
-                                       l * VEC) = x;
+            x = make_uint4(__float_as_uint(s[p][0]), __float_as_uint(s[p][1]),
+                           __float_as_uint(s[p][2]), __float_as_uint(s[p][3]));
         } else {
-            uint4 x;
-            x.x = f32_to_bf16_rne(s[p][0]) | (f32_to_bf16_rne(s[p][1]) << 16);
-            x.y = f32_to_bf16_rne(s[p][2]) | (f32_to_bf16_rne(s[p][3]) << 16);
-            x.z = f32_to_bf16_rne(s[p][4]) | (f32_to_bf16_rne(s[p][5]) << 16);
-            x.w = f32_to_bf16_rne(s[p][6]) | (f32_to_bf16_rne(s[p][7]) << 16);
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(head_base) + j * DK +
-                                      l * VEC) = x;
+            x = make_uint4(pack_bf16x2(s[p][0], s[p][1]), pack_bf16x2(s[p][2], s[p][3]),
+                           pack_bf16x2(s[p][4], s[p][5]), pack_bf16x2(s[p][6], s[p][7]));
         }
+        *reinterpret_cast<uint4*>(base + (size_t)p * DV * esz) = x;
     }
 }
 
-// FP32 record store, [dv][dk] like the pool.
-template <int DK, int PASSES, int ROWS, int VEC>
-__device__ __forceinline__ void store_record(float* rec, int r, int l,
-                                             const float (&s)[PASSES][VEC]) {
+// FP32 record store, [dk][dv] like the pool.
+template <int DV, int RPT, int VEC>
+__device__ __forceinline__ void store_record(float* rec, int r, int c,
+                                             const float (&s)[RPT][VEC]) {
+    float* base = rec + (size_t)(r * RPT) * DV + c * VEC;
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int j = r + ROWS * p;
+    for (int p = 0; p < RPT; ++p)
 #pragma unroll
-        for (int e = 0; e < VEC; e += 4) {
-            *reinterpret_cast<float4*>(rec + j * DK + l * VEC + e) =
+        for (int e = 0; e < VEC; e += 4)
+            *reinterpret_cast<float4*>(base + p * DV + e) =
                 make_float4(s[p][e], s[p][e + 1], s[p][e + 2], s[p][e + 3]);
-        }
-    }
 }
 
 // Phase A of a token: the causal conv of this thread's channels (t < DK: q
-// and k channel t; DK <= t < DK + DV: v channel t - DK) into conv_s, and the
-// raw token copied to the ring (decode, entry pos mod 4) or to draft_conv
-// (verify).  Conv taps 0..2 read the three previous raw tokens (earlier
-// drafts, else the ring, else zero before position 0), tap 3 the current.
+// and k channel t; DK <= t < DK + DV: v channel t - DK), and the raw token
+// copied to the ring (decode: entry pos mod 4) or to draft_conv (verify).
+// Conv taps 0..2 read the three previous raw tokens (earlier drafts, else
+// the ring, else zero before position 0), tap 3 the current one.
 template <int DK, int DV, int ACT, bool VERIFY>
 __device__ __forceinline__ void conv_token(const TokenArgs& a, int b, int h, int t, int n,
-                                       int slot, int pos, float4 wq4, float4 wk4,
-                                       float4 wv4, float* conv_s, float (*red_s)[4],
-                                       float& cq, float& ck) {
+                                           int slot, int pos, float4 w4a, float4 w4b,
+                                           float& ca, float& cb) {
     constexpr int C = 2 * DK + DV;
     const int tid = threadIdx.x;
     const int H = a.H;
     const bool has_qk = tid < DK;
     const bool has_v = tid >= DK && tid < DK + DV;
-    const size_t ring_slot = (size_t)slot * kConvW;  // ring [slot][4][H][C]
+    ca = 0.f;
+    cb = 0.f;
+    if (!has_qk && !has_v) return;
     const int64_t tok = (int64_t)b * n + t;
-    const int wave = tid / kWave;
-    float cv = 0.f;
-    cq = 0.f;
-    ck = 0.f;
-    if (has_qk || has_v) {
-        const int ch_q = tid, ch_k = DK + tid, ch_v = 2 * DK + (tid - DK);
-        float hq[kConvW], hk[kConvW], hv[kConvW];
+    const size_t ring_slot = (size_t)slot * kConvW;   // ring [slot][4][H][C]
+    const int vch = tid - DK;
+    float xa[kConvW], xb[kConvW];
 #pragma unroll
-        for (int j = 0; j < kConvW; ++j) {
-            const int rel = t - (kConvW - 1) + j;   // draft-token index
-            float xq = 0.f, xk = 0.f, xv = 0.f;
-            if (rel >= 0) {
-                if (has_qk) {
-                    xq = ld_act<ACT>(a.q, ((int64_t)b * n + rel) * H * DK + h * DK + tid);
-                    xk = ld_act<ACT>(a.k, ((int64_t)b * n + rel) * H * DK + h * DK + tid);
-                } else {
-                    xv = ld_act<ACT>(a.v, ((int64_t)b * n + rel) * H * DV + h * DV + (tid - DK));
-                }
-            } else if (pos + rel >= 0) {
-                const size_t e = ring_slot + ((pos + rel) & (kConvW - 1));
-                const int64_t base = ((int64_t)e * H + h) * C;
-                if (has_qk) {
-                    xq = ld_act<ACT>(a.ring, base + ch_q);
-                    xk = ld_act<ACT>(a.ring, base + ch_k);
-                } else {
-                    xv = ld_act<ACT>(a.ring, base + ch_v);
-                }
-            }
-            hq[j] = xq; hk[j] = xk; hv[j] = xv;
-        }
-        if (has_qk) {
-            cq = wq4.x * hq[0]; cq = fmaf(wq4.y, hq[1], cq);
-            cq = fmaf(wq4.z, hq[2], cq); cq = fmaf(wq4.w, hq[3], cq);
-            ck = wk4.x * hk[0]; ck = fmaf(wk4.y, hk[1], ck);
-            ck = fmaf(wk4.z, hk[2], ck); ck = fmaf(wk4.w, hk[3], ck);
-            conv_s[ch_q] = cq;
-            conv_s[ch_k] = ck;
-        } else {
-            cv = wv4.x * hv[0]; cv = fmaf(wv4.y, hv[1], cv);
-            cv = fmaf(wv4.z, hv[2], cv); cv = fmaf(wv4.w, hv[3], cv);
-            conv_s[ch_v] = cv;
-        }
-        // keep the raw token: decode -> ring entry pos mod 4,
-        // verify -> draft_conv[b, t, h, :]
-        if constexpr (!VERIFY) {
-            const int64_t base = ((int64_t)(ring_slot + (pos & (kConvW - 1))) * H + h) * C;
+    for (int j = 0; j < kConvW; ++j) {
+        const int rel = t - (kConvW - 1) + j;          // draft-token index
+        float va = 0.f, vb = 0.f;
+        if (rel >= 0) {
+            const int64_t row = (int64_t)b * n + rel;
             if (has_qk) {
-                cp_act<ACT>(a.ring, base + ch_q, a.q, tok * H * DK + h * DK + tid);
-                cp_act<ACT>(a.ring, base + ch_k, a.k, tok * H * DK + h * DK + tid);
+                va = ld_act<ACT>(a.q, (row * H + h) * DK + tid);
+                vb = ld_act<ACT>(a.k, (row * H + h) * DK + tid);
             } else {
-                cp_act<ACT>(a.ring, base + ch_v, a.v, tok * H * DV + h * DV + (tid - DK));
+                va = ld_act<ACT>(a.v, (row * H + h) * DV + vch);
             }
-        } else {
-            const int64_t base = (tok * H + h) * C;
+        } else if (pos + rel >= 0) {
+            const int64_t base = ((int64_t)(ring_slot + ((pos + rel) & (kConvW - 1))) * H + h) * C;
             if (has_qk) {
-                cp_act<ACT>(a.draft_conv, base + ch_q, a.q, tok * H * DK + h * DK + tid);
-                cp_act<ACT>(a.draft_conv, base + ch_k, a.k, tok * H * DK + h * DK + tid);
+                va = ld_act<ACT>(a.ring, base + tid);
+                vb = ld_act<ACT>(a.ring, base + DK + tid);
             } else {
-                cp_act<ACT>(a.draft_conv, base + ch_v, a.v, tok * H * DV + h * DV + (tid - DK));
+                va = ld_act<ACT>(a.ring, base + 2 * DK + vch);
             }
         }
+        xa[j] = va;
+        xb[j] = vb;
     }
-    {
-        float sq = cq * cq, sk = ck * ck, sqk = cq * ck;
-        sq = wave_sum(sq);
-        sk = wave_sum(sk);
-        sqk = wave_sum(sqk);
-        if ((tid % kWave) == 0) {
-            red_s[wave][0] = sq;
-            red_s[wave][1] = sk;
-            red_s[wave][2] = sqk;
-        }
+    ca = w4a.x * xa[0];
+    ca = fmaf(w4a.y, xa[1], ca);
+    ca = fmaf(w4a.z, xa[2], ca);
+    ca = fmaf(w4a.w, xa[3], ca);
+    if (has_qk) {
+        cb = w4b.x * xb[0];
+        cb = fmaf(w4b.y, xb[1], cb);
+        cb = fmaf(w4b.z, xb[2], cb);
+        cb = fmaf(w4b.w, xb[3], cb);
+    }
+    // keep the raw token: decode -> ring entry pos mod 4, verify -> draft_conv
+    void* dst = VERIFY ? a.draft_conv : a.ring;
+    const int64_t dbase = VERIFY ? (tok * H + h) * C
+                                 : ((int64_t)(ring_slot + (pos & (kConvW - 1))) * H + h) * C;
+    if (has_qk) {
+        cp_act<ACT>(dst, dbase + tid, a.q, (tok * H + h) * DK + tid);
+        cp_act<ACT>(dst, dbase + DK + tid, a.k, (tok * H + h) * DK + tid);
+    } else {
+        cp_act<ACT>(dst, dbase + 2 * DK + vch, a.v, (tok * H + h) * DV + vch);
+    }
+}
+
+// Phase A of a token: conv, the decay factor of this thread's key channel,
+// beta and the gate input, the conv of v into LDS, and the per-wave partial
+// sums of |c_q|^2, |c_k|^2 and c_q . c_k.
+template <int DK, int DV, int ACT, bool VERIFY>
+__device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
+                                        int slot, int pos, float4 w4a, float4 w4b,
+                                        float* vt_s, float (*red_s)[4], float& ca,
+                                        float& cb, float& al, float& beta, float& gv) {
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    const int64_t tok = (int64_t)b * n + t;
+    const bool has_qk = tid < DK;
+    const bool has_v = tid >= DK && tid < DK + DV;
+    conv_token<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, w4a, w4b, ca, cb);
+    al = has_qk ? ld_act<ACT>(a.alpha, (tok * H + h) * DK + tid) : 0.f;
+    beta = ld_act<ACT>(a.beta, tok * H + h);
+    gv = (tid < DV) ? ld_act<ACT>(a.g, (tok * H + h) * DV + tid) : 0.f;
+    if (has_v) vt_s[tid - DK] = ca;
+    const float cq = has_qk ? ca : 0.f, ck = cb;
+    const float sq = wave_sum(cq * cq), sk = wave_sum(ck * ck), sqk = wave_sum(cq * ck);
+    if ((tid % kWave) == 0) {
+        const int wave = tid / kWave;
+        red_s[wave][0] = sq;
+        red_s[wave][1] = sk;
+        red_s[wave][2] = sqk;
     }
 }
 
@@ -217,160 +217,184 @@ template <int DK, int DV, int ACT, int ST, bool VERIFY>
 __global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
     constexpr int VEC = (ST == kF32) ? 4 : 8;
     using M = TileMap<DK, DV, VEC>;
-    constexpr int LANES = M::LANES, ROWS = M::ROWS, PASSES = M::PASSES;
-    constexpr int NT = M::NT;
-    constexpr int C = 2 * DK + DV;
-    constexpr int NW = NT / kWave;
+    constexpr int LJ = M::LJ, RG = M::RG, RPT = M::RPT;
+    constexpr int NW = M::NT / kWave;
+    constexpr int PAD = 4;
 
-    __shared__ float conv_s[C];      // conv outputs of the token
+    __shared__ float vt_s[DV];                   // conv of v
+    __shared__ float ak_s[DK], aq_s[DK];         // alpha*kh, alpha*qh
+    __shared__ float al_s[DK], kh_s[DK];         // alpha, kh
     __shared__ float delta_s[DV];
-    __shared__ float orow_s[DV];     // o' = S^T (alpha * qh)
+    __shared__ float part_s[2][RG][DV + PAD];    // dk-reduction partials
     __shared__ float red_s[NW][4];
 
     const int tid = threadIdx.x;
     const int H = a.H;
     const int h = blockIdx.x % H;
     const int b = blockIdx.x / H;
+    const int wave = tid / kWave;
+    const int c = tid % LJ;                      // dv chunk: j = c*VEC + e
+    const int r = tid / LJ;                      // row group: i = r*RPT + p
+    const int n = a.n;
+    const bool has_qk = tid < DK;
+    const bool has_v = tid >= DK && tid < DK + DV;
+
+    // slot-independent loads first: conv taps and the norm weight
+    float4 w4a = make_float4(0, 0, 0, 0), w4b = w4a;
+    if (has_qk) {
+        w4a = *reinterpret_cast<const float4*>(a.wq + ((size_t)h * DK + tid) * kConvW);
+        w4b = *reinterpret_cast<const float4*>(a.wk + ((size_t)h * DK + tid) * kConvW);
+    } else if (has_v) {
+        w4a = *reinterpret_cast<const float4*>(a.wv + ((size_t)h * DV + tid - DK) * kConvW);
+    }
+    const float norm_w = (tid < DV) ? (a.norm_w ? a.norm_w[tid] : 1.0f) : 0.0f;
+
     const int slot = a.slot_ids[b];
+    const int pos = a.positions[b];
     if (slot < 0) return;
     if (slot >= a.num_slots) {
         if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_SLOT);
         return;
     }
-    const int pos = a.positions[b];
     if (pos < 0) {
         if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_POSITION);
         return;
     }
-    const int n = a.n;
-    const int l = tid % LANES;
-    const int r = tid / LANES;
-    const int wave = tid / kWave;
 
     // ---- state in: issued first, consumed after the conv ----------------
-    const size_t head_elems = (size_t)DV * DK;
+    const size_t head_elems = (size_t)DK * DV;
     const size_t head_off = ((size_t)slot * H + h) * head_elems;
-    uint4 raw[PASSES];
+    const void* pool_head = static_cast<const char*>(a.pool) +
+                            head_off * (ST == kF32 ? 4 : 2);
+    uint4 raw[RPT];
     if (pos > 0) {
-        const void* base = (ST == kF32)
-            ? static_cast<const void*>(static_cast<const float*>(a.pool) + head_off)
-            : static_cast<const void*>(static_cast<const uint16_t*>(a.pool) + head_off);
-        load_state_raw<ST, DK, PASSES, ROWS, VEC>(base, r, l, raw);
+        load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw);
     } else {
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) raw[p] = make_uint4(0, 0, 0, 0);
+        for (int p = 0; p < RPT; ++p) raw[p] = make_uint4(0, 0, 0, 0);
     }
 
-    // ---- conv taps of this thread's channels
-    const bool has_qk = tid < DK;
-    const bool has_v = tid >= DK && tid < DK + DV;
-    float4 wq4 = make_float4(0, 0, 0, 0), wk4 = wq4, wv4 = wq4;
-    if (has_qk) {
-        wq4 = *reinterpret_cast<const float4*>(a.wq + ((size_t)h * DK + tid) * kConvW);
-        wk4 = *reinterpret_cast<const float4*>(a.wk + ((size_t)h * DK + tid) * kConvW);
-    } else if (has_v) {
-        wv4 = *reinterpret_cast<const float4*>(a.wv + ((size_t)h * DV + tid - DK) * kConvW);
-    }
-    const float norm_w = (tid < DV) ? (a.norm_w ? a.norm_w[tid] : 1.0f) : 0.0f;
-
-    float s[PASSES][VEC];
-    float cq = 0.f, ck = 0.f;
-    // ---------------- A. conv, raw copy, norm partial sums ---------------
-    conv_token<DK, DV, ACT, VERIFY>(a, b, h, 0, n, slot, pos, wq4, wk4, wv4, conv_s, red_s,
-                                    cq, ck);
-    unpack_state<ST, PASSES, VEC>(raw, s);
+    // token 0's phase A overlaps the state loads; the unpack then waits for them
+    float ca, cb, al, beta, gv;
+    phase_a<DK, DV, ACT, VERIFY>(a, b, h, 0, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
+                                 beta, gv);
+    float s[RPT][VEC];
+    unpack_state<ST, RPT, VEC>(raw, s);
 
     for (int t = 0; t < n; ++t) {
         const int64_t tok = (int64_t)b * n + t;     // row of the inputs
+        // ---------------- A. conv, raw copy, norm partial sums -----------
         if (t > 0)
-            conv_token<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, wq4, wk4, wv4, conv_s,
-                                            red_s, cq, ck);
-        // per-thread decay factors for its dk slice (independent of LDS)
-        float al[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-            al[e] = ld_act<ACT>(a.alpha, tok * H * DK + h * DK + l * VEC + e);
-        const float beta = ld_act<ACT>(a.beta, tok * H + h);
+            phase_a<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
+                                         al, beta, gv);
         __syncthreads();
 
-        // ---------------- B. normalise, partial dots, reduction ----------
+        // ---------------- B. normalised keys and queries ----------------
         float sq = 0.f, sk = 0.f, sqk = 0.f;
 #pragma unroll
-        for (int w = 0; w < DK / kWave; ++w) {   // q/k channels live in waves 0..DK/64-1
+        for (int w = 0; w < DK / kWave; ++w) {       // q/k live in waves 0..DK/64-1
             sq += red_s[w][0];
             sk += red_s[w][1];
             sqk += red_s[w][2];
         }
         const float rq = a.q_scale / sqrtf(sq + a.l2_eps);
         const float rk = 1.0f / sqrtf(sk + a.l2_eps);
-        const float kq = sqk * rq * rk;          // kh . qh
-        float kh[VEC], akh[VEC], aqh[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            const int i = l * VEC + e;
-            kh[e] = conv_s[DK + i] * rk;
-            akh[e] = al[e] * kh[e];
-            aqh[e] = al[e] * (conv_s[i] * rq);
-        }
-        float vals[LANES];
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            float u = 0.f, o = 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                u = fmaf(s[p][e], akh[e], u);
-                o = fmaf(s[p][e], aqh[e], o);
-            }
-            vals[p] = u;
-            vals[PASSES + p] = o;
-        }
-        const float red = group_transpose_sum<LANES>(vals, l);
-        if (l < PASSES) {
-            const int j = r + ROWS * l;
-            delta_s[j] = beta * (conv_s[2 * DK + j] - red);
-        } else {
-            const int j = r + ROWS * (l - PASSES);
-            orow_s[j] = red;
+        const float kq = sqk * rq * rk;              // kh . qh
+        if (has_qk) {
+            const float kh = cb * rk, qh = ca * rq;
+            ak_s[tid] = al * kh;
+            aq_s[tid] = al * qh;
+            al_s[tid] = al;
+            kh_s[tid] = kh;
         }
         __syncthreads();
 
-        // ---------------- C. state update, store, read-out ----------------
+        // ---------------- C. in-thread dk partials -----------------------
+        {
+            float u[VEC], o[VEC];
 #pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const float d = delta_s[r + ROWS * p];
+            for (int e = 0; e < VEC; ++e) u[e] = o[e] = 0.f;
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) s[p][e] = fmaf(kh[e], d, s[p][e] * al[e]);
+            for (int p4 = 0; p4 < RPT; p4 += 4) {
+                const float4 ak4 = *reinterpret_cast<const float4*>(&ak_s[r * RPT + p4]);
+                const float4 aq4 = *reinterpret_cast<const float4*>(&aq_s[r * RPT + p4]);
+                const float akv[4] = {ak4.x, ak4.y, ak4.z, ak4.w};
+                const float aqv[4] = {aq4.x, aq4.y, aq4.z, aq4.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) {
+                        u[e] = fmaf(s[p4 + q][e], akv[q], u[e]);
+                        o[e] = fmaf(s[p4 + q][e], aqv[q], o[e]);
+                    }
+            }
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                *reinterpret_cast<float4*>(&part_s[0][r][c * VEC + e]) =
+                    make_float4(u[e], u[e + 1], u[e + 2], u[e + 3]);
+                *reinterpret_cast<float4*>(&part_s[1][r][c * VEC + e]) =
+                    make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
+            }
         }
-        if constexpr (VERIFY) {
-            float* rec = a.records + ((size_t)tok * H + h) * head_elems;
-            store_record<DK, PASSES, ROWS, VEC>(rec, r, l, s);
-        }
+        __syncthreads();
+
+        // ---------------- D. finish the reductions, delta, read-out --------
         float o = 0.f;
-        if (tid < DV) o = fmaf(kq, delta_s[tid], orow_s[tid]);
+        if (tid < DV) {
+            float u = 0.f, op = 0.f;
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                u += part_s[0][g][tid];
+                op += part_s[1][g][tid];
+            }
+            const float d = beta * (vt_s[tid] - u);
+            delta_s[tid] = d;
+            o = fmaf(kq, d, op);
+        }
         {
             const float ms = wave_sum(o * o);
             if ((tid % kWave) == 0) red_s[wave][3] = ms;
         }
         __syncthreads();
 
-        // ---------------- D. gated RMSNorm -------------------------------
+        // ---------------- E. state update, store, gated RMSNorm ----------
+        {
+            float d[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; e += 4) {
+                const float4 d4 = *reinterpret_cast<const float4*>(&delta_s[c * VEC + e]);
+                d[e] = d4.x; d[e + 1] = d4.y; d[e + 2] = d4.z; d[e + 3] = d4.w;
+            }
+#pragma unroll
+            for (int p4 = 0; p4 < RPT; p4 += 4) {
+                const float4 al4 = *reinterpret_cast<const float4*>(&al_s[r * RPT + p4]);
+                const float4 kh4 = *reinterpret_cast<const float4*>(&kh_s[r * RPT + p4]);
+                const float alv[4] = {al4.x, al4.y, al4.z, al4.w};
+                const float khv[4] = {kh4.x, kh4.y, kh4.z, kh4.w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e)
+                        s[p4 + q][e] = fmaf(khv[q], d[e], s[p4 + q][e] * alv[q]);
+            }
+        }
+        if constexpr (VERIFY) {
+            store_record<DV, RPT, VEC>(a.records + ((size_t)tok * H + h) * head_elems, r, c, s);
+        }
         if (tid < DV) {
             float ms = 0.f;
 #pragma unroll
             for (int w = 0; w < DV / kWave; ++w) ms += red_s[w][3];
             const float rr = 1.0f / sqrtf(ms / (float)DV + a.norm_eps);
-            const float gv = ld_act<ACT>(a.g, tok * H * DV + h * DV + tid);
             a.y[(tok * H + h) * DV + tid] = norm_w * (o * rr) * gate_fn(a.gate, gv);
         }
-        // The next token's first writes (conv_s, red_s[.][0..2]) touch only
-        // LDS that every thread finished reading before the second barrier.
+        // The next token's LDS writes (vt_s, red_s[.][0..2], then ak_s..kh_s
+        // after its first barrier) touch only what every thread finished
+        // reading before this token's last barrier or in its own phase E.
     }
 
     if constexpr (!VERIFY) {
-        void* base = (ST == kF32)
-            ? static_cast<void*>(static_cast<float*>(a.pool) + head_off)
-            : static_cast<void*>(static_cast<uint16_t*>(a.pool) + head_off);
-        store_state<ST, DK, PASSES, ROWS, VEC>(base, r, l, s);
+        store_state<ST, DV, RPT, VEC>(const_cast<void*>(pool_head), r, c, s);
     }
 }
 

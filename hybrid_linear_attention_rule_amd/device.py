@@ -2,7 +2,7 @@
 library's physical layouts, and read results back in logical layouts.
 
 Layout conversion only: no arithmetic of the mixer.  The state pool is
-[num_slots, H, dv, dk] (a logical S[i][j] sits at [j][i]); the conv ring is
+[num_slots, H, dk, dv] (the logical S[i][j] order); the conv ring is
 [num_slots, 4, H, 2dk+dv] with the raw token of position p in entry p mod 4.
 Rows are mapped to a shuffled set of slots, and spare slots are filled with
 NaN so that any stray access shows.
@@ -61,9 +61,9 @@ def make_state(case: Case, *, spare_slots=3, seed=0, device="cuda", gate="sigmoi
     slots = rng.permutation(num_slots)[:B].astype(np.int32)
     shape = shape_of(case, gate, q_scale)
 
-    pool_h = np.full((num_slots, H, dv, dk), np.nan if fill_nan else 0.0,
+    pool_h = np.full((num_slots, H, dk, dv), np.nan if fill_nan else 0.0,
                      dtype=np.float32)
-    pool_h[slots] = np.swapaxes(case.S0, 2, 3)
+    pool_h[slots] = case.S0
     ring_h = np.full((num_slots, RING, H, C), np.nan if fill_nan else 0.0,
                      dtype=np.float32)
     for b in range(B):
@@ -81,8 +81,7 @@ def make_state(case: Case, *, spare_slots=3, seed=0, device="cuda", gate="sigmoi
 def read_states(ds: DeviceState, slots=None) -> np.ndarray:
     """Logical float64 states [B, H, dk, dv] of the given slots (host copy)."""
     slots = ds.slots if slots is None else slots
-    phys = ds.pool.float().cpu().numpy()[slots]
-    return np.swapaxes(phys, 2, 3).astype(np.float64)
+    return ds.pool.float().cpu().numpy()[slots].astype(np.float64)
 
 
 def read_window(ds: DeviceState, positions: np.ndarray, slots=None) -> np.ndarray:

@@ -216,8 +216,8 @@ def prefill_workspace_bytes(shape: KdaShape, num_seqs: int, total_tokens: int) -
 # ------------------------------------------------------- device buffers
 
 def alloc_pool(shape: KdaShape, num_slots: int, device="cuda") -> torch.Tensor:
-    """State pool [num_slots, H, dv, dk] in the storage dtype."""
-    return torch.zeros((num_slots, shape.num_heads, shape.head_v, shape.head_k),
+    """State pool [num_slots, H, dk, dv] in the storage dtype."""
+    return torch.zeros((num_slots, shape.num_heads, shape.head_k, shape.head_v),
                        dtype=shape.state_dtype, device=device)
 
 

@@ -50,7 +50,8 @@
  *
  * Layouts (row-major, contiguous):
  *   C = 2*dk + dv, the raw channels of one head in the order q | k | v.
- *   state pool   [num_slots, H, dv, dk]   state dtype (S[i][j] at [j][i])
+ *   state pool   [num_slots, H, dk, dv]   state dtype, S[i][j] with i the key
+ *                                          channel (dv contiguous)
  *   conv ring    [num_slots, 4, H, C]     act dtype; entry (p mod 4) holds the
  *                                          raw token at position p
  *   conv weights conv_w_q [H*dk, 4], conv_w_k [H*dk, 4], conv_w_v [H*dv, 4]
@@ -120,11 +121,11 @@ const char *kda_status_str(int code);
 
 /* ----- sizes (host functions; 0 when the shape is invalid) ------------- */
 
-/* Bytes of a state pool of `num_slots` slots: num_slots*H*dv*dk*sizeof. */
+/* Bytes of a state pool of `num_slots` slots: num_slots*H*dk*dv*sizeof. */
 size_t kda_state_bytes(const kda_shape *shape, int64_t num_slots);
 /* Bytes of a conv ring of `num_slots` slots: num_slots*4*H*C*sizeof(act). */
 size_t kda_conv_bytes(const kda_shape *shape, int64_t num_slots);
-/* Bytes of the FP32 verify records [batch, n_draft, H, dv, dk]. */
+/* Bytes of the FP32 verify records [batch, n_draft, H, dk, dv]. */
 size_t kda_draft_state_bytes(const kda_shape *shape, int32_t batch,
                              int32_t n_draft);
 /* Bytes of the raw draft tokens kept by verify [batch, n_draft, H, C] act. */
@@ -193,7 +194,7 @@ int kda_decode(const kda_shape *shape, const kda_params *params,
  * targets", Description).
  *   q, k, alpha [batch, n_draft, H, dk]; v, g [batch, n_draft, H, dv];
  *   beta [batch, n_draft, H]: act.  1 <= n_draft <= 16.
- *   draft_states [batch, n_draft, H, dv, dk] FP32: the state after each
+ *   draft_states [batch, n_draft, H, dk, dv] FP32: the state after each
  *            draft token (never rounded, whatever the storage dtype).
  *   draft_conv [batch, n_draft, H, C] act: the raw draft tokens, kept for
  *            the commit.

@@ -20,7 +20,7 @@ def run_verify_gpu(case, ds, slots=None):
     slots = ds.slots if slots is None else slots
     slot_t = torch.from_numpy(slots.astype(np.int32)).cuda()
     pos_t = torch.from_numpy(case.pos0.astype(np.int32)).cuda()
-    rec = torch.full((B, n, H, dv, dk), float("nan"), device="cuda")
+    rec = torch.full((B, n, H, dk, dv), float("nan"), device="cuda")
     dconv = torch.full((B, n, H, C), float("nan"), device="cuda",
                        dtype=ds.shape.act_dtype)
     y = torch.full((B, n, H, dv), float("nan"), device="cuda")
@@ -58,7 +58,7 @@ def check_verify_commit(case):
     # records and outputs are FP32 under either storage dtype; with BF16
     # storage the start state is the dequantised BF16 pool, shared by both
     assert_parity(y.cpu().numpy(), y_ref, 2e-5, "verify y")
-    rec_l = np.swapaxes(rec.cpu().numpy(), 3, 4)
+    rec_l = rec.cpu().numpy()
     assert_parity(rec_l, rec_ref, 2e-5, "verify records")
     # raw drafts are kept bit for bit
     raw = np.concatenate([case.tokens.q, case.tokens.k, case.tokens.v], axis=-1)
