@@ -74,37 +74,26 @@ __device__ __forceinline__ float gate_fn(int gate, float x) {
     return gate == kGateSilu ? x * sig : sig;
 }
 
-// Sum over a whole wavefront; every lane gets the total.  Fixed order.
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = kWave / 2; d >= 1; d >>= 1) x += __shfl_xor(x, d, kWave);
-    return x;
+// DPP move of a float within rows of 16 lanes (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Recursive-halving reduction over groups of G consecutive lanes, for
-// N == G values per lane.  On return lane (lane % G) == i of the group holds
-// the group's sum of value i.  N - 1 shuffles per lane, fixed order.
-//
-// At each level the upper lane of a pair first swaps the two halves of its
-// values, so that every lane keeps v[0..half) and sends v[half..2*half).
-// The swap reads each element twice, which keeps the selects on values: a
-// select between two element addresses would turn the register array into a
-// dynamically indexed one (compare-and-select chains).
-template <int G>
-__device__ __forceinline__ float group_transpose_sum(float (&v)[G], int lane_in_group) {
-#pragma unroll
-    for (int half = G / 2; half >= 1; half >>= 1) {
-        const bool upper = (lane_in_group & half) != 0;
-#pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float a = v[i], b = v[i + half];
-            v[i] = upper ? b : a;
-            v[i + half] = upper ? a : b;
-        }
-#pragma unroll
-        for (int i = 0; i < half; ++i) v[i] += __shfl_xor(v[i + half], half, kWave);
-    }
-    return v[0];
+// Sum over a whole wavefront; the result is uniform.  Fixed order: pairs,
+// quads, halves and rows of 16 by DPP, then the four row sums in lane order.
+// Must be called with every lane of the wave active.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mov<0xB1>(x);    // quad_perm(1,0,3,2): lane ^ 1
+    x += dpp_mov<0x4E>(x);    // quad_perm(2,3,0,1): lane ^ 2
+    x += dpp_mov<0x141>(x);   // row_half_mirror: lane i <-> 7 - i
+    x += dpp_mov<0x140>(x);   // row_mirror: lane i <-> 15 - i
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return ((r0 + r1) + r2) + r3;
 }
 
 }  // namespace kda

@@ -26,9 +26,10 @@
 // Thread map: the state of a head is stored [dk][dv] (dv contiguous).  A
 // thread owns VEC consecutive dv entries (16 bytes of storage) of RPT
 // consecutive key rows; LJ = dv / VEC lanes span a row and RG = 2 * VEC row
-// groups span dk.  The dk-reductions run in-thread over the thread's RPT
+// groups span dk (32 state elements per thread: 512 threads for
+// dk = dv = 128).  The dk-reductions run in-thread over the thread's RPT
 // rows, then over the RG row groups through LDS in a fixed order, so every
-// result is bitwise reproducible.  Workgroup size is 2 * dv threads.
+// result is bitwise reproducible.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -38,14 +39,30 @@ namespace kda {
 
 template <int DK, int DV, int VEC>
 struct TileMap {
-    static constexpr int NT = 2 * DV;          // threads per workgroup
+    static constexpr int NT = DK * DV / 32;    // threads per workgroup: 32 state
+                                               // elements per thread
     static constexpr int LJ = DV / VEC;        // lanes along one dv row
-    static constexpr int RG = NT / LJ;         // row groups (= 2 * VEC)
+    static constexpr int RG = NT / LJ;         // row groups
     static constexpr int RPT = DK / RG;        // consecutive rows per thread
     static_assert(kWave % LJ == 0, "a dv row must tile a wave");
     static_assert(RPT >= 4 && DK % RG == 0 && RPT % 4 == 0, "rows per thread");
     static_assert(NT >= DK + DV, "conv needs one thread per q/k and v channel");
+    static_assert(NT % kWave == 0 && NT <= 1024, "workgroup size");
 };
+
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+
+// Streaming 128-bit accesses: each state byte is touched once per call and
+// not again until the next call, so loads and stores bypass cache retention
+// (nontemporal hint).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+    const v4u32 v = __builtin_nontemporal_load(static_cast<const v4u32*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, uint4 x) {
+    const v4u32 v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, static_cast<v4u32*>(p));
+}
 
 // Raw 128-bit words of the thread's state slice (issued early).
 template <int ST, int DV, int RPT, int VEC>
@@ -55,8 +72,7 @@ __device__ __forceinline__ void load_state_raw(const void* head_base, int r, int
     const char* base = static_cast<const char*>(head_base) +
                        ((size_t)(r * RPT) * DV + (size_t)c * VEC) * esz;
 #pragma unroll
-    for (int p = 0; p < RPT; ++p)
-        raw[p] = *reinterpret_cast<const uint4*>(base + (size_t)p * DV * esz);
+    for (int p = 0; p < RPT; ++p) raw[p] = ld_stream(base + (size_t)p * DV * esz);
 }
 
 template <int ST, int RPT, int VEC>
@@ -101,7 +117,7 @@ __device__ __forceinline__ void store_state(void* head_base, int r, int c,
             x = make_uint4(pack_bf16x2(s[p][0], s[p][1]), pack_bf16x2(s[p][2], s[p][3]),
                            pack_bf16x2(s[p][4], s[p][5]), pack_bf16x2(s[p][6], s[p][7]));
         }
-        *reinterpret_cast<uint4*>(base + (size_t)p * DV * esz) = x;
+        st_stream(base + (size_t)p * DV * esz, x);
     }
 }
 
@@ -114,96 +130,111 @@ __device__ __forceinline__ void store_record(float* rec, int r, int c,
     for (int p = 0; p < RPT; ++p)
 #pragma unroll
         for (int e = 0; e < VEC; e += 4)
-            *reinterpret_cast<float4*>(base + p * DV + e) =
-                make_float4(s[p][e], s[p][e + 1], s[p][e + 2], s[p][e + 3]);
+            st_stream(base + p * DV + e,
+                      make_uint4(__float_as_uint(s[p][e]), __float_as_uint(s[p][e + 1]),
+                                 __float_as_uint(s[p][e + 2]), __float_as_uint(s[p][e + 3])));
 }
 
-// Phase A of a token: the causal conv of this thread's channels (t < DK: q
-// and k channel t; DK <= t < DK + DV: v channel t - DK), and the raw token
-// copied to the ring (decode: entry pos mod 4) or to draft_conv (verify).
-// Conv taps 0..2 read the three previous raw tokens (earlier drafts, else
-// the ring, else zero before position 0), tap 3 the current one.
-template <int DK, int DV, int ACT, bool VERIFY>
-__device__ __forceinline__ void conv_token(const TokenArgs& a, int b, int h, int t, int n,
-                                           int slot, int pos, float4 w4a, float4 w4b,
-                                           float& ca, float& cb) {
-    constexpr int C = 2 * DK + DV;
-    const int tid = threadIdx.x;
-    const int H = a.H;
-    const bool has_qk = tid < DK;
-    const bool has_v = tid >= DK && tid < DK + DV;
-    ca = 0.f;
-    cb = 0.f;
-    if (!has_qk && !has_v) return;
-    const int64_t tok = (int64_t)b * n + t;
-    const size_t ring_slot = (size_t)slot * kConvW;   // ring [slot][4][H][C]
-    const int vch = tid - DK;
-    float xa[kConvW], xb[kConvW];
-#pragma unroll
-    for (int j = 0; j < kConvW; ++j) {
-        const int rel = t - (kConvW - 1) + j;          // draft-token index
-        float va = 0.f, vb = 0.f;
-        if (rel >= 0) {
-            const int64_t row = (int64_t)b * n + rel;
-            if (has_qk) {
-                va = ld_act<ACT>(a.q, (row * H + h) * DK + tid);
-                vb = ld_act<ACT>(a.k, (row * H + h) * DK + tid);
-            } else {
-                va = ld_act<ACT>(a.v, (row * H + h) * DV + vch);
-            }
-        } else if (pos + rel >= 0) {
-            const int64_t base = ((int64_t)(ring_slot + ((pos + rel) & (kConvW - 1))) * H + h) * C;
-            if (has_qk) {
-                va = ld_act<ACT>(a.ring, base + tid);
-                vb = ld_act<ACT>(a.ring, base + DK + tid);
-            } else {
-                va = ld_act<ACT>(a.ring, base + 2 * DK + vch);
-            }
-        }
-        xa[j] = va;
-        xb[j] = vb;
-    }
-    ca = w4a.x * xa[0];
-    ca = fmaf(w4a.y, xa[1], ca);
-    ca = fmaf(w4a.z, xa[2], ca);
-    ca = fmaf(w4a.w, xa[3], ca);
-    if (has_qk) {
-        cb = w4b.x * xb[0];
-        cb = fmaf(w4b.y, xb[1], cb);
-        cb = fmaf(w4b.z, xb[2], cb);
-        cb = fmaf(w4b.w, xb[3], cb);
-    }
-    // keep the raw token: decode -> ring entry pos mod 4, verify -> draft_conv
-    void* dst = VERIFY ? a.draft_conv : a.ring;
-    const int64_t dbase = VERIFY ? (tok * H + h) * C
-                                 : ((int64_t)(ring_slot + (pos & (kConvW - 1))) * H + h) * C;
-    if (has_qk) {
-        cp_act<ACT>(dst, dbase + tid, a.q, (tok * H + h) * DK + tid);
-        cp_act<ACT>(dst, dbase + DK + tid, a.k, (tok * H + h) * DK + tid);
-    } else {
-        cp_act<ACT>(dst, dbase + 2 * DK + vch, a.v, (tok * H + h) * DV + vch);
-    }
+template <int ACT>
+__device__ __forceinline__ float act_from_bits(uint32_t bits) {
+    if constexpr (ACT == kF32) return __uint_as_float(bits);
+    else return bf16_to_f32(bits);
 }
 
-// Phase A of a token: conv, the decay factor of this thread's key channel,
-// beta and the gate input, the conv of v into LDS, and the per-wave partial
-// sums of |c_q|^2, |c_k|^2 and c_q . c_k.
+// Phase A of a token.  Conv roles, one per wave (dk and dv are multiples of
+// the wave size): waves covering threads t < DK convolve q channel t (A) and
+// k channel t (B); waves covering DK <= t < DK + DV convolve v channel t - DK
+// (A); the remaining waves only load their inputs.  Conv taps 0..2 read the
+// three previous raw tokens (earlier drafts of this call, else the ring, else
+// zero before position 0), tap 3 the current token.  Every row address is
+// wave-uniform (a scalar base plus a 32-bit lane offset), and every load is
+// issued before any loaded value is used, so no wait for one tap stalls the
+// others or the state stream; taps before position 0 are zeroed afterwards.
+// The raw token is copied to the ring (decode: entry pos mod 4) or to
+// draft_conv (verify).  Also loads alpha, beta and g, writes the conv of v to
+// LDS and the per-wave partial sums of |c_q|^2, |c_k|^2 and c_q . c_k.
 template <int DK, int DV, int ACT, bool VERIFY>
 __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
                                         int slot, int pos, float4 w4a, float4 w4b,
                                         float* vt_s, float (*red_s)[4], float& ca,
                                         float& cb, float& al, float& beta, float& gv) {
+    constexpr int C = 2 * DK + DV;
+    constexpr size_t ESZ = (ACT == kF32) ? 4 : 2;
     const int tid = threadIdx.x;
     const int H = a.H;
     const int64_t tok = (int64_t)b * n + t;
-    const bool has_qk = tid < DK;
-    const bool has_v = tid >= DK && tid < DK + DV;
-    conv_token<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, w4a, w4b, ca, cb);
-    al = has_qk ? ld_act<ACT>(a.alpha, (tok * H + h) * DK + tid) : 0.f;
+    const int wfirst = __builtin_amdgcn_readfirstlane(tid);
+    const bool qk = wfirst < DK;                         // wave-uniform role
+    const bool isv = !qk && wfirst < DK + DV;
+    const int lc = qk ? tid : (isv ? tid - DK : 0);     // channel within q|k or v
+
+    const char* qb = static_cast<const char*>(a.q);
+    const char* kb = static_cast<const char*>(a.k);
+    const char* vb = static_cast<const char*>(a.v);
+    const char* ringb = static_cast<const char*>(a.ring);
+
+    // unconditional loads from valid lane offsets; lanes that do not own a
+    // channel discard the value
+    const float al_ld = ld_act<ACT>(static_cast<const char*>(a.alpha) +
+                                        (size_t)(tok * H + h) * DK * ESZ, qk ? tid : 0);
+    const float g_ld = ld_act<ACT>(static_cast<const char*>(a.g) +
+                                       (size_t)(tok * H + h) * DV * ESZ, tid < DV ? tid : 0);
     beta = ld_act<ACT>(a.beta, tok * H + h);
-    gv = (tid < DV) ? ld_act<ACT>(a.g, (tok * H + h) * DV + tid) : 0.f;
-    if (has_v) vt_s[tid - DK] = ca;
-    const float cq = has_qk ? ca : 0.f, ck = cb;
+    al = qk ? al_ld : 0.f;
+    gv = (tid < DV) ? g_ld : 0.f;
+
+    ca = 0.f;
+    cb = 0.f;
+    if (qk || isv) {
+        const size_t ring_slot = (size_t)slot * kConvW;   // ring [slot][4][H][C]
+        uint32_t bA[kConvW], bB[kConvW];
+#pragma unroll
+        for (int j = 0; j < kConvW; ++j) {
+            const int rel = t - (kConvW - 1) + j;          // draft-token index
+            const char* pa;
+            const char* pb;
+            if (rel >= 0) {
+                const int64_t row = (int64_t)b * n + rel;
+                pa = qk ? qb + (size_t)(row * H + h) * DK * ESZ
+                        : vb + (size_t)(row * H + h) * DV * ESZ;
+                pb = kb + (size_t)(row * H + h) * DK * ESZ;
+            } else {
+                const char* e = ringb +
+                    ((size_t)(ring_slot + ((pos + rel) & (kConvW - 1))) * H + h) * C * ESZ;
+                pa = e + (qk ? 0 : 2 * DK) * ESZ;
+                pb = e + DK * ESZ;
+            }
+            bA[j] = ld_act_bits<ACT>(pa, lc);
+            bB[j] = ld_act_bits<ACT>(pb, lc);
+        }
+        float xa[kConvW], xb[kConvW];
+#pragma unroll
+        for (int j = 0; j < kConvW; ++j) {
+            const int rel = t - (kConvW - 1) + j;
+            const bool live = rel >= 0 || pos + rel >= 0;
+            xa[j] = live ? act_from_bits<ACT>(bA[j]) : 0.f;
+            xb[j] = live ? act_from_bits<ACT>(bB[j]) : 0.f;
+        }
+        ca = w4a.x * xa[0];
+        ca = fmaf(w4a.y, xa[1], ca);
+        ca = fmaf(w4a.z, xa[2], ca);
+        ca = fmaf(w4a.w, xa[3], ca);
+        if (qk) {
+            cb = w4b.x * xb[0];
+            cb = fmaf(w4b.y, xb[1], cb);
+            cb = fmaf(w4b.z, xb[2], cb);
+            cb = fmaf(w4b.w, xb[3], cb);
+        }
+        // keep the raw token: decode -> ring entry pos mod 4, verify -> draft_conv
+        char* dst = VERIFY
+            ? static_cast<char*>(a.draft_conv) + (size_t)(tok * H + h) * C * ESZ
+            : static_cast<char*>(a.ring) +
+                  ((size_t)(ring_slot + (pos & (kConvW - 1))) * H + h) * C * ESZ;
+        st_act_bits<ACT>(dst + (qk ? 0 : 2 * DK) * ESZ, lc, bA[kConvW - 1]);
+        if (qk) st_act_bits<ACT>(dst + DK * ESZ, lc, bB[kConvW - 1]);
+    }
+    if (isv) vt_s[lc] = ca;
+    const float cq = qk ? ca : 0.f, ck = cb;
     const float sq = wave_sum(cq * cq), sk = wave_sum(ck * ck), sqk = wave_sum(cq * ck);
     if ((tid % kWave) == 0) {
         const int wave = tid / kWave;
@@ -214,7 +245,7 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
 }
 
 template <int DK, int DV, int ACT, int ST, bool VERIFY>
-__global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
+__global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     constexpr int VEC = (ST == kF32) ? 4 : 8;
     using M = TileMap<DK, DV, VEC>;
     constexpr int LJ = M::LJ, RG = M::RG, RPT = M::RPT;
@@ -235,18 +266,18 @@ __global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
     const int wave = tid / kWave;
     const int c = tid % LJ;                      // dv chunk: j = c*VEC + e
     const int r = tid / LJ;                      // row group: i = r*RPT + p
-    const int n = a.n;
-    const bool has_qk = tid < DK;
-    const bool has_v = tid >= DK && tid < DK + DV;
+    const int n = VERIFY ? a.n : 1;             // decode: exactly one token
+    const bool qk_lane = tid < DK;
+    const bool v_lane = tid >= DK && tid < DK + DV;
 
-    // slot-independent loads first: conv taps and the norm weight
-    float4 w4a = make_float4(0, 0, 0, 0), w4b = w4a;
-    if (has_qk) {
-        w4a = *reinterpret_cast<const float4*>(a.wq + ((size_t)h * DK + tid) * kConvW);
-        w4b = *reinterpret_cast<const float4*>(a.wk + ((size_t)h * DK + tid) * kConvW);
-    } else if (has_v) {
-        w4a = *reinterpret_cast<const float4*>(a.wv + ((size_t)h * DV + tid - DK) * kConvW);
-    }
+    // slot-independent loads first: conv taps (q|v and k channel of this
+    // thread's conv role; idle lanes read a valid row they do not use) and
+    // the norm weight
+    const float* wA = qk_lane ? a.wq + ((size_t)h * DK + tid) * kConvW
+                              : a.wv + ((size_t)h * DV + (v_lane ? tid - DK : 0)) * kConvW;
+    const float* wB = a.wk + ((size_t)h * DK + (qk_lane ? tid : 0)) * kConvW;
+    const float4 w4a = *reinterpret_cast<const float4*>(wA);
+    const float4 w4b = *reinterpret_cast<const float4*>(wB);
     const float norm_w = (tid < DV) ? (a.norm_w ? a.norm_w[tid] : 1.0f) : 0.0f;
 
     const int slot = a.slot_ids[b];
@@ -256,22 +287,18 @@ __global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
         if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_SLOT);
         return;
     }
-    if (pos < 0) {
-        if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_POSITION);
-        return;
-    }
 
-    // ---- state in: issued first, consumed after the conv ----------------
+    // ---- state in: issued as soon as the slot is known (a fresh sequence,
+    // position 0, discards what it loaded), consumed after the conv --------
     const size_t head_elems = (size_t)DK * DV;
     const size_t head_off = ((size_t)slot * H + h) * head_elems;
     const void* pool_head = static_cast<const char*>(a.pool) +
                             head_off * (ST == kF32 ? 4 : 2);
     uint4 raw[RPT];
-    if (pos > 0) {
-        load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw);
-    } else {
-#pragma unroll
-        for (int p = 0; p < RPT; ++p) raw[p] = make_uint4(0, 0, 0, 0);
+    load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw);
+    if (pos < 0) {
+        if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_POSITION);
+        return;
     }
 
     // token 0's phase A overlaps the state loads; the unpack then waits for them
@@ -280,7 +307,14 @@ __global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
                                  beta, gv);
     float s[RPT][VEC];
     unpack_state<ST, RPT, VEC>(raw, s);
+    if (pos == 0) {
+#pragma unroll
+        for (int p = 0; p < RPT; ++p)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s[p][e] = 0.f;
+    }
 
+#pragma unroll 1
     for (int t = 0; t < n; ++t) {
         const int64_t tok = (int64_t)b * n + t;     // row of the inputs
         // ---------------- A. conv, raw copy, norm partial sums -----------
@@ -300,7 +334,7 @@ __global__ __launch_bounds__(2 * DV) void token_kernel(TokenArgs a) {
         const float rq = a.q_scale / sqrtf(sq + a.l2_eps);
         const float rk = 1.0f / sqrtf(sk + a.l2_eps);
         const float kq = sqk * rq * rk;              // kh . qh
-        if (has_qk) {
+        if (qk_lane) {
             const float kh = cb * rk, qh = ca * rq;
             ak_s[tid] = al * kh;
             aq_s[tid] = al * qh;
@@ -456,7 +490,7 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
 template <int DK, int DV, int ACT, int ST>
 static int launch_token_t(const TokenArgs& a, int32_t batch, bool verify,
                           hipStream_t stream) {
-    const dim3 grid((unsigned)batch * (unsigned)a.H), block(2 * DV);
+    const dim3 grid((unsigned)batch * (unsigned)a.H), block(DK * DV / 32);
     if (verify)
         hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, true>), grid, block, 0, stream, a);
     else
