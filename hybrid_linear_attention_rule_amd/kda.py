@@ -329,10 +329,25 @@ def commit_accepted(shape, slot_ids, positions, accepted, draft_states, draft_co
 
 def prefill(shape, params, cu_seqlens, max_seqlen, slot_ids, positions, q, k, v,
             alpha, beta, g, pool, ring, y, workspace, status=None, stream=None):
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().kda_prefill(ctypes.byref(shape.c()), ctypes.byref(params.c()),
-                              slot_ids.numel(), _ptr(cu_seqlens), q.shape[0],
-                              int(max_seqlen), pool.shape[0], _ptr(slot_ids),
-                              _ptr(positions), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                              _ptr(beta), _ptr(g), _ptr(pool), _ptr(ring), _ptr(y),
-                              _ptr(workspace), ws_bytes, _ptr(status), _stream(stream)))
+    """Chunked prefill of the packed sequences cu_seqlens describes.
+    workspace: a device tensor of at least prefill_workspace_bytes() bytes."""
+    B = slot_ids.numel()
+    T = q.shape[0]
+    _check_params(shape, params)
+    _expect(cu_seqlens, B + 1, torch.int32, "cu_seqlens")
+    _expect(slot_ids, B, torch.int32, "slot_ids")
+    _expect(positions, B, torch.int32, "positions")
+    _check_tokens(shape, T, q, k, v, alpha, beta, g)
+    _check_pool_ring(shape, pool, ring)
+    _expect(y, T * shape.num_heads * shape.head_v, torch.float32, "y")
+    ws_bytes = 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous device tensor")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().kda_prefill(ctypes.byref(shape.c()), ctypes.byref(params.c()), B,
+                              _ptr(cu_seqlens), T, int(max_seqlen), pool.shape[0],
+                              _ptr(slot_ids), _ptr(positions), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(alpha), _ptr(beta), _ptr(g), _ptr(pool), _ptr(ring),
+                              _ptr(y), _ptr(workspace), ws_bytes, _ptr(status),
+                              _stream(stream)))

@@ -1,0 +1,121 @@
+"""GPU parity of kda_prefill (chunkwise WY/UT form on the matrix cores)
+against the CPU oracle's token-by-token recurrence."""
+import numpy as np
+import pytest
+
+from gpu_util import assert_parity, need_gpu, tol_for
+from hybrid_linear_attention_rule_amd import device as dev
+from hybrid_linear_attention_rule_amd import kda
+from hybrid_linear_attention_rule_amd import workloads as wl
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill_gpu(case, ds=None, *, slots=None, max_seqlen=None, cu=None):
+    torch = need_gpu()
+    ds = dev.make_state(case) if ds is None else ds
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    T = int(case.cu_seqlens[-1])
+    y = torch.full((T, case.H, case.dv), float("nan"), device="cuda")
+    slots = ds.slots if slots is None else slots
+    slot_t = torch.from_numpy(np.asarray(slots, dtype=np.int32)).cuda()
+    pos_t = torch.from_numpy(case.pos0.astype(np.int32)).cuda()
+    cu_t = torch.from_numpy(np.asarray(case.cu_seqlens if cu is None else cu,
+                                       dtype=np.int32)).cuda()
+    nbytes = kda.prefill_workspace_bytes(ds.shape, case.batch, T)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mx = max(case.lens) if max_seqlen is None else max_seqlen
+    kda.prefill(ds.shape, ds.params, cu_t, mx, slot_t, pos_t, tok["q"], tok["k"],
+                tok["v"], tok["alpha"], tok["beta"], tok["g"], ds.pool, ds.ring, y, ws,
+                status)
+    torch.cuda.synchronize()
+    return ds, y.cpu().numpy(), int(status.item())
+
+
+def check_prefill(case, *, full_outputs=True):
+    print(f"case {case.name}: lens={case.lens} H={case.H} d={case.dk} act={case.act} "
+          f"state={case.state}", flush=True)
+    ds, y, status = run_prefill_gpu(case)
+    assert status == 0
+    y_ref, S_ref, h_ref = oracle.prefill_case(case)
+    tol = tol_for(case.state)
+    assert_parity(dev.read_states(ds), S_ref, tol, "final states")
+    if full_outputs:
+        assert_parity(y, y_ref, 2e-5, "all outputs")
+    lo = int(case.cu_seqlens[case.slice_seq]) + case.slice_start
+    sl = slice(lo, lo + case.slice_len)
+    assert_parity(y[sl], y_ref[sl], 2e-5, f"{case.slice_len}-token output slice")
+    end_pos = case.pos0 + np.asarray(case.lens)
+    np.testing.assert_array_equal(dev.read_window(ds, end_pos), h_ref)
+    spare = np.setdiff1d(np.arange(ds.num_slots), ds.slots)
+    assert np.all(np.isnan(ds.pool[spare].float().cpu().numpy()))
+    return ds
+
+
+@pytest.mark.parametrize("lens", [[1, 63, 64, 65, 130], [200, 3, 2]])
+def test_prefill_ragged_lengths(lens):
+    need_gpu()
+    case = wl.make_prefill(70 + len(lens), lens=lens, H=3, dk=128, dv=128, act="bf16",
+                           state="f32", slice_len=32, name=f"prefill_ragged_{len(lens)}")
+    check_prefill(case)
+
+
+@pytest.mark.parametrize("act,state", [("f32", "f32"), ("bf16", "bf16"), ("f32", "bf16")])
+def test_prefill_dtypes(act, state):
+    need_gpu()
+    case = wl.make_prefill(80, lens=[150, 77], H=2, dk=128, dv=128, act=act, state=state,
+                           slice_len=32, name=f"prefill_{act}_{state}")
+    check_prefill(case)
+
+
+def test_prefill_continues_from_stored_state_and_history():
+    """positions > 0: the chunk pass reads the ring for the first tokens and
+    the state pass starts from the stored state."""
+    need_gpu()
+    case = wl.make_prefill(81, lens=[70, 5, 129], H=2, dk=128, dv=128, act="bf16",
+                           state="f32", init="random", slice_len=32,
+                           name="prefill_continued")
+    check_prefill(case)
+
+
+def test_prefill_strong_decay_stays_finite():
+    """Decays down to alpha ~ e^-12 per token: the factorised exponentials
+    stay <= 1, nothing overflows."""
+    need_gpu()
+    case = wl.make_prefill(82, lens=[128, 64], H=2, dk=128, dv=128, act="f32",
+                           state="f32", slice_len=32, name="prefill_strong_decay")
+    rng = np.random.default_rng(5)
+    case.tokens.alpha[:] = wl.round_f32(np.exp(-rng.uniform(0.0, 12.0,
+                                                            case.tokens.alpha.shape)))
+    check_prefill(case)
+
+
+def test_config4_chunked_prefill():
+    need_gpu()
+    check_prefill(wl.config(4))
+
+
+def test_prefill_bad_seqlens_and_inactive_sequences():
+    torch = need_gpu()
+    case = wl.make_prefill(83, lens=[40, 30], H=2, dk=128, dv=128, act="bf16",
+                           state="f32", slice_len=8, name="prefill_bad")
+    # sequence 1 inactive: untouched; sequence 0 checked
+    ds = dev.make_state(case)
+    slots = ds.slots.copy()
+    slots[1] = -1
+    pool1 = ds.pool[ds.slots[1]].clone()
+    ds, y, status = run_prefill_gpu(case, ds, slots=slots)
+    assert status == 0
+    assert np.isnan(y[40:]).all()
+    assert torch.equal(ds.pool[ds.slots[1]].view(torch.uint8), pool1.view(torch.uint8))
+    # non-monotone cu_seqlens: reported, that sequence skipped
+    ds = dev.make_state(case)
+    pool0 = ds.pool.clone()
+    ds, y, status = run_prefill_gpu(case, ds, cu=[0, 50, 40])
+    assert status & kda.STATUS_BAD_SEQLENS
+    # a sequence longer than max_seqlen is reported too
+    ds = dev.make_state(case)
+    ds, y, status = run_prefill_gpu(case, ds, max_seqlen=32)
+    assert status & kda.STATUS_BAD_SEQLENS
