@@ -7,36 +7,39 @@
 // stored once at the end ("Extend NVIDIA/TensorRT-LLM#19991 with isolated
 // NVFP4 Kimi K3 targets", Description).
 //
-// Within a chunk of L <= 64 tokens with start state S0, let G_t be the sum of
-// log alpha over tokens 0..t of the chunk (per key channel).  The write
-// vectors u_t of the token-by-token recurrence satisfy
+// Within a chunk of L <= 64 tokens with start state S0, let e(t, i) be the
+// product of alpha over tokens i+1..t (per key channel; 1 when i = t).  The
+// write vectors u_t of the token-by-token recurrence satisfy
 //     (I + A) U = diag(beta) (V - K_G S0),
-//     A_ti = beta_t sum_c kh_tc kh_ic exp(G_tc - G_ic)   (i < t),
-// so U = Ut - W S0 with T = (I + A)^-1, Ut = T diag(beta) V and
-// W = T diag(beta) (exp(G) * K).  Then
-//     O   = (exp(G) * Q) S0 + (P (.) causal) U,
-//           P_ti = sum_c qh_tc kh_ic exp(G_tc - G_ic)   (i <= t),
-//     S_L = Diag(exp(G_last)) S0 + (exp(G_last - G) * K)^T U.
+//     A_ti = beta_t sum_c kh_tc kh_ic e_c(t, i)    (i < t),
+// with K_G = kh scaled by e(t, -1), the decay from the chunk start.  So
+// U = Ut - W S0, where [W | Ut] solves (I + A) X = diag(beta) [K_G | V].
+// Then
+//     O   = (e(t,-1) * Q) S0 + (P (.) causal) U,
+//           P_ti = sum_c qh_tc kh_ic e_c(t, i)   (i <= t),
+//     S_L = Diag(e(last,-1)) S0 + (e(last, t) * K)^T U.
+//
+// Decay factors are products of alpha, never exponentials of differences of
+// prefix sums, so nothing can overflow or lose range for any alpha in
+// (0, 1].  Tokens are grouped in 4-token sub-blocks.  For a pair (t, i) in
+// different sub-blocks, e(t, i) factors through any sub-block boundary J
+// between them: (alpha over J..t) * (alpha over i+1..J-1), both factors in
+// [0, 1], so those entries are matrix-core products of scaled keys and
+// queries.  Pairs inside one sub-block are formed elementwise in registers.
 //
 // Three kernels:
-//   chunk  (parallel over chunk x head): conv, L2 norms, decay sums, A, P,
-//          T, W, Ut and the scaled Q / K, written to the workspace;
+//   chunk  (parallel over chunk x head): conv, L2 norms, decay products, A
+//          and P, the diagonal 16x16 inverses of (I + A), the blocked forward
+//          substitution for [W | Ut]; writes W (negated), exp-scaled Q and K
+//          and P as pre-split fp16 pairs in matrix-core fragment order, Ut in
+//          FP32, and the chunk's total decay;
 //   state  (per sequence x head x 64 value columns, sequential over the
 //          sequence's chunks): U, O and the next state on the matrix cores,
-//          the state slice held in registers; O is written unnormalised;
-//   finish (per token x head): the gated RMSNorm of O, and the ring update
-//          with the last three raw tokens of each sequence.
-//
-// Decay factors.  Every exponential is taken of a sum of log alpha over a
-// token range, so its argument is <= 0 and nothing can overflow for any
-// alpha in (0, 1].  The sums come from block-local prefix sums over 16-token
-// blocks plus whole-block totals, never from the difference of two long
-// prefix sums.  Pairs inside one 16-token block are formed elementwise;
-// pairs across blocks factor through the first token n of the row block,
-//     exp(G_t - G_i) = exp(G_t - G_n) * exp(G_n - G_i)    (i < n <= t),
-// both factors <= 1, so those tiles are products on the matrix cores.
-// log alpha is clamped at -80 (alpha below 1.8e-35 acts as 1.8e-35; the
-// state it scales changes by at most that fraction).
+//          the state slice in registers, each chunk's operands streamed into
+//          LDS in two halves by direct global-to-LDS loads, double-buffered;
+//          O is written unnormalised; the final state is stored once and the
+//          ring gets the sequence's last raw tokens;
+//   finish (per token x head): the gated RMSNorm of O.
 #include "kda_device.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -44,21 +47,27 @@
 namespace kda {
 
 constexpr int PC = 64;             // chunk length
-constexpr int PB = 16;             // sub-block for the decay factors
-constexpr int NB = PC / PB;        // sub-blocks per chunk
 constexpr int PD = 128;            // dk = dv handled by the prefill kernels
 constexpr int LR = PD + 4;         // padded LDS row of a [PC][PD] tile (floats)
 constexpr int LS = PC + 4;         // padded LDS row of a [PC][PC] tile
-constexpr float kLogAlphaMin = -80.0f;
+constexpr int NSB = PC / 4;        // 4-token sub-blocks per chunk
 
-// Workspace per (chunk slot, head), in floats.
-constexpr int WS_W = 0;                    // W      [PC][PD]
-constexpr int WS_U = WS_W + PC * PD;       // Ut     [PC][PD]
-constexpr int WS_QG = WS_U + PC * PD;      // exp(G) * qh            [PC][PD]
-constexpr int WS_KC = WS_QG + PC * PD;     // exp(G_last - G) * kh   [PC][PD]
-constexpr int WS_P = WS_KC + PC * PD;      // P (causal, incl. diagonal) [PC][PC]
-constexpr int WS_GAMMA = WS_P + PC * PC;   // exp(G_last)            [PD]
-constexpr int WS_PER = WS_GAMMA + PD;
+// Workspace per (chunk slot, head), in bytes.  A fragment is one 16x16x32
+// MFMA operand for a wave: 64 lanes x 8 fp16 hi values, then 64 x 8 lo.
+// Half h of a chunk (tokens 32h..32h+31 for the token-indexed operands)
+// holds, in this order: -W tiles (2 x 4), scaled-Q tiles (2 x 4), scaled-K
+// tiles for that half of the tokens (8), and the P tiles of its rows.
+constexpr int FRAG_B = 2048;
+constexpr int HALF_FRAGS = 28;
+constexpr int HALF_B = HALF_FRAGS * FRAG_B;
+constexpr int UT_OFF = 2 * HALF_B;             // Ut, FP32, D-tile order
+constexpr int GAM_OFF = UT_OFF + PC * PD * 4;  // total decay of the chunk [PD]
+constexpr int WS_B = GAM_OFF + PD * 4;
+
+__device__ __forceinline__ int frag_w(int u, int kb) { return 4 * u + kb; }
+__device__ __forceinline__ int frag_q(int u, int kb) { return 8 + 4 * u + kb; }
+__device__ __forceinline__ int frag_k(int ct) { return 16 + ct; }
+__device__ __forceinline__ int frag_p(int hh, int u, int kb) { return 24 + u * (hh + 1) + kb; }
 
 // Chunk slot of chunk c of sequence s: floor(lo / 64) + s + c.  Distinct for
 // all (s, c) of monotone cu_seqlens and below ceil(total / 64) + num_seqs.
@@ -69,7 +78,7 @@ __device__ __forceinline__ int64_t chunk_slot(int lo, int s, int c) {
 size_t prefill_workspace_bytes(const kda_shape& sh, int32_t num_seqs, int64_t total_tokens) {
     if (sh.head_k != PD || sh.head_v != PD) return 0;
     const int64_t slots = (total_tokens + PC - 1) / PC + num_seqs;
-    return (size_t)slots * sh.num_heads * WS_PER * sizeof(float);
+    return (size_t)slots * sh.num_heads * WS_B;
 }
 
 struct SeqView {
@@ -99,553 +108,819 @@ __device__ __forceinline__ bool seq_view(const PrefillArgs& a, int s, bool repor
     return true;
 }
 
-// Raw activation of history token `lt` (local index within the sequence,
-// may be negative) for channel `ch` of the q|k|v layout: the packed input for
-// lt >= 0, the ring for earlier positions >= 0, else zero.
+// Eight consecutive activations, widened to FP32 (16-byte aligned).
 template <int ACT>
-__device__ __forceinline__ float hist_raw(const PrefillArgs& a, const SeqView& v, int h,
-                                          int lt, const void* src, int src_dim, int src_ch,
-                                          int ring_ch) {
-    constexpr int C = 3 * PD;
-    if (lt >= 0) return ld_act<ACT>(src, ((int64_t)(v.lo + lt) * a.H + h) * src_dim + src_ch);
-    const int p = v.pos + lt;
-    if (p < 0) return 0.f;
-    return ld_act<ACT>(a.ring,
-                       (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * a.H + h) * C + ring_ch);
+__device__ __forceinline__ void ld8(const void* base, int64_t idx, float (&x)[8]) {
+    if constexpr (ACT == kF32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        const float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+        x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
+        x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
+        x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
+        x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+    }
+}
+
+// Raw channels [ch0, ch0 + 8) of one of q|k|v for local chunk token lt
+// (-3 <= lt < 64): the packed input inside the sequence, the ring for
+// earlier positions >= 0, zero before position 0 and past the chunk's end.
+// Branch-free: the load always goes to a valid address (the chunk's first
+// token when the value is zero) and the value is selected afterwards, so
+// all of a lane's loads are in flight together.
+template <int ACT>
+__device__ __forceinline__ void raw8(const PrefillArgs& a, const SeqView& v, int h, int t0,
+                                     int L, int lt, const void* src, int ch0, int ring_ch0,
+                                     float (&x)[8]) {
+    const int gt = t0 + lt;
+    const int p = v.pos + gt;
+    const bool in_seq = gt >= 0;
+    const bool ok = lt < L && (in_seq || p >= 0);
+    const bool use_ring = ok && !in_seq;
+    const int64_t idx_in = ((int64_t)(v.lo + (ok && in_seq ? gt : t0)) * a.H + h) * PD + ch0;
+    const int64_t idx_ring =
+        (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * a.H + h) * (3 * PD) + ring_ch0;
+    ld8<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in, x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
+}
+
+// Sum over each row of 16 lanes; every lane of the row gets the same value.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_mov<0x128>(x);   // row_ror:8
+    x += dpp_mov<0x124>(x);   // row_ror:4
+    x += dpp_mov<0x122>(x);   // row_ror:2
+    x += dpp_mov<0x121>(x);   // row_ror:1
+    return x;
+}
+
+__device__ __forceinline__ void ld4x2(const float* p0, const float* p1, float (&x)[8]) {
+    const float4 a = *reinterpret_cast<const float4*>(p0);
+    const float4 b = *reinterpret_cast<const float4*>(p1);
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void st_frag(char* dst, int lane, const SplitOp& sp) {
+    *reinterpret_cast<f16x8_t*>(dst + lane * 16) = sp.hi;
+    *reinterpret_cast<f16x8_t*>(dst + 1024 + lane * 16) = sp.lo;
+}
+
+// Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
+// [c0, c0 + 8); zero for tokens at or past L.
+template <int ACT>
+__device__ __forceinline__ void conv4x8(const PrefillArgs& a, const SeqView& v, int h, int t0,
+                                        int L, int tb, const void* src, const float* w,
+                                        int c0, int ring_c0, float (&c)[4][8]) {
+    float x[7][8];
+#pragma unroll
+    for (int m = 0; m < 7; ++m) raw8<ACT>(a, v, h, t0, L, tb - 3 + m, src, c0, ring_c0, x[m]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(w + ((size_t)h * PD + c0 + q) * kConvW);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = w4.x * x[e][q];
+            acc = fmaf(w4.y, x[e + 1][q], acc);
+            acc = fmaf(w4.z, x[e + 2][q], acc);
+            acc = fmaf(w4.w, x[e + 3][q], acc);
+            c[e][q] = tb + e < L ? acc : 0.f;
+        }
+    }
 }
 
 // ---------------------------------------------------------------- chunk
 
 template <int ACT>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int cps) {
-    __shared__ float Qn[PC][LR];       // normalised q, later the conv of v
-    __shared__ float Kn[PC][LR];       // normalised k
-    __shared__ float Gb[PC][LR];       // block-local prefix sums of log alpha
-    __shared__ float Am[PC][LS];       // beta_t * (K K^T decayed), strictly lower
-    __shared__ float Pm[PC][LS];       // (Q K^T decayed), lower incl. diagonal
-    __shared__ float Tm[PC][LS];       // (I + A)^-1
-    __shared__ float Bt[NB][PD];       // block totals of log alpha
+    __shared__ float KD[PC][LR];       // kh * (alpha over the sub-block start..t)
+    __shared__ float QD[PC][LR];       // qh * the same; later beta * V
+    __shared__ float KE[PC][LR];       // kh * (alpha over t+1..sub-block end); later -W
+    __shared__ float Am[PC][LS];       // beta_t kh_t.kh_i e(t,i), strictly lower; T_bb on the diagonal later
+    __shared__ float Pm[PC][LS];       // qh_t.kh_i e(t,i), lower incl. diagonal
+    __shared__ float T4[NSB][PD];      // alpha product over each sub-block
+    __shared__ float AUX[2 * NSB][PD]; // step 2: per-wave suffix tables; then prefix | suffix tables
     __shared__ float bet[PC];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int H = a.H;
-    const int h = blockIdx.y;
-    const int s = blockIdx.x / cps, cc = blockIdx.x % cps;
+    const int per_c = a.num_seqs * H;
+    // later chunks first, so the first chunks are the most recently written
+    const int cc = cps - 1 - (int)(blockIdx.x / per_c);
+    const int rem = (int)(blockIdx.x % per_c);
+    const int s = rem / H, h = rem % H;
     SeqView v;
     if (!seq_view(a, s, cc == 0 && h == 0 && tid == 0, v)) return;
     const int t0 = cc * PC;
     if (t0 >= v.len) return;
     const int L = min(PC, v.len - t0);
-    float* ws = static_cast<float*>(a.workspace) +
-                ((size_t)chunk_slot(v.lo, s, cc) * H + h) * WS_PER;
+    char* ws = static_cast<char*>(a.workspace) + ((size_t)chunk_slot(v.lo, s, cc) * H + h) * WS_B;
 
-    // zero A, P (upper parts and unused tiles stay zero)
-    for (int e = tid; e < PC * LS; e += 256) {
-        (&Am[0][0])[e] = 0.f;
-        (&Pm[0][0])[e] = 0.f;
-    }
-
-    // ---- 1. conv of q (threads 0..127) and k (128..255), one channel each
+    // ---- 1. per lane: sub-block j = g of row block `wave` (tokens tb..tb+3),
+    // channels c0..c0+7: conv, L2 norms, decay products, in-sub-block pairs
+    const int tb = 16 * wave + 4 * g;
+    const int c0 = 8 * n;
+    float cv[4][8], bt[4];
     {
-        const int ch = tid & (PD - 1);
-        const bool isk = tid >= PD;
-        const void* src = isk ? a.k : a.q;
-        const float4 w4 = *reinterpret_cast<const float4*>(
-            (isk ? a.wk : a.wq) + ((size_t)h * PD + ch) * kConvW);
-        const int ring_ch = (isk ? PD : 0) + ch;
-        float x0 = hist_raw<ACT>(a, v, h, t0 - 3, src, PD, ch, ring_ch);
-        float x1 = hist_raw<ACT>(a, v, h, t0 - 2, src, PD, ch, ring_ch);
-        float x2 = hist_raw<ACT>(a, v, h, t0 - 1, src, PD, ch, ring_ch);
-        float (*dst)[LR] = isk ? Kn : Qn;
-#pragma unroll 16
-        for (int t = 0; t < PC; ++t) {
-            const float x3 =
-                t < L ? ld_act<ACT>(src, ((int64_t)(v.lo + t0 + t) * H + h) * PD + ch) : 0.f;
-            float c = w4.x * x0;
-            c = fmaf(w4.y, x1, c);
-            c = fmaf(w4.z, x2, c);
-            c = fmaf(w4.w, x3, c);
-            dst[t][ch] = t < L ? c : 0.f;
-            x0 = x1;
-            x1 = x2;
-            x2 = x3;
+        float qh[4][8], kh[4][8], al[4][8];
+        conv4x8<ACT>(a, v, h, t0, L, tb, a.q, a.wq, c0, c0, qh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float sq = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
+            const float r = a.q_scale / sqrtf(row16_sum(sq) + a.l2_eps);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
-    }
-    // ---- decay sums (threads 0..127) and beta (threads 128..191)
-    if (tid < PD) {
-        const int ch = tid;
-        float run = 0.f;
-        for (int t = 0; t < PC; ++t) {
-            if ((t % PB) == 0) run = 0.f;
-            float lg = 0.f;
-            if (t < L) {
-                const float al = ld_act<ACT>(a.alpha, ((int64_t)(v.lo + t0 + t) * H + h) * PD + ch);
-                lg = fmaxf(logf(al), kLogAlphaMin);
+        conv4x8<ACT>(a, v, h, t0, L, tb, a.k, a.wk, c0, PD + c0, kh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float sk = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sk = fmaf(kh[e][q], kh[e][q], sk);
+            const float r = 1.0f / sqrtf(row16_sum(sk) + a.l2_eps);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) kh[e][q] *= r;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
+            const int t = tb + e;
+            const int64_t row = (int64_t)(v.lo + t0 + min(t, L - 1)) * H + h;
+            ld8<ACT>(a.alpha, row * PD + c0, al[e]);
+            const float b = ld_act<ACT>(a.beta, row);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) al[e][q] = t < L ? al[e][q] : 1.f;
+            bt[e] = t < L ? b : 0.f;
+        }
+        conv4x8<ACT>(a, v, h, t0, L, tb, a.v, a.wv, c0, 2 * PD + c0, cv);
+
+        // pairs inside the sub-block: e(t, i) = alpha over i+1..t
+        float pp[10], pa[6];
+        {
+            int ip = 0, ia = 0;
+#pragma unroll
+            for (int ei = 0; ei < 4; ++ei) {
+                float d[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) d[q] = 1.f;
+#pragma unroll
+                for (int et = ei; et < 4; ++et) {
+                    if (et > ei) {
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) d[q] *= al[et][q];
+                    }
+                    float sp = 0.f, sa = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float kd = kh[ei][q] * d[q];
+                        sp = fmaf(qh[et][q], kd, sp);
+                        sa = fmaf(kh[et][q], kd, sa);
+                    }
+                    pp[ip++] = row16_sum(sp);
+                    if (et > ei) pa[ia++] = row16_sum(sa);
+                }
             }
-            run += lg;
-            Gb[t][ch] = run;
-            if ((t % PB) == PB - 1) Bt[t / PB][ch] = run;
         }
-    } else if (tid < PD + PC) {
-        const int t = tid - PD;
-        bet[t] = t < L ? ld_act<ACT>(a.beta, (int64_t)(v.lo + t0 + t) * H + h) : 0.f;
+        if (n == 0) {
+            // 4x4 sub-tiles on the diagonal, zeros above
+            int ip = 0, ia = 0;
+            float P4[4][4], A4[4][4];
+#pragma unroll
+            for (int ei = 0; ei < 4; ++ei)
+#pragma unroll
+                for (int et = 0; et < 4; ++et) {
+                    P4[et][ei] = 0.f;
+                    A4[et][ei] = 0.f;
+                }
+#pragma unroll
+            for (int ei = 0; ei < 4; ++ei)
+#pragma unroll
+                for (int et = ei; et < 4; ++et) {
+                    P4[et][ei] = pp[ip++];
+                    if (et > ei) A4[et][ei] = bt[et] * pa[ia++];
+                }
+#pragma unroll
+            for (int et = 0; et < 4; ++et) {
+                *reinterpret_cast<float4*>(&Pm[tb + et][tb]) =
+                    make_float4(P4[et][0], P4[et][1], P4[et][2], P4[et][3]);
+                *reinterpret_cast<float4*>(&Am[tb + et][tb]) =
+                    make_float4(A4[et][0], A4[et][1], A4[et][2], A4[et][3]);
+                bet[tb + et] = bt[et];
+            }
+        }
+
+        // decay products inside the sub-block
+        float D4[4][8], E4[4][8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            D4[0][q] = al[0][q];
+            E4[3][q] = 1.f;
+        }
+#pragma unroll
+        for (int e = 1; e < 4; ++e)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) D4[e][q] = D4[e - 1][q] * al[e][q];
+#pragma unroll
+        for (int e = 2; e >= 0; --e)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) E4[e][q] = E4[e + 1][q] * al[e + 1][q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float* kd = &KD[tb + e][c0];
+            float* qd = &QD[tb + e][c0];
+            float* ke = &KE[tb + e][c0];
+            *reinterpret_cast<float4*>(kd) = make_float4(kh[e][0] * D4[e][0], kh[e][1] * D4[e][1],
+                                                         kh[e][2] * D4[e][2], kh[e][3] * D4[e][3]);
+            *reinterpret_cast<float4*>(kd + 4) = make_float4(kh[e][4] * D4[e][4], kh[e][5] * D4[e][5],
+                                                             kh[e][6] * D4[e][6], kh[e][7] * D4[e][7]);
+            *reinterpret_cast<float4*>(qd) = make_float4(qh[e][0] * D4[e][0], qh[e][1] * D4[e][1],
+                                                         qh[e][2] * D4[e][2], qh[e][3] * D4[e][3]);
+            *reinterpret_cast<float4*>(qd + 4) = make_float4(qh[e][4] * D4[e][4], qh[e][5] * D4[e][5],
+                                                             qh[e][6] * D4[e][6], qh[e][7] * D4[e][7]);
+            *reinterpret_cast<float4*>(ke) = make_float4(kh[e][0] * E4[e][0], kh[e][1] * E4[e][1],
+                                                         kh[e][2] * E4[e][2], kh[e][3] * E4[e][3]);
+            *reinterpret_cast<float4*>(ke + 4) = make_float4(kh[e][4] * E4[e][4], kh[e][5] * E4[e][5],
+                                                             kh[e][6] * E4[e][6], kh[e][7] * E4[e][7]);
+        }
+        *reinterpret_cast<float4*>(&T4[tb >> 2][c0]) =
+            make_float4(D4[3][0], D4[3][1], D4[3][2], D4[3][3]);
+        *reinterpret_cast<float4*>(&T4[tb >> 2][c0 + 4]) =
+            make_float4(D4[3][4], D4[3][5], D4[3][6], D4[3][7]);
     }
     __syncthreads();
 
-    // ---- 2. L2 norms: wave w normalises tokens 16w..16w+15
-    for (int tl = 0; tl < PB; ++tl) {
-        const int t = wave * PB + tl;
-        const float q0 = Qn[t][lane], q1 = Qn[t][lane + 64];
-        const float k0 = Kn[t][lane], k1 = Kn[t][lane + 64];
-        const float sq = wave_sum(q0 * q0 + q1 * q1);
-        const float sk = wave_sum(k0 * k0 + k1 * k1);
-        const float rq = a.q_scale / sqrtf(sq + a.l2_eps);
-        const float rk = 1.0f / sqrtf(sk + a.l2_eps);
-        Qn[t][lane] = q0 * rq;
-        Qn[t][lane + 64] = q1 * rq;
-        Kn[t][lane] = k0 * rk;
-        Kn[t][lane + 64] = k1 * rk;
-    }
-    __syncthreads();
-
-    // ---- 3. scaled q and k for the state pass, and exp(G_last)
-    for (int e = tid; e < PC * PD; e += 256) {
-        const int t = e / PD, c = e % PD, bt = t / PB;
-        float before = 0.f, after = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (b < bt) before += Bt[b][c];
-            if (b > bt) after += Bt[b][c];
-        }
-        const float gpre = before + Gb[t][c];                 // G_t
-        const float gsuf = (Bt[bt][c] - Gb[t][c]) + after;    // G_last - G_t
-        ws[WS_QG + e] = Qn[t][c] * expf(gpre);
-        ws[WS_KC + e] = Kn[t][c] * expf(gsuf);
-    }
-    if (tid < PD) {
-        float tot = 0.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) tot += Bt[b][tid];
-        ws[WS_GAMMA + tid] = expf(tot);
-    }
-
-    // ---- 4a. diagonal 16-token blocks, elementwise: wave w owns block w
-    {
-        const int base = wave * PB;
-        for (int p = lane; p < PB * (PB + 1) / 2; p += 64) {
-            int tl = 0;
-            while ((tl + 1) * (tl + 2) / 2 <= p) ++tl;
-            const int il = p - tl * (tl + 1) / 2;
-            const int t = base + tl, i = base + il;
-            float sa = 0.f, sp = 0.f;
-            for (int c = 0; c < PD; ++c) {
-                const float e = expf(Gb[t][c] - Gb[i][c]);
-                const float ki = Kn[i][c] * e;
-                sa = fmaf(Kn[t][c], ki, sa);
-                sp = fmaf(Qn[t][c], ki, sp);
-            }
-            Am[t][i] = il < tl ? bet[t] * sa : 0.f;
-            Pm[t][i] = sp;
-        }
-    }
-    // ---- 4b. tiles below the diagonal on the matrix cores: wave w owns row
-    // block w; reference n0 = 16w (first token of the row block)
+    // ---- 2a. wave w >= 1: suffix table AUX[o + j] = alpha over sub-blocks
+    // j+1 .. 4w-1, for j < 4w (the column factors of the tiles left of the
+    // diagonal block)
+    const int aux_o = 2 * wave * (wave - 1);
     if (wave > 0) {
-        const int n0 = wave * PB;
-        const int t = n0 + n;                     // A-operand row of this lane
-        SplitOp kl[4], ql[4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int c = lane + 64 * half;
+            float run = 1.f;
+            for (int jj = 4 * wave - 1; jj >= 0; --jj) {
+                AUX[aux_o + jj][c] = run;
+                run *= T4[jj][c];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 2b. cross-sub-block entries of A and P on the matrix cores; wave w
+    // owns row block w.  Diagonal 16x16 block: adjacent sub-blocks through
+    // their common boundary ("adj"), sub-blocks two or three apart through
+    // the boundary before local sub-block 2 ("J2").  Tiles left of it:
+    // through the row block's first boundary.
+    {
+        const int t = 16 * wave + n;              // A-operand row of this lane
+        const int i = 16 * wave + n;              // B-operand column of this lane
+        f32x4_t aA1 = {0.f, 0.f, 0.f, 0.f}, aP1 = aA1, aA2 = aA1, aP2 = aA1;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            float xk[8], xq[8];
+            const int cb = 32 * kb + 8 * g;
+            float rk[8], rq[8], ck[8], f3[8], f1[8];
+            ld4x2(&KD[t][cb], &KD[t][cb + 4], rk);
+            ld4x2(&QD[t][cb], &QD[t][cb + 4], rq);
+            ld4x2(&KE[i][cb], &KE[i][cb + 4], ck);
+            ld4x2(&T4[4 * wave + 2][cb], &T4[4 * wave + 2][cb + 4], f3);
+            ld4x2(&T4[4 * wave + 1][cb], &T4[4 * wave + 1][cb + 4], f1);
+            float rk2[8], rq2[8], ck2[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                const int c = 32 * kb + 8 * g + q;
-                const float e = expf(Gb[t][c] - Gb[n0][c]);
-                xk[q] = Kn[t][c] * e;
-                xq[q] = Qn[t][c] * e;
+                const float fr = n >= 12 ? f3[q] : 1.f;
+                const float fc = n < 4 ? f1[q] : 1.f;
+                rk2[q] = rk[q] * fr;
+                rq2[q] = rq[q] * fr;
+                ck2[q] = ck[q] * fc;
             }
-            kl[kb] = split_op(xk);
-            ql[kb] = split_op(xq);
+            const SplitOp sck = split_op(ck), sck2 = split_op(ck2);
+            aA1 = mma3(split_op(rk), sck, aA1);
+            aP1 = mma3(split_op(rq), sck, aP1);
+            aA2 = mma3(split_op(rk2), sck2, aA2);
+            aP2 = mma3(split_op(rq2), sck2, aP2);
         }
-        for (int bi = 0; bi < wave; ++bi) {
-            const int i = bi * PB + n;            // B-operand column of this lane
-            f32x4_t accA = {0.f, 0.f, 0.f, 0.f}, accP = accA;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                float xr[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int c = 32 * kb + 8 * g + q;
-                    float r = Bt[bi][c] - Gb[i][c];
-                    for (int b = bi + 1; b < wave; ++b) r += Bt[b][c];
-                    r += Gb[n0][c];
-                    xr[q] = Kn[i][c] * expf(r);
-                }
-                const SplitOp kr = split_op(xr);
-                accA = mma3(kl[kb], kr, accA);
-                accP = mma3(ql[kb], kr, accP);
+        for (int r = 0; r < 4; ++r) {
+            const int tl = 4 * g + r, jtl = g, jil = n >> 2;
+            if (jil < jtl) {
+                const bool adj = jtl - jil == 1;
+                Am[16 * wave + tl][16 * wave + n] = bet[16 * wave + tl] * (adj ? aA1[r] : aA2[r]);
+                Pm[16 * wave + tl][16 * wave + n] = adj ? aP1[r] : aP2[r];
+            } else if (jil > jtl) {
+                Am[16 * wave + tl][16 * wave + n] = 0.f;
+                Pm[16 * wave + tl][16 * wave + n] = 0.f;
             }
+        }
+        // tiles right of the diagonal block are zero
+        for (int bi = wave + 1; bi < 4; ++bi)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tr = n0 + 4 * g + r;
-                Am[tr][bi * PB + n] = bet[tr] * accA[r];
-                Pm[tr][bi * PB + n] = accP[r];
+                Am[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
+                Pm[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
             }
-        }
-    }
-    __syncthreads();
-
-    // ---- 5. wave 0: T = (I + A)^-1, lane i owns column i (forward
-    // substitution); waves 1..3: conv of v into Qn, and P to the workspace
-    if (wave == 0) {
-        const int i = lane;
-        float x[PC];
+        if (wave > 0) {
+            // row operand: scaled to the row block's first token
+            const int jtl = n >> 2;
+            SplitOp xk[4], xq[4];
 #pragma unroll
-        for (int t = 0; t < PC; ++t) x[t] = 0.f;
-#pragma unroll
-        for (int t = 0; t < PC; ++t) {
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-            for (int s4 = 0; s4 < t; s4 += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&Am[t][s4]);
-                a0 = fmaf(a4.x, x[s4], a0);
-                a1 = fmaf(a4.y, x[s4 + 1], a1);
-                a2 = fmaf(a4.z, x[s4 + 2], a2);
-                a3 = fmaf(a4.w, x[s4 + 3], a3);
-            }
-            const float acc = (a0 + a1) + (a2 + a3);
-            x[t] = t < i ? 0.f : (t == i ? 1.f : -acc);
-        }
-#pragma unroll
-        for (int t = 0; t < PC; ++t) Tm[t][i] = x[t];
-    } else {
-        const int ch = tid - 64;                  // 0..191
-        if (ch < PD) {
-            const float4 w4 =
-                *reinterpret_cast<const float4*>(a.wv + ((size_t)h * PD + ch) * kConvW);
-            const int ring_ch = 2 * PD + ch;
-            float x0 = hist_raw<ACT>(a, v, h, t0 - 3, a.v, PD, ch, ring_ch);
-            float x1 = hist_raw<ACT>(a, v, h, t0 - 2, a.v, PD, ch, ring_ch);
-            float x2 = hist_raw<ACT>(a, v, h, t0 - 1, a.v, PD, ch, ring_ch);
-#pragma unroll 16
-            for (int t = 0; t < PC; ++t) {
-                const float x3 =
-                    t < L ? ld_act<ACT>(a.v, ((int64_t)(v.lo + t0 + t) * H + h) * PD + ch) : 0.f;
-                float c = w4.x * x0;
-                c = fmaf(w4.y, x1, c);
-                c = fmaf(w4.z, x2, c);
-                c = fmaf(w4.w, x3, c);
-                Qn[t][ch] = t < L ? c : 0.f;
-                x0 = x1;
-                x1 = x2;
-                x2 = x3;
-            }
-        }
-        for (int e = tid - 64; e < PC * PC; e += 192) {
-            const int t = e / PC, i = e % PC;
-            ws[WS_P + e] = Pm[t][i];
-        }
-    }
-    __syncthreads();
-
-    // ---- 6. W = T diag(beta) (exp(G) * K) and Ut = T diag(beta) V on the
-    // matrix cores: wave w owns value/key columns 32w..32w+31
-    {
-        SplitOp ta[4][2];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float x[8];
-                const int t = 16 * tt + n;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) x[q] = Tm[t][32 * kb + 8 * g + q];
-                ta[tt][kb] = split_op(x);
-            }
-#pragma unroll
-        for (int cl = 0; cl < 2; ++cl) {
-            const int c = 32 * wave + 16 * cl + n;   // B-operand column of this lane
-            f32x4_t accW[4], accU[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                accW[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                accU[tt] = accW[tt];
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float xw[8], xu[8];
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cb = 32 * kb + 8 * g;
+                float rk[8], rq[8], t0f[8], t1f[8], t2f[8];
+                ld4x2(&KD[t][cb], &KD[t][cb + 4], rk);
+                ld4x2(&QD[t][cb], &QD[t][cb + 4], rq);
+                ld4x2(&T4[4 * wave][cb], &T4[4 * wave][cb + 4], t0f);
+                ld4x2(&T4[4 * wave + 1][cb], &T4[4 * wave + 1][cb + 4], t1f);
+                ld4x2(&T4[4 * wave + 2][cb], &T4[4 * wave + 2][cb + 4], t2f);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const int i = 32 * kb + 8 * g + q, bi = i / PB;
-                    float gpre = Gb[i][c];
-                    for (int b = 0; b < bi; ++b) gpre += Bt[b][c];
-                    xw[q] = bet[i] * Kn[i][c] * expf(gpre);
-                    xu[q] = bet[i] * Qn[i][c];
+                    float f = jtl >= 1 ? t0f[q] : 1.f;
+                    f *= jtl >= 2 ? t1f[q] : 1.f;
+                    f *= jtl >= 3 ? t2f[q] : 1.f;
+                    rk[q] *= f;
+                    rq[q] *= f;
                 }
-                const SplitOp bw = split_op(xw), bu = split_op(xu);
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    if (32 * kb > 16 * tt + 15) continue;   // T is lower triangular
-                    accW[tt] = mma3(ta[tt][kb], bw, accW[tt]);
-                    accU[tt] = mma3(ta[tt][kb], bu, accU[tt]);
-                }
+                xk[kb] = split_op(rk);
+                xq[kb] = split_op(rq);
             }
+            for (int bi = 0; bi < wave; ++bi) {
+                const int ic = 16 * bi + n;
+                const int ji = ic >> 2;
+                f32x4_t A = {0.f, 0.f, 0.f, 0.f}, P = A;
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt)
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int cb = 32 * kb + 8 * g;
+                    float ck[8], sf[8];
+                    ld4x2(&KE[ic][cb], &KE[ic][cb + 4], ck);
+                    ld4x2(&AUX[aux_o + ji][cb], &AUX[aux_o + ji][cb + 4], sf);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) ck[q] *= sf[q];
+                    const SplitOp sck = split_op(ck);
+                    A = mma3(xk[kb], sck, A);
+                    P = mma3(xq[kb], sck, P);
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * tt + 4 * g + r;
-                    ws[WS_W + t * PD + c] = accW[tt][r];
-                    ws[WS_U + t * PD + c] = accU[tt][r];
+                    const int tr = 16 * wave + 4 * g + r;
+                    Am[tr][ic] = bet[tr] * A[r];
+                    Pm[tr][ic] = P[r];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 3a. prefix / suffix products over whole sub-blocks, and the
+    // chunk's total decay
+    if (tid < PD) {
+        float run = 1.f;
+#pragma unroll
+        for (int jj = 0; jj < NSB; ++jj) {
+            AUX[jj][tid] = run;
+            run *= T4[jj][tid];
+        }
+        reinterpret_cast<float*>(ws + GAM_OFF)[tid] = run;
+    } else {
+        const int c = tid - PD;
+        float run = 1.f;
+#pragma unroll
+        for (int jj = NSB - 1; jj >= 0; --jj) {
+            AUX[NSB + jj][c] = run;
+            run *= T4[jj][c];
+        }
+    }
+    __syncthreads();
+
+    // ---- 3b. wave 0: T_bb = (I + A_bb)^-1 for the four diagonal blocks,
+    // in place (lane = block * 16 + column).  Waves 1..3: scaled-Q,
+    // scaled-K and P fragments to the workspace.
+    if (wave == 0) {
+        const int b = lane >> 4, ic = lane & 15;
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            float acc = 0.f;
+#pragma unroll
+            for (int s4 = 0; s4 < t; s4 += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 * b + t][16 * b + s4]);
+                acc = fmaf(a4.x, x[s4], acc);
+                acc = fmaf(a4.y, x[s4 + 1], acc);
+                acc = fmaf(a4.z, x[s4 + 2], acc);
+                acc = fmaf(a4.w, x[s4 + 3], acc);
+            }
+            x[t] = t < ic ? 0.f : (t == ic ? 1.f : -acc);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Am[16 * b + t][16 * b + ic] = x[t];
+    } else {
+        for (int f = wave - 1; f < 38; f += 3) {
+            float x[8];
+            char* dst;
+            if (f < 16) {                      // (e(t,-1) * qh) rows, A operand
+                const int tt = f >> 2, kb = f & 3;
+                const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
+                float qd[8], pr[8];
+                ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
+                ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q];
+                dst = ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B;
+            } else if (f < 32) {               // (e(last,t) * kh)^T, A operand
+                const int ct = (f - 16) & 7, kb = (f - 16) >> 3;
+                const int c = 16 * ct + n;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int ts = 32 * kb + kslot(g, q);
+                    x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c];
+                }
+                dst = ws + kb * HALF_B + frag_k(ct) * FRAG_B;
+            } else {                           // P rows, A operand
+                const int p = f - 32;
+                const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
+                const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
+                ld4x2(&Pm[t][cb], &Pm[t][cb + 16], x);
+                dst = ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B;
+            }
+            st_frag(dst, lane, split_op(x));
+        }
+    }
+    __syncthreads();
+
+    // ---- beta * V into the freed QD tile
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float* vd = &QD[tb + e][c0];
+        *reinterpret_cast<float4*>(vd) = make_float4(bt[e] * cv[e][0], bt[e] * cv[e][1],
+                                                     bt[e] * cv[e][2], bt[e] * cv[e][3]);
+        *reinterpret_cast<float4*>(vd + 4) = make_float4(bt[e] * cv[e][4], bt[e] * cv[e][5],
+                                                         bt[e] * cv[e][6], bt[e] * cv[e][7]);
+    }
+    __syncthreads();
+
+    // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
+    // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns
+    // column tiles 4w..4w+3 of the 256 columns (waves 0-1: W, 2-3: Ut).
+    {
+        const bool isW = wave < 2;
+        f32x4_t X[4][4];
+        SplitOp4 Xs[3][4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            f32x4_t acc[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = 16 * ((4 * wave + u) & 7) + n;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * b + 4 * g + r;
+                    acc[u][r] = isW ? bet[t] * KD[t][c] * AUX[t >> 2][c] : QD[t][c];
+                }
+            }
+            if (b == 1) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 + n][4 * g]);
+                const float av[4] = {-a4.x, -a4.y, -a4.z, -a4.w};
+                const SplitOp4 sa = split_op4(av);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) acc[u] = mma3(sa, Xs[0][u], acc[u]);
+            } else if (b >= 2) {
+                float av[8];
+                ld4x2(&Am[16 * b + n][4 * g], &Am[16 * b + n][16 + 4 * g], av);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) av[q] = -av[q];
+                const SplitOp sa = split_op(av);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    SplitOp xb;
+                    xb.hi = __builtin_shufflevector(Xs[0][u].hi, Xs[1][u].hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                    xb.lo = __builtin_shufflevector(Xs[0][u].lo, Xs[1][u].lo, 0, 1, 2, 3, 4, 5, 6, 7);
+                    acc[u] = mma3(sa, xb, acc[u]);
+                }
+                if (b == 3) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(&Am[48 + n][32 + 4 * g]);
+                    const float a3[4] = {-a4.x, -a4.y, -a4.z, -a4.w};
+                    const SplitOp4 sa3 = split_op4(a3);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[u] = mma3(sa3, Xs[2][u], acc[u]);
+                }
+            }
+            const float4 t4 = *reinterpret_cast<const float4*>(&Am[16 * b + n][16 * b + 4 * g]);
+            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+            const SplitOp4 st = split_op4(tv);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                X[b][u] = mma3(st, split_op4(acc[u]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+                if (b < 3) Xs[b][u] = split_op4(X[b][u]);
+            }
+        }
+        if (isW) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int c = 16 * (4 * wave + u) + n;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) KE[16 * b + 4 * g + r][c] = -X[b][u][r];
+                }
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int j16 = 4 * (wave - 2) + u;
+                    const int hh = b >> 1, uu = b & 1;
+                    *reinterpret_cast<f32x4_t*>(ws + UT_OFF +
+                                                ((((hh * 8 + j16) * 2 + uu) * 64 + lane) * 16)) = X[b][u];
                 }
         }
+    }
+    __syncthreads();
+
+    // ---- 5. -W fragments (A operand, k = key channel in pairing order)
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+        const int f = wave + 4 * k4;
+        const int tt = f >> 2, kb = f & 3;
+        const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
+        float x[8];
+        ld4x2(&KE[t][cb], &KE[t][cb + 16], x);
+        st_frag(ws + (tt >> 1) * HALF_B + frag_w(tt & 1, kb) * FRAG_B, lane, split_op(x));
     }
 }
 
 // ---------------------------------------------------------------- state
 
-template <int ST>
+__device__ __forceinline__ SplitOp ld_frag(const char* buf, int f, int lane) {
+    SplitOp o;
+    o.hi = *reinterpret_cast<const f16x8_t*>(buf + f * FRAG_B + lane * 16);
+    o.lo = *reinterpret_cast<const f16x8_t*>(buf + f * FRAG_B + 1024 + lane * 16);
+    return o;
+}
+
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// One half of a chunk's fragments into LDS: 56 pieces of 1 KB, wave w
+// copies pieces w, w+4, ...; lane l moves 16 bytes straight from global
+// memory to LDS (M0 holds the wave's LDS destination).  Issued as inline
+// assembly: the compiler would otherwise wait for these loads before every
+// LDS read of the other buffer.  The caller waits for them explicitly
+// (s_waitcnt vmcnt(0)) before the barrier that publishes the buffer.
+__device__ __forceinline__ void dma_half(const char* src, char* dst, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < HALF_B / 1024 / 4; ++q) {
+        const int piece = wave + 4 * q;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src + piece * 1024 + lane * 16),
+                       "{m0}"((lds_char_t*)(dst + piece * 1024))
+                     : "memory");
+    }
+}
+
+template <int ACT, int ST>
 __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
-    __shared__ float Ws[PC][LR];
-    __shared__ float Qs[PC][LR];
-    __shared__ float Ks[PC][LR];
-    __shared__ float Ps[PC][LS];
-    __shared__ float gam[PD];
+    __shared__ __attribute__((aligned(16))) char buf0[HALF_B];
+    __shared__ __attribute__((aligned(16))) char buf1[HALF_B];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
     const int H = a.H;
-    const int half = blockIdx.x & 1;
-    const int sh = blockIdx.x >> 1;
-    const int h = sh % H, s = sh / H;
+    // The buffers are filled only by the assembly loads above; this store,
+    // which never runs (num_seqs >= 1), keeps the compiler from treating
+    // them as never written.
+    if (a.num_seqs < 0) {
+        buf0[tid] = 0;
+        buf1[tid] = 0;
+    }
+    // the two column halves of one (sequence, head) sit eight workgroups
+    // apart, so both land on the same XCD and share its L2
+    const int G = a.num_seqs * H;
+    const int r16 = blockIdx.x & 15;
+    const int half = r16 >> 3;
+    const int p = (int)(blockIdx.x >> 4) * 8 + (r16 & 7);
+    if (p >= G) return;
+    const int s = p / H, h = p % H;
     SeqView v;
     if (!seq_view(a, s, false, v)) return;
     if (v.len == 0) return;
-    const int j0 = 64 * half + 16 * wave;          // this wave's value columns
+    const int j16 = 4 * half + wave;
+    const int jc = 16 * j16 + n;
     const size_t head_off = ((size_t)v.slot * H + h) * PD * PD;
 
-    // state slice S[c][j0 + n], c = 16 ct + 4 g + r, in the D-tile layout
-    f32x4_t S[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = 0.f;
-            if (v.pos > 0) {
-                const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + j0 + n;
-                x = ST == kF32 ? static_cast<const float*>(a.pool)[e]
-                               : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[e]);
-            }
-            S[ct][r] = x;
-        }
-
-    // The next chunk's operands are loaded into registers while the current
-    // chunk computes, then written to LDS after the step's barrier: one
-    // memory round trip per chunk, hidden behind the previous chunk's work.
-    constexpr int NF4 = PC * PD / 4 / 256;        // float4 per thread per [PC][PD] tile
-    constexpr int NP4 = PC * PC / 4 / 256;        // float4 per thread for P
-    float4 fw[NF4], fq[NF4], fk[NF4], fp[NP4];
-    float fu[16], fg = 0.f;
-    auto fetch = [&](int cc) {
-        const float* ws = static_cast<const float*>(a.workspace) +
-                          ((size_t)chunk_slot(v.lo, s, cc) * H + h) * WS_PER;
-#pragma unroll
-        for (int k = 0; k < NF4; ++k) {
-            const int e4 = tid + 256 * k;
-            const int t = e4 / (PD / 4), c = 4 * (e4 % (PD / 4));
-            fw[k] = *reinterpret_cast<const float4*>(ws + WS_W + t * PD + c);
-            fq[k] = *reinterpret_cast<const float4*>(ws + WS_QG + t * PD + c);
-            fk[k] = *reinterpret_cast<const float4*>(ws + WS_KC + t * PD + c);
-        }
-#pragma unroll
-        for (int k = 0; k < NP4; ++k) {
-            const int e4 = tid + 256 * k;
-            const int t = e4 / (PC / 4), i = 4 * (e4 % (PC / 4));
-            fp[k] = *reinterpret_cast<const float4*>(ws + WS_P + t * PC + i);
-        }
-        if (tid < PD) fg = ws[WS_GAMMA + tid];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                fu[4 * tt + r] = ws[WS_U + (16 * tt + 4 * g + r) * PD + j0 + n];
+    auto cws = [&](int c) -> const char* {
+        return static_cast<const char*>(a.workspace) +
+               ((size_t)chunk_slot(v.lo, s, c) * H + h) * WS_B;
+    };
+    auto ld_ut = [&](int c, int hh, int u) -> f32x4_t {
+        return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
+                                                 ((((hh * 8 + j16) * 2 + u) * 64 + lane) * 16));
+    };
+    auto ld_gam = [&](int c, int ct) -> f32x4_t {
+        return *reinterpret_cast<const f32x4_t*>(cws(c) + GAM_OFF + (16 * ct + 4 * g) * 4);
     };
 
     const int nch = (v.len + PC - 1) / PC;
-    fetch(0);
-    for (int cc = 0; cc < nch; ++cc) {
-        const int L = min(PC, v.len - cc * PC);
-        __syncthreads();                           // the previous chunk's LDS reads are done
+    dma_half(cws(0), buf0, wave, lane);
+    f32x4_t ut0[2] = {ld_ut(0, 0, 0), ld_ut(0, 0, 1)};
+    f32x4_t gm[8];
 #pragma unroll
-        for (int k = 0; k < NF4; ++k) {
-            const int e4 = tid + 256 * k;
-            const int t = e4 / (PD / 4), c = 4 * (e4 % (PD / 4));
-            *reinterpret_cast<float4*>(&Ws[t][c]) = fw[k];
-            *reinterpret_cast<float4*>(&Qs[t][c]) = fq[k];
-            *reinterpret_cast<float4*>(&Ks[t][c]) = fk[k];
-        }
-#pragma unroll
-        for (int k = 0; k < NP4; ++k) {
-            const int e4 = tid + 256 * k;
-            const int t = e4 / (PC / 4), i = 4 * (e4 % (PC / 4));
-            *reinterpret_cast<float4*>(&Ps[t][i]) = fp[k];
-        }
-        if (tid < PD) gam[tid] = fg;
-        f32x4_t U[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) U[tt][r] = fu[4 * tt + r];
-        if (cc + 1 < nch) fetch(cc + 1);
-        __syncthreads();
+    for (int ct = 0; ct < 8; ++ct) gm[ct] = ld_gam(0, ct);
 
-        // S as the B operand (k = key channel), stacked D-tile pairing
-        SplitOp sb[4];
+    // state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
+    f32x4_t S[8];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            float x[8];
+    for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (v.pos > 0) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                x[q] = S[2 * kb][q];
-                x[4 + q] = S[2 * kb + 1][q];
-            }
-            sb[kb] = split_op(x);
-        }
-        // U = Ut - W S
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int t = 16 * tt + n;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const float4 lo4 = *reinterpret_cast<const float4*>(&Ws[t][32 * kb + 4 * g]);
-                const float4 hi4 = *reinterpret_cast<const float4*>(&Ws[t][32 * kb + 16 + 4 * g]);
-                float x[8] = {-lo4.x, -lo4.y, -lo4.z, -lo4.w, -hi4.x, -hi4.y, -hi4.z, -hi4.w};
-                U[tt] = mma3(split_op(x), sb[kb], U[tt]);
-            }
-        }
-        // U as the B operand (k = token), stacked D-tile pairing
-        SplitOp ub[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float x[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                x[q] = U[2 * kb][q];
-                x[4 + q] = U[2 * kb + 1][q];
-            }
-            ub[kb] = split_op(x);
-        }
-        // O = (exp(G) * Q) S + P U, written unnormalised into y
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            const int t = 16 * tt + n;
-            f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const float4 lo4 = *reinterpret_cast<const float4*>(&Qs[t][32 * kb + 4 * g]);
-                const float4 hi4 = *reinterpret_cast<const float4*>(&Qs[t][32 * kb + 16 + 4 * g]);
-                float x[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-                o = mma3(split_op(x), sb[kb], o);
-            }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                if (32 * kb > 16 * tt + 15) continue;       // P is causal
-                const float4 lo4 = *reinterpret_cast<const float4*>(&Ps[t][32 * kb + 4 * g]);
-                const float4 hi4 = *reinterpret_cast<const float4*>(&Ps[t][32 * kb + 16 + 4 * g]);
-                float x[8] = {lo4.x, lo4.y, lo4.z, lo4.w, hi4.x, hi4.y, hi4.z, hi4.w};
-                o = mma3(split_op(x), ub[kb], o);
-            }
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tr = 16 * tt + 4 * g + r;
-                if (tr < L)
-                    a.y[((int64_t)(v.lo + cc * PC + tr) * H + h) * PD + j0 + n] = o[r];
+                const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
+                S[ct][r] = ST == kF32 ? static_cast<const float*>(a.pool)[e]
+                                      : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[e]);
+            }
+    }
+
+    // O of the previous half, stored after the next barrier so that the
+    // store latency overlaps the next half's work
+    f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    int orow0 = -1;
+    auto store_o = [&]() {
+        if (orow0 < 0) return;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tl = orow0 + 16 * u + 4 * g + r;
+                if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[u][r];
+            }
+    };
+
+    for (int cc = 0; cc < nch; ++cc) {
+        // ---- first half: tokens 0..31 of the chunk
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        dma_half(cws(cc) + HALF_B, buf1, wave, lane);
+        const f32x4_t ut1[2] = {ld_ut(cc, 1, 0), ld_ut(cc, 1, 1)};
+        store_o();
+
+        SplitOp sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
+        f32x4_t U0[2], O[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            U0[u] = ut0[u];
+            O[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                U0[u] = mma3(ld_frag(buf0, frag_w(u, kb), lane), sb[kb], U0[u]);
+                O[u] = mma3(ld_frag(buf0, frag_q(u, kb), lane), sb[kb], O[u]);
             }
         }
-        // S <- Diag(exp(G_last)) S + (exp(G_last - G) * K)^T U
+        const SplitOp ub0 = split_pair(U0[0], U0[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) O[u] = mma3(ld_frag(buf0, frag_p(0, u, 0), lane), ub0, O[u]);
+        f32x4_t Sn[8];
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            f32x4_t acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = gam[16 * ct + 4 * g + r] * S[ct][r];
-            const int c = 16 * ct + n;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float x[8];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) x[q] = Ks[32 * kb + kslot(g, q)][c];
-                acc = mma3(split_op(x), ub[kb], acc);
-            }
-            S[ct] = acc;
+            Sn[ct] = gm[ct] * S[ct];
+            Sn[ct] = mma3(ld_frag(buf0, frag_k(ct), lane), ub0, Sn[ct]);
         }
+        Oprev[0] = O[0];
+        Oprev[1] = O[1];
+        orow0 = cc * PC;
+
+        // ---- second half: tokens 32..63
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (cc + 1 < nch) {
+            dma_half(cws(cc + 1), buf0, wave, lane);
+            ut0[0] = ld_ut(cc + 1, 0, 0);
+            ut0[1] = ld_ut(cc + 1, 0, 1);
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) gm[ct] = ld_gam(cc + 1, ct);
+        }
+        store_o();
+
+        f32x4_t U1[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            U1[u] = ut1[u];
+            O[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                U1[u] = mma3(ld_frag(buf1, frag_w(u, kb), lane), sb[kb], U1[u]);
+                O[u] = mma3(ld_frag(buf1, frag_q(u, kb), lane), sb[kb], O[u]);
+            }
+        }
+        const SplitOp ub1 = split_pair(U1[0], U1[1]);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            O[u] = mma3(ld_frag(buf1, frag_p(1, u, 0), lane), ub0, O[u]);
+            O[u] = mma3(ld_frag(buf1, frag_p(1, u, 1), lane), ub1, O[u]);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            Sn[ct] = mma3(ld_frag(buf1, frag_k(ct), lane), ub1, Sn[ct]);
+            S[ct] = Sn[ct];
+        }
+        Oprev[0] = O[0];
+        Oprev[1] = O[1];
+        orow0 = cc * PC + 32;
     }
+    store_o();
 
     // typed store of the final state, once
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + j0 + n;
+            const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
             if (ST == kF32)
                 static_cast<float*>(a.pool)[e] = S[ct][r];
             else
                 static_cast<uint16_t*>(a.pool)[e] = (uint16_t)f32_to_bf16_rne(S[ct][r]);
         }
+
+    // ring: the sequence's last min(3, len) raw tokens (the chunk kernel,
+    // which read the old entries, has finished)
+    if (half == 0) {
+        constexpr int C = 3 * PD;
+        const int pend = v.pos + v.len;
+        const int pfirst = max(v.pos, pend - (kConvW - 1));
+        for (int pp = pfirst; pp < pend; ++pp) {
+            const int64_t row = v.lo + (pp - v.pos);
+            const int64_t dst = (((int64_t)v.slot * kConvW + (pp & (kConvW - 1))) * H + h) * C;
+            for (int ch = tid; ch < C; ch += 256) {
+                const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
+                st_act_bits<ACT>(a.ring, dst + ch,
+                                 ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------- finish
 
-// Gated RMSNorm of O (one wave per token and head), and in the first
-// workgroup of each (sequence, head) the ring update with the sequence's
-// last min(3, len) raw tokens.
+// Gated RMSNorm of O in place: 32 lanes per (token, head) row, four values
+// per lane.  Rows of sequences that are skipped are left untouched.
 template <int ACT>
-__global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a, int tpb) {
-    constexpr int C = 3 * PD;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int H = a.H;
-    const int h = blockIdx.y;
-    const int s = blockIdx.x / tpb, blk = blockIdx.x % tpb;
-    SeqView v;
-    if (!seq_view(a, s, false, v)) return;
-    if (blk == 0) {
-        const int pend = v.pos + v.len;
-        const int pfirst = max(v.pos, pend - (kConvW - 1));
-        for (int p = pfirst; p < pend; ++p) {
-            const int64_t row = v.lo + (p - v.pos);
-            const int64_t dst = (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * H + h) * C;
-            for (int ch = tid; ch < C; ch += 256) {
-                const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
-                const int sc = ch % PD;
-                st_act_bits<ACT>(a.ring, dst + ch, ld_act_bits<ACT>(src, (row * H + h) * PD + sc));
-            }
-        }
+__global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
+    const int tid = threadIdx.x, l32 = tid & 31;
+    const int64_t rows = a.total_tokens * a.H;
+    const int64_t row = (int64_t)blockIdx.x * 8 + (tid >> 5);
+    bool ok = row < rows;
+    const int64_t token = ok ? row / a.H : 0;
+    const int h = ok ? (int)(row % a.H) : 0;
+    // the sequence holding the token (cu_seqlens is monotone for valid input)
+    int lo_s = 0, hi_s = a.num_seqs;
+    while (hi_s - lo_s > 1) {
+        const int mid = (lo_s + hi_s) >> 1;
+        if (a.cu_seqlens[mid] <= token) lo_s = mid; else hi_s = mid;
     }
-    const int t = blk * 4 + wave;
-    if (t >= v.len) return;
-    const int64_t row = v.lo + t;
-    float* y = a.y + (row * H + h) * PD;
-    const float o0 = y[lane], o1 = y[lane + 64];
-    const float ms = wave_sum(o0 * o0 + o1 * o1);
-    const float rr = 1.0f / sqrtf(ms / (float)PD + a.norm_eps);
-    const float w0 = a.norm_w ? a.norm_w[lane] : 1.0f;
-    const float w1 = a.norm_w ? a.norm_w[lane + 64] : 1.0f;
-    const float g0 = ld_act<ACT>(a.g, (row * H + h) * PD + lane);
-    const float g1 = ld_act<ACT>(a.g, (row * H + h) * PD + lane + 64);
-    y[lane] = w0 * (o0 * rr) * gate_fn(a.gate, g0);
-    y[lane + 64] = w1 * (o1 * rr) * gate_fn(a.gate, g1);
+    SeqView v;
+    ok = ok && seq_view(a, lo_s, false, v) && token >= v.lo && token < v.lo + v.len;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    float* y = a.y + (ok ? row : 0) * PD + 4 * l32;
+    if (ok) o = *reinterpret_cast<const float4*>(y);
+    float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+    ss = row16_sum(ss);
+    ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));  // lane ^ 16
+    if (!ok) return;
+    const float rr = 1.0f / sqrtf(ss / (float)PD + a.norm_eps);
+    const float4 w = a.norm_w ? *reinterpret_cast<const float4*>(a.norm_w + 4 * l32)
+                              : make_float4(1.f, 1.f, 1.f, 1.f);
+    const int64_t gi = (token * a.H + h) * PD + 4 * l32;
+    const float g0 = ld_act<ACT>(a.g, gi), g1 = ld_act<ACT>(a.g, gi + 1);
+    const float g2 = ld_act<ACT>(a.g, gi + 2), g3 = ld_act<ACT>(a.g, gi + 3);
+    *reinterpret_cast<float4*>(y) =
+        make_float4(w.x * (o.x * rr) * gate_fn(a.gate, g0), w.y * (o.y * rr) * gate_fn(a.gate, g1),
+                    w.z * (o.z * rr) * gate_fn(a.gate, g2), w.w * (o.w * rr) * gate_fn(a.gate, g3));
 }
 
 template <int ACT, int ST>
 static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const int cps = (a.max_seqlen + PC - 1) / PC;
-    const int tpb = (a.max_seqlen + 3) / 4;
-    hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)a.num_seqs * cps, a.H),
-                       dim3(256), 0, stream, a, cps);
-    hipLaunchKernelGGL((prefill_state_kernel<ST>), dim3((unsigned)a.num_seqs * a.H * 2),
-                       dim3(256), 0, stream, a);
-    hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.num_seqs * tpb, a.H),
-                       dim3(256), 0, stream, a, tpb);
+    const int64_t nchunk = (int64_t)cps * a.num_seqs * a.H;
+    const int64_t G = (int64_t)a.num_seqs * a.H;
+    const int64_t sgrid = (G + 7) / 8 * 16;
+    const int64_t frows = (a.total_tokens * a.H + 7) / 8;
+    if (nchunk > 0)
+        hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)nchunk), dim3(256), 0,
+                           stream, a, cps);
+    if (sgrid > 0)
+        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid), dim3(256), 0,
+                           stream, a);
+    if (frows > 0)
+        hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)frows), dim3(256), 0,
+                           stream, a);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
