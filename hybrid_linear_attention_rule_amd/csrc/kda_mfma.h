@@ -11,8 +11,9 @@
 // passes of 16 cycles against 32 cycles per four-deep FP32 MFMA step.  A
 // bf16 pair (8 + 8 significant bits) was measured to leave ~2e-5 relative
 // error in the read-outs, too close to the FP32 parity bar.
-// Domain: |x| < 65504 for every operand (normalised keys and queries, decay
-// factors <= 1, bounded states and values all satisfy it).
+// Domain: |x| < 65504 for every (scaled) operand.  Values whose lo part
+// would fall below the fp16 normal range (|x| < 2^-3) lose precision, so
+// callers scale bounded operands up by a power of two first.
 //
 // Lane layout of one 16x16x32 MFMA (wave64), checked on gfx950 for bf16;
 // the f16 form has the same layout:
@@ -49,16 +50,17 @@ struct SplitOp4 {
     f16x4_t lo;
 };
 
-// Splits two FP32 values.  The pair is pinned in registers first: otherwise
-// FP contraction may fold the multiply that produced x into the conversion
-// (a fused multiply-convert for hi in one place and a separately rounded
-// product in another), and hi + lo would then miss x by one fp16 ulp.  hi is
-// one packed RNE conversion; x - hi is exact in FP32 and is formed by one
-// mixed-precision FMA that reads hi's fp16 halves directly; lo is one more
-// packed conversion.
+// Splits two FP32 values.  The pair is pinned in registers first by an empty
+// non-volatile asm that the compiler cannot see through but may still
+// schedule freely: otherwise FP contraction may fold the multiply that
+// produced x into the conversion (a fused multiply-convert for hi in one
+// place and a separately rounded product in another), and hi + lo would then
+// miss x by one fp16 ulp.  hi is one packed RNE conversion; x - hi is exact
+// in FP32 and is formed by one mixed-precision FMA that reads hi's fp16
+// halves directly; lo is one more packed conversion.
 __device__ __forceinline__ void split2(float x0, float x1, f16x2_t& hi, f16x2_t& lo) {
     f32x2_t xv = {x0, x1};
-    asm volatile("" : "+v"(xv));
+    asm("" : "+v"(xv));
     hi = __builtin_convertvector(xv, f16x2_t);
     float r0, r1;
     asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r0) : "v"(hi), "v"(xv[0]));
@@ -114,6 +116,16 @@ __device__ __forceinline__ f32x4_t mma3(const SplitOp& a, const SplitOp& b, f32x
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.lo, acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.hi, acc, 0, 0, 0);
     return acc;
+}
+
+// One of the three passes of a split product (0: lo*hi, 1: hi*lo, 2: hi*hi).
+// Issuing pass p for several independent accumulators before pass p + 1
+// keeps the matrix pipe busy instead of waiting on one accumulator chain.
+template <int P>
+__device__ __forceinline__ f32x4_t mma_pass(const SplitOp& a, const SplitOp& b, f32x4_t acc) {
+    if constexpr (P == 0) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.lo, b.hi, acc, 0, 0, 0);
+    else if constexpr (P == 1) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.lo, acc, 0, 0, 0);
+    else return __builtin_amdgcn_mfma_f32_16x16x32_f16(a.hi, b.hi, acc, 0, 0, 0);
 }
 
 // acc += a * b over one 16-deep k block.

@@ -44,6 +44,8 @@
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
+#include <type_traits>
+
 namespace kda {
 
 constexpr int PC = 64;             // chunk length
@@ -51,6 +53,16 @@ constexpr int PD = 128;            // dk = dv handled by the prefill kernels
 constexpr int LR = PD + 4;         // padded LDS row of a [PC][PD] tile (floats)
 constexpr int LS = PC + 4;         // padded LDS row of a [PC][PC] tile
 constexpr int NSB = PC / 4;        // 4-token sub-blocks per chunk
+
+// Matrix-core operands bounded by 1 in magnitude (normalised keys and
+// queries times decay factors, A and P) are multiplied by 2^12 before the
+// fp16 split, T_bb and W (bounded by 256 in practice) by 2^8: the split of a
+// value below 2^-3 would otherwise lose its lo part to fp16 subnormals, about
+// 3e-8 absolute per element, which small rows of P turn into output error.
+// Products are scaled back by exact powers of two.  Values (V, Ut, U, S) are
+// split unscaled.
+constexpr float kSc = 4096.f, kInvSc = 1.f / 4096.f, kInvSc2 = 1.f / 16777216.f;
+constexpr float kScW = 256.f, kInvScW = 1.f / 256.f;
 
 // Workspace per (chunk slot, head), in bytes.  A fragment is one 16x16x32
 // MFMA operand for a wave: 64 lanes x 8 fp16 hi values, then 64 x 8 lo.
@@ -108,44 +120,98 @@ __device__ __forceinline__ bool seq_view(const PrefillArgs& a, int s, bool repor
     return true;
 }
 
-// Eight consecutive activations, widened to FP32 (16-byte aligned).
+// Eight consecutive activations of one token, as loaded (16-byte aligned).
 template <int ACT>
-__device__ __forceinline__ void ld8(const void* base, int64_t idx, float (&x)[8]) {
+struct Raw8;
+template <>
+struct Raw8<kF32> {
+    float4 a, b;
+};
+template <>
+struct Raw8<kBF16> {
+    uint4 u;
+};
+
+template <int ACT>
+__device__ __forceinline__ Raw8<ACT> ld_raw8(const void* base, int64_t idx) {
+    Raw8<ACT> r;
     if constexpr (ACT == kF32) {
         const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-        const float4 a = p[0], b = p[1];
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        r.a = p[0];
+        r.b = p[1];
     } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-        x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xffff0000u);
-        x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xffff0000u);
-        x[4] = __uint_as_float(u.z << 16); x[5] = __uint_as_float(u.z & 0xffff0000u);
-        x[6] = __uint_as_float(u.w << 16); x[7] = __uint_as_float(u.w & 0xffff0000u);
+        r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
     }
+    return r;
+}
+
+// Widens to FP32; zero where !ok.
+template <int ACT>
+__device__ __forceinline__ void unpack8(const Raw8<ACT>& r, bool ok, float (&x)[8]) {
+    if constexpr (ACT == kF32) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+    } else {
+        x[0] = __uint_as_float(r.u.x << 16); x[1] = __uint_as_float(r.u.x & 0xffff0000u);
+        x[2] = __uint_as_float(r.u.y << 16); x[3] = __uint_as_float(r.u.y & 0xffff0000u);
+        x[4] = __uint_as_float(r.u.z << 16); x[5] = __uint_as_float(r.u.z & 0xffff0000u);
+        x[6] = __uint_as_float(r.u.w << 16); x[7] = __uint_as_float(r.u.w & 0xffff0000u);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
 }
 
 // Raw channels [ch0, ch0 + 8) of one of q|k|v for local chunk token lt
 // (-3 <= lt < 64): the packed input inside the sequence, the ring for
-// earlier positions >= 0, zero before position 0 and past the chunk's end.
-// Branch-free: the load always goes to a valid address (the chunk's first
-// token when the value is zero) and the value is selected afterwards, so
-// all of a lane's loads are in flight together.
+// earlier positions >= 0, zero before position 0 and past the chunk's end
+// (`ok` false).  Branch-free: the load always goes to a valid address (the
+// chunk's first token when the value is zero), so all of a lane's loads are
+// in flight together.
 template <int ACT>
-__device__ __forceinline__ void raw8(const PrefillArgs& a, const SeqView& v, int h, int t0,
-                                     int L, int lt, const void* src, int ch0, int ring_ch0,
-                                     float (&x)[8]) {
+__device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v, int h, int t0,
+                                          int L, int lt, const void* src, int ch0, int ring_ch0,
+                                          bool& ok) {
     const int gt = t0 + lt;
     const int p = v.pos + gt;
     const bool in_seq = gt >= 0;
-    const bool ok = lt < L && (in_seq || p >= 0);
+    ok = lt < L && (in_seq || p >= 0);
     const bool use_ring = ok && !in_seq;
     const int64_t idx_in = ((int64_t)(v.lo + (ok && in_seq ? gt : t0)) * a.H + h) * PD + ch0;
     const int64_t idx_ring =
         (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * a.H + h) * (3 * PD) + ring_ch0;
-    ld8<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in, x);
+    return ld_raw8<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in);
+}
+
+// Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
+// [c0, c0 + 8), from the seven raw tokens tb-3..tb+3; zero for tokens at or
+// past L.
+template <int ACT>
+__device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[7],
+                                        const float* w, int h, int c0, int tb, int L,
+                                        float (&c)[4][8]) {
+    float x[7][8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
+    for (int m = 0; m < 7; ++m) unpack8<ACT>(r[m], ok[m], x[m]);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const float4 w4 = *reinterpret_cast<const float4*>(w + ((size_t)h * PD + c0 + q) * kConvW);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float acc = w4.x * x[e][q];
+            acc = fmaf(w4.y, x[e + 1][q], acc);
+            acc = fmaf(w4.z, x[e + 2][q], acc);
+            acc = fmaf(w4.w, x[e + 3][q], acc);
+            c[e][q] = tb + e < L ? acc : 0.f;
+        }
+    }
+}
+
+// Index of (channel c, token t) in a [PD][PC] transposed tile whose 4-token
+// chunks are permuted by channel, so that the 16 lanes of a matrix-core lane
+// group reading 4 consecutive tokens of 16 consecutive channels hit distinct
+// LDS banks.
+__device__ __forceinline__ int swz(int c, int t) {
+    return c * PC + ((((t >> 2) ^ (c & 15)) << 2) | (t & 3));
 }
 
 // Sum over each row of 16 lanes; every lane of the row gets the same value.
@@ -169,41 +235,36 @@ __device__ __forceinline__ void st_frag(char* dst, int lane, const SplitOp& sp) 
     *reinterpret_cast<f16x8_t*>(dst + 1024 + lane * 16) = sp.lo;
 }
 
-// Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
-// [c0, c0 + 8); zero for tokens at or past L.
-template <int ACT>
-__device__ __forceinline__ void conv4x8(const PrefillArgs& a, const SeqView& v, int h, int t0,
-                                        int L, int tb, const void* src, const float* w,
-                                        int c0, int ring_c0, float (&c)[4][8]) {
-    float x[7][8];
-#pragma unroll
-    for (int m = 0; m < 7; ++m) raw8<ACT>(a, v, h, t0, L, tb - 3 + m, src, c0, ring_c0, x[m]);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const float4 w4 = *reinterpret_cast<const float4*>(w + ((size_t)h * PD + c0 + q) * kConvW);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float acc = w4.x * x[e][q];
-            acc = fmaf(w4.y, x[e + 1][q], acc);
-            acc = fmaf(w4.z, x[e + 2][q], acc);
-            acc = fmaf(w4.w, x[e + 3][q], acc);
-            c[e][q] = tb + e < L ? acc : 0.f;
-        }
-    }
-}
-
 // ---------------------------------------------------------------- chunk
 
 template <int ACT>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int cps) {
-    __shared__ float KD[PC][LR];       // kh * (alpha over the sub-block start..t)
-    __shared__ float QD[PC][LR];       // qh * the same; later beta * V
-    __shared__ float KE[PC][LR];       // kh * (alpha over t+1..sub-block end); later -W
-    __shared__ float Am[PC][LS];       // beta_t kh_t.kh_i e(t,i), strictly lower; T_bb on the diagonal later
-    __shared__ float Pm[PC][LS];       // qh_t.kh_i e(t,i), lower incl. diagonal
-    __shared__ float T4[NSB][PD];      // alpha product over each sub-block
-    __shared__ float AUX[2 * NSB][PD]; // step 2: per-wave suffix tables; then prefix | suffix tables
-    __shared__ float bet[PC];
+    // LDS regions (bytes), reused as the steps go:
+    //   RA  kh * D4 [PC][LR]                    -> -W [PC][LR] (step 4)
+    //   RB  qh * D4 [PC][LR]                    -> beta K_G transposed (step X)
+    //   RC  kh * E4 [PC][LR]                    -> beta V transposed (step X)
+    //   RD  A [PC][LS], T_bb on its diagonal blocks after step 3b
+    //   RE  P [PC][LS]
+    //   RF  alpha product over each sub-block [NSB][PD]
+    //   RG  step 2: per-wave suffix tables; from step 3a: prefix | suffix
+    //       products over whole sub-blocks [2 NSB][PD]
+    //   RH  beta [PC]
+    // D4 = alpha over the sub-block start..t, E4 = alpha over t+1..sub-block end.
+    constexpr int RA = 0, RB = RA + PC * LR * 4, RC = RB + PC * LR * 4;
+    constexpr int RD = RC + PC * LR * 4, RE = RD + PC * LS * 4, RF = RE + PC * LS * 4;
+    constexpr int RG = RF + NSB * PD * 4, RH = RG + 2 * NSB * PD * 4, LDS_B = RH + PC * 4;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_B];
+    float (*KD)[LR] = reinterpret_cast<float (*)[LR]>(lds + RA);
+    float (*QD)[LR] = reinterpret_cast<float (*)[LR]>(lds + RB);
+    float (*KE)[LR] = reinterpret_cast<float (*)[LR]>(lds + RC);
+    float (*Am)[LS] = reinterpret_cast<float (*)[LS]>(lds + RD);
+    float (*Pm)[LS] = reinterpret_cast<float (*)[LS]>(lds + RE);
+    float (*T4)[PD] = reinterpret_cast<float (*)[PD]>(lds + RF);
+    float (*AUX)[PD] = reinterpret_cast<float (*)[PD]>(lds + RG);
+    float* bet = reinterpret_cast<float*>(lds + RH);
+    float (*Wn)[LR] = reinterpret_cast<float (*)[LR]>(lds + RA);
+    float* RWt = reinterpret_cast<float*>(lds + RB);
+    float* VT = reinterpret_cast<float*>(lds + RC);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -226,8 +287,26 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
     const int c0 = 8 * n;
     float cv[4][8], bt[4];
     {
+        // every load first, so that one memory latency covers them all
+        Raw8<ACT> rq[7], rk[7], rv[7], ra[4];
+        bool okm[7];
+        float rb[4];
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+            rq[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.q, c0, c0, okm[m]);
+            rk[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, okm[m]);
+            rv[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, okm[m]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
+            const int64_t row = (int64_t)(v.lo + t0 + min(tb + e, L - 1)) * H + h;
+            ra[e] = ld_raw8<ACT>(a.alpha, row * PD + c0);
+            rb[e] = ld_act<ACT>(a.beta, row);
+        }
+
         float qh[4][8], kh[4][8], al[4][8];
-        conv4x8<ACT>(a, v, h, t0, L, tb, a.q, a.wq, c0, c0, qh);
+        conv4x8<ACT>(rq, okm, a.wq, h, c0, tb, L, qh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sq = 0.f;
@@ -237,7 +316,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
-        conv4x8<ACT>(a, v, h, t0, L, tb, a.k, a.wk, c0, PD + c0, kh);
+        conv4x8<ACT>(rk, okm, a.wk, h, c0, tb, L, kh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sk = 0.f;
@@ -249,16 +328,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
-            const int t = tb + e;
-            const int64_t row = (int64_t)(v.lo + t0 + min(t, L - 1)) * H + h;
-            ld8<ACT>(a.alpha, row * PD + c0, al[e]);
-            const float b = ld_act<ACT>(a.beta, row);
+            const bool in = tb + e < L;
+            unpack8<ACT>(ra[e], true, al[e]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) al[e][q] = t < L ? al[e][q] : 1.f;
-            bt[e] = t < L ? b : 0.f;
+            for (int q = 0; q < 8; ++q) al[e][q] = in ? al[e][q] : 1.f;
+            bt[e] = in ? rb[e] : 0.f;
         }
-        conv4x8<ACT>(a, v, h, t0, L, tb, a.v, a.wv, c0, 2 * PD + c0, cv);
+        conv4x8<ACT>(rv, okm, a.wv, h, c0, tb, L, cv);
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
         float pp[10], pa[6];
@@ -393,6 +469,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             float rk2[8], rq2[8], ck2[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
+                rk[q] *= kSc;
+                rq[q] *= kSc;
+                ck[q] *= kSc;
                 const float fr = n >= 12 ? f3[q] : 1.f;
                 const float fc = n < 4 ? f1[q] : 1.f;
                 rk2[q] = rk[q] * fr;
@@ -410,8 +489,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             const int tl = 4 * g + r, jtl = g, jil = n >> 2;
             if (jil < jtl) {
                 const bool adj = jtl - jil == 1;
-                Am[16 * wave + tl][16 * wave + n] = bet[16 * wave + tl] * (adj ? aA1[r] : aA2[r]);
-                Pm[16 * wave + tl][16 * wave + n] = adj ? aP1[r] : aP2[r];
+                Am[16 * wave + tl][16 * wave + n] =
+                    bet[16 * wave + tl] * ((adj ? aA1[r] : aA2[r]) * kInvSc2);
+                Pm[16 * wave + tl][16 * wave + n] = (adj ? aP1[r] : aP2[r]) * kInvSc2;
             } else if (jil > jtl) {
                 Am[16 * wave + tl][16 * wave + n] = 0.f;
                 Pm[16 * wave + tl][16 * wave + n] = 0.f;
@@ -442,8 +522,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                     float f = jtl >= 1 ? t0f[q] : 1.f;
                     f *= jtl >= 2 ? t1f[q] : 1.f;
                     f *= jtl >= 3 ? t2f[q] : 1.f;
-                    rk[q] *= f;
-                    rq[q] *= f;
+                    rk[q] *= f * kSc;
+                    rq[q] *= f * kSc;
                 }
                 xk[kb] = split_op(rk);
                 xq[kb] = split_op(rq);
@@ -459,7 +539,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                     ld4x2(&KE[ic][cb], &KE[ic][cb + 4], ck);
                     ld4x2(&AUX[aux_o + ji][cb], &AUX[aux_o + ji][cb + 4], sf);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) ck[q] *= sf[q];
+                    for (int q = 0; q < 8; ++q) ck[q] *= sf[q] * kSc;
                     const SplitOp sck = split_op(ck);
                     A = mma3(xk[kb], sck, A);
                     P = mma3(xq[kb], sck, P);
@@ -467,8 +547,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * wave + 4 * g + r;
-                    Am[tr][ic] = bet[tr] * A[r];
-                    Pm[tr][ic] = P[r];
+                    Am[tr][ic] = bet[tr] * (A[r] * kInvSc2);
+                    Pm[tr][ic] = P[r] * kInvSc2;
                 }
             }
         }
@@ -530,7 +610,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
                 ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q];
+                for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q] * kSc;
                 dst = ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B;
             } else if (f < 32) {               // (e(last,t) * kh)^T, A operand
                 const int ct = (f - 16) & 7, kb = (f - 16) >> 3;
@@ -538,7 +618,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     const int ts = 32 * kb + kslot(g, q);
-                    x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c];
+                    x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c] * kSc;
                 }
                 dst = ws + kb * HALF_B + frag_k(ct) * FRAG_B;
             } else {                           // P rows, A operand
@@ -546,6 +626,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
                 const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
                 ld4x2(&Pm[t][cb], &Pm[t][cb + 16], x);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) x[q] *= kSc;
                 dst = ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B;
             }
             st_frag(dst, lane, split_op(x));
@@ -553,14 +635,22 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
     }
     __syncthreads();
 
-    // ---- beta * V into the freed QD tile
+    // ---- X. beta_t K_G = beta_t kh_t e(t,-1) and beta_t V, transposed to
+    // [channel][token] (swizzled) so that the solve reads 4 tokens at once
+    {
+        const int c = tid & (PD - 1), th = tid >> 7;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        float* vd = &QD[tb + e][c0];
-        *reinterpret_cast<float4*>(vd) = make_float4(bt[e] * cv[e][0], bt[e] * cv[e][1],
-                                                     bt[e] * cv[e][2], bt[e] * cv[e][3]);
-        *reinterpret_cast<float4*>(vd + 4) = make_float4(bt[e] * cv[e][4], bt[e] * cv[e][5],
-                                                         bt[e] * cv[e][6], bt[e] * cv[e][7]);
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const int t = 32 * th + 4 * t4;
+            const float pre = AUX[t >> 2][c];
+            *reinterpret_cast<float4*>(&RWt[swz(c, t)]) =
+                make_float4(bet[t] * KD[t][c] * pre, bet[t + 1] * KD[t + 1][c] * pre,
+                            bet[t + 2] * KD[t + 2][c] * pre, bet[t + 3] * KD[t + 3][c] * pre);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            *reinterpret_cast<float4*>(&VT[swz(c0 + q, tb)]) =
+                make_float4(bt[0] * cv[0][q], bt[1] * cv[1][q], bt[2] * cv[2][q], bt[3] * cv[3][q]);
     }
     __syncthreads();
 
@@ -577,15 +667,11 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = 16 * ((4 * wave + u) & 7) + n;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * b + 4 * g + r;
-                    acc[u][r] = isW ? bet[t] * KD[t][c] * AUX[t >> 2][c] : QD[t][c];
-                }
+                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]) * kSc;
             }
             if (b == 1) {
                 const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 + n][4 * g]);
-                const float av[4] = {-a4.x, -a4.y, -a4.z, -a4.w};
+                const float av[4] = {-a4.x * kSc, -a4.y * kSc, -a4.z * kSc, -a4.w * kSc};
                 const SplitOp4 sa = split_op4(av);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) acc[u] = mma3(sa, Xs[0][u], acc[u]);
@@ -593,7 +679,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 float av[8];
                 ld4x2(&Am[16 * b + n][4 * g], &Am[16 * b + n][16 + 4 * g], av);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) av[q] = -av[q];
+                for (int q = 0; q < 8; ++q) av[q] = -av[q] * kSc;
                 const SplitOp sa = split_op(av);
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -604,18 +690,18 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 }
                 if (b == 3) {
                     const float4 a4 = *reinterpret_cast<const float4*>(&Am[48 + n][32 + 4 * g]);
-                    const float a3[4] = {-a4.x, -a4.y, -a4.z, -a4.w};
+                    const float a3[4] = {-a4.x * kSc, -a4.y * kSc, -a4.z * kSc, -a4.w * kSc};
                     const SplitOp4 sa3 = split_op4(a3);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) acc[u] = mma3(sa3, Xs[2][u], acc[u]);
                 }
             }
             const float4 t4 = *reinterpret_cast<const float4*>(&Am[16 * b + n][16 * b + 4 * g]);
-            const float tv[4] = {t4.x, t4.y, t4.z, t4.w};
+            const float tv[4] = {t4.x * kScW, t4.y * kScW, t4.z * kScW, t4.w * kScW};
             const SplitOp4 st = split_op4(tv);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                X[b][u] = mma3(st, split_op4(acc[u]), f32x4_t{0.f, 0.f, 0.f, 0.f});
+                X[b][u] = mma3(st, split_op4(acc[u] * kInvSc), f32x4_t{0.f, 0.f, 0.f, 0.f}) * kInvScW;
                 if (b < 3) Xs[b][u] = split_op4(X[b][u]);
             }
         }
@@ -626,7 +712,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 for (int u = 0; u < 4; ++u) {
                     const int c = 16 * (4 * wave + u) + n;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) KE[16 * b + 4 * g + r][c] = -X[b][u][r];
+                    for (int r = 0; r < 4; ++r) Wn[16 * b + 4 * g + r][c] = -X[b][u][r];
                 }
         } else {
 #pragma unroll
@@ -649,7 +735,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         const int tt = f >> 2, kb = f & 3;
         const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
         float x[8];
-        ld4x2(&KE[t][cb], &KE[t][cb + 16], x);
+        ld4x2(&Wn[t][cb], &Wn[t][cb + 16], x);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] *= kScW;
         st_frag(ws + (tt >> 1) * HALF_B + frag_w(tt & 1, kb) * FRAG_B, lane, split_op(x));
     }
 }
@@ -661,6 +749,14 @@ __device__ __forceinline__ SplitOp ld_frag(const char* buf, int f, int lane) {
     o.hi = *reinterpret_cast<const f16x8_t*>(buf + f * FRAG_B + lane * 16);
     o.lo = *reinterpret_cast<const f16x8_t*>(buf + f * FRAG_B + 1024 + lane * 16);
     return o;
+}
+
+// body(P) for the three passes P = 0, 1, 2 of a split product.
+template <class F>
+__device__ __forceinline__ void three_passes(F&& body) {
+    body(std::integral_constant<int, 0>{});
+    body(std::integral_constant<int, 1>{});
+    body(std::integral_constant<int, 2>{});
 }
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -773,28 +869,41 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         SplitOp sb[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
-        f32x4_t U0[2], O[2];
+        // U0 = Ut - W S and O = (e(t,-1) q) S: four accumulators, each MFMA
+        // pass issued for all four before the next
+        // (scales: U accumulates at 2^8 from -W, O at 2^12 from the scaled q
+        // and P, the next state at 2^12 from the scaled k)
+        f32x4_t acc[4] = {ut0[0] * kScW, ut0[1] * kScW, f32x4_t{0.f, 0.f, 0.f, 0.f},
+                          f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            U0[u] = ut0[u];
-            O[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) {
+            const SplitOp fa[4] = {ld_frag(buf0, frag_w(0, kb), lane), ld_frag(buf0, frag_w(1, kb), lane),
+                                   ld_frag(buf0, frag_q(0, kb), lane), ld_frag(buf0, frag_q(1, kb), lane)};
+            three_passes([&](auto P) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                U0[u] = mma3(ld_frag(buf0, frag_w(u, kb), lane), sb[kb], U0[u]);
-                O[u] = mma3(ld_frag(buf0, frag_q(u, kb), lane), sb[kb], O[u]);
-            }
+                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(fa[i], sb[kb], acc[i]);
+            });
         }
-        const SplitOp ub0 = split_pair(U0[0], U0[1]);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) O[u] = mma3(ld_frag(buf0, frag_p(0, u, 0), lane), ub0, O[u]);
+        const SplitOp ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
+        f32x4_t O[2] = {acc[2], acc[3]};
         f32x4_t Sn[8];
+        {
+            const SplitOp fp[2] = {ld_frag(buf0, frag_p(0, 0, 0), lane), ld_frag(buf0, frag_p(0, 1, 0), lane)};
+            SplitOp fk[8];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            Sn[ct] = gm[ct] * S[ct];
-            Sn[ct] = mma3(ld_frag(buf0, frag_k(ct), lane), ub0, Sn[ct]);
+            for (int ct = 0; ct < 8; ++ct) {
+                fk[ct] = ld_frag(buf0, frag_k(ct), lane);
+                Sn[ct] = gm[ct] * S[ct] * kSc;
+            }
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub0, Sn[ct]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
+            });
         }
-        Oprev[0] = O[0];
-        Oprev[1] = O[1];
+        Oprev[0] = O[0] * kInvSc;
+        Oprev[1] = O[1] * kInvSc;
         orow0 = cc * PC;
 
         // ---- second half: tokens 32..63
@@ -809,30 +918,41 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         }
         store_o();
 
-        f32x4_t U1[2];
+        acc[0] = ut1[0] * kScW;
+        acc[1] = ut1[1] * kScW;
+        acc[2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc[3] = acc[2];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            U1[u] = ut1[u];
-            O[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 4; ++kb) {
+            const SplitOp fa[4] = {ld_frag(buf1, frag_w(0, kb), lane), ld_frag(buf1, frag_w(1, kb), lane),
+                                   ld_frag(buf1, frag_q(0, kb), lane), ld_frag(buf1, frag_q(1, kb), lane)};
+            three_passes([&](auto P) {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                U1[u] = mma3(ld_frag(buf1, frag_w(u, kb), lane), sb[kb], U1[u]);
-                O[u] = mma3(ld_frag(buf1, frag_q(u, kb), lane), sb[kb], O[u]);
-            }
+                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(fa[i], sb[kb], acc[i]);
+            });
         }
-        const SplitOp ub1 = split_pair(U1[0], U1[1]);
+        const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
+        O[0] = acc[2];
+        O[1] = acc[3];
+        {
+            const SplitOp fp[4] = {ld_frag(buf1, frag_p(1, 0, 0), lane), ld_frag(buf1, frag_p(1, 1, 0), lane),
+                                   ld_frag(buf1, frag_p(1, 0, 1), lane), ld_frag(buf1, frag_p(1, 1, 1), lane)};
+            SplitOp fk[8];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            O[u] = mma3(ld_frag(buf1, frag_p(1, u, 0), lane), ub0, O[u]);
-            O[u] = mma3(ld_frag(buf1, frag_p(1, u, 1), lane), ub1, O[u]);
+            for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf1, frag_k(ct), lane);
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub1, Sn[ct]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[2 + u], ub1, O[u]);
+            });
         }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            Sn[ct] = mma3(ld_frag(buf1, frag_k(ct), lane), ub1, Sn[ct]);
-            S[ct] = Sn[ct];
-        }
-        Oprev[0] = O[0];
-        Oprev[1] = O[1];
+        for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
+        Oprev[0] = O[0] * kInvSc;
+        Oprev[1] = O[1] * kInvSc;
         orow0 = cc * PC + 32;
     }
     store_o();
