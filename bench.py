@@ -11,7 +11,8 @@ Printed: one JSON line with the throughput (token-head state updates per
 second), the roofline of the decode kernel (algorithmic bytes per launch over
 its average launch time, HIP events on the launch stream), the CPU oracle's
 throughput on a bounded sample of the same workload, and the same figures for
-the other modes (large-batch BF16-state decode, speculative verify + commit).
+the other modes (large-batch BF16-state decode, speculative verify + commit,
+chunked prefill with its algorithmic and issued matrix-core rates).
 
 The timed launches replay a captured HIP graph, so the host never sits
 between two kernels; the per-launch time is the replay time over the number
@@ -34,6 +35,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E peak, GB/s
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, TFLOP/s
 
 
 def parse():
@@ -79,6 +81,65 @@ def verify_bytes_per_head(n, dk, dv, act_b, state_b):
             + 3 * C * act_b                # conv history
             + n * C * act_b                # raw drafts kept
             + n * dv * 4)                  # y
+
+
+def prefill_flops_per_chunk(C, d, L=None):
+    """Algorithmic FLOPs of the chunk form for one (chunk, head), counting
+    triangles once: A (strictly lower) and P (lower incl. diagonal) as
+    d-deep dot products, T applied to [beta K_G | beta V], then
+    U = Ut - W S, O = Qg S + P U and S <- gamma S + Kc^T U."""
+    L = C if L is None else L
+    tri_lo, tri_le = L * (L - 1) // 2, L * (L + 1) // 2
+    return 2 * (tri_lo * d + tri_le * d       # A, P
+                + tri_le * 2 * d              # T [beta K_G | beta V]
+                + 3 * L * d * d               # W S, Qg S, Kc^T U
+                + tri_le * d)                 # P U
+
+
+# MFMA instructions the prefill kernels issue per (chunk, head): chunk kernel
+# A/P products 336 and solve 96 of 16x16x32 plus 288 of 16x16x16; state
+# kernel 2 workgroups x 4 waves x 162 of 16x16x32 (three passes per product).
+PREFILL_MFMA_32_PER_CHUNK = 336 + 96 + 2 * 4 * 162
+PREFILL_MFMA_16_PER_CHUNK = 288
+
+
+def prefill_bytes(lens, H, dk, dv, act_b, st_b):
+    """Algorithmic HBM bytes of one prefill call from position 0: q, k, v,
+    alpha, g and beta read once, y (FP32) written once, the final state and
+    the ring's last three raw tokens written once per (sequence, head),
+    conv taps and norm weight once."""
+    T = int(np.sum(lens))
+    C = 2 * dk + dv
+    per_th = (C + dk + dv) * act_b + act_b + dv * 4
+    per_sh = dk * dv * st_b + 3 * C * act_b
+    return T * H * per_th + len(lens) * H * per_sh + H * C * 4 * 4 + dv * 4
+
+
+# ------------------------------------------------------------ measured traffic
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "token_kernel_batched_decode_hbm_traffic.md")
+TOKEN_KERNEL_SOURCES = ("kda_token.hip", "kda_device.h", "kda_internal.h")
+
+
+def decode_traffic():
+    """HBM bytes per launch of the batched-decode kernel, from the rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs recorded under profiles/ (scaled by the same
+    counters' reading for a 1 GiB copy).  None when the kernel's sources have
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
+    h = hashlib.sha256()
+    for f in TOKEN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "hybrid_linear_attention_rule_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 # ------------------------------------------------------------ helpers
@@ -227,6 +288,64 @@ def run_verify_mode(torch, case, K, W, layers):
         parity_rel_err={"y": e_y, "records": e_r})
 
 
+# ------------------------------------------------------------ prefill
+
+def run_prefill_mode(torch, case, K, W):
+    from hybrid_linear_attention_rule_amd import device as dev
+    from hybrid_linear_attention_rule_amd import kda
+    import oracle
+
+    ds = dev.make_state(case, spare_slots=0, fill_nan=False)
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    T = int(case.cu_seqlens[-1])
+    H, dk, dv = case.H, case.dk, case.dv
+    y = torch.empty((T, H, dv), device="cuda")
+    ws = torch.empty(kda.prefill_workspace_bytes(ds.shape, case.batch, T),
+                     dtype=torch.uint8, device="cuda")
+    cu_t = torch.from_numpy(case.cu_seqlens.astype(np.int32)).cuda()
+    pos_t = torch.from_numpy(case.pos0.astype(np.int32)).cuda()
+
+    def launch(i):
+        # from position 0 the pool is written, not read: every call is the same
+        kda.prefill(ds.shape, ds.params, cu_t, max(case.lens), ds.slot_ids, pos_t,
+                    tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], tok["g"],
+                    ds.pool, ds.ring, y, ws)
+
+    launch(0)
+    torch.cuda.synchronize()
+    y_ref, S_ref, _ = oracle.prefill_case(case)
+    e_y = rel_err(y.cpu().numpy(), y_ref)
+    tol = 2e-5 if case.state == "f32" else 1e-2
+    e_s = rel_err(dev.read_states(ds), S_ref)
+    assert e_y <= 2e-5 and e_s <= tol, f"prefill parity failed: {e_y} {e_s}"
+    n_timed_req = max(4, K // 32)
+    total, per_launch, n_timed = timed_loop(torch, launch, n_timed_req, max(2, W // 8), 4)
+    act_b = 2 if case.act == "bf16" else 4
+    st_b = 2 if case.state == "bf16" else 4
+    lens = np.asarray(case.lens)
+    flops = sum(H * (prefill_flops_per_chunk(64, dk) * (int(L) // 64) +
+                     (prefill_flops_per_chunk(64, dk, int(L) % 64) if L % 64 else 0))
+                for L in lens)
+    chunks = int(sum((int(L) + 63) // 64 for L in lens)) * H
+    issued = chunks * (PREFILL_MFMA_32_PER_CHUNK * 16 * 16 * 32 * 2 +
+                       PREFILL_MFMA_16_PER_CHUNK * 16 * 16 * 16 * 2)
+    nbytes = prefill_bytes(lens, H, dk, dv, act_b, st_b)
+    floor_s = max(flops / (MFMA_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
+    return dict(
+        workload=case.name, seq_lens=[int(x) for x in lens], heads=H, dk=dk, dv=dv,
+        chunk=64, act=case.act, state=case.state, launches_timed=n_timed,
+        prefill_us=per_launch * 1e6, tokens_per_s=T / per_launch,
+        th_per_s=T * H / per_launch,
+        algorithmic_gflop=flops / 1e9, mfma_tflops_algorithmic=flops / per_launch / 1e12,
+        mfma_frac_algorithmic=flops / per_launch / 1e12 / MFMA_PEAK_TFLOPS,
+        issued_gflop=issued / 1e9, mfma_tflops_issued=issued / per_launch / 1e12,
+        mfma_frac_issued=issued / per_launch / 1e12 / MFMA_PEAK_TFLOPS,
+        bytes_per_launch=nbytes, hbm_gbs=nbytes / per_launch / 1e9,
+        hbm_frac=nbytes / per_launch / 1e9 / HBM_PEAK_GBS,
+        roofline_floor_us=floor_s * 1e6, roofline_frac=floor_s / per_launch,
+        parity_rel_err={"y": e_y, "state": e_s})
+
+
 # ------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(case, seconds):
@@ -295,6 +414,11 @@ def main():
         print(f"# verify {case2.name}", file=sys.stderr, flush=True)
         modes["spec_verify_commit"] = run_verify_mode(torch, case2, args.steps,
                                                       args.warmup, 8)
+        case4 = wl.config(4)
+        print(f"# prefill {case4.name}", file=sys.stderr, flush=True)
+        modes["chunked_prefill"] = run_prefill_mode(torch, case4, args.steps, args.warmup)
+        print(f"# prefill {modes['chunked_prefill']['prefill_us']:.1f} us",
+              file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
@@ -320,7 +444,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac"], "traffic": None,
+                     "frac": head["hbm_frac"], "traffic": decode_traffic(),
                      "kernel": "kda::token_kernel<128,128,bf16,f32,decode>",
                      "kernel_us": head["kernel_us"],
                      "bytes_per_launch": head["bytes_per_launch"]},

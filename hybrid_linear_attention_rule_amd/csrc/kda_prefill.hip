@@ -751,6 +751,15 @@ __device__ __forceinline__ SplitOp ld_frag(const char* buf, int f, int lane) {
     return o;
 }
 
+// The four fragments of step kb of a half: -W rows (two tiles), scaled-q
+// rows (two tiles).
+__device__ __forceinline__ void load_wq(const char* buf, int kb, int lane, SplitOp (&f)[4]) {
+    f[0] = ld_frag(buf, frag_w(0, kb), lane);
+    f[1] = ld_frag(buf, frag_w(1, kb), lane);
+    f[2] = ld_frag(buf, frag_q(0, kb), lane);
+    f[3] = ld_frag(buf, frag_q(1, kb), lane);
+}
+
 // body(P) for the three passes P = 0, 1, 2 of a split product.
 template <class F>
 __device__ __forceinline__ void three_passes(F&& body) {
@@ -794,8 +803,9 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         buf0[tid] = 0;
         buf1[tid] = 0;
     }
-    // the two column halves of one (sequence, head) sit eight workgroups
-    // apart, so both land on the same XCD and share its L2
+    // two workgroups per (sequence, head), 64 value columns each (wave w
+    // owns 16); the two sit eight workgroups apart, so both land on the same
+    // XCD and share its L2
     const int G = a.num_seqs * H;
     const int r16 = blockIdx.x & 15;
     const int half = r16 >> 3;
@@ -858,57 +868,75 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
             }
     };
 
+    // The explicit waits below also cover the assembly DMA loads, which the
+    // compiler does not count: registers loaded before such a wait are passed
+    // through it, so that the compiler sees them as ready and inserts no
+    // counted wait of its own (which would also wait on the newer DMA).
+    f32x4_t ut1[2];
     for (int cc = 0; cc < nch; ++cc) {
         // ---- first half: tokens 0..31 of the chunk
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)"
+                     : "+v"(ut0[0]), "+v"(ut0[1]), "+v"(gm[0]), "+v"(gm[1]), "+v"(gm[2]),
+                       "+v"(gm[3]), "+v"(gm[4]), "+v"(gm[5]), "+v"(gm[6]), "+v"(gm[7])
+                     :
+                     : "memory");
+        asm volatile("" : "+v"(S[0]), "+v"(S[1]), "+v"(S[2]), "+v"(S[3]), "+v"(S[4]), "+v"(S[5]),
+                          "+v"(S[6]), "+v"(S[7]));
         __syncthreads();
         dma_half(cws(cc) + HALF_B, buf1, wave, lane);
-        const f32x4_t ut1[2] = {ld_ut(cc, 1, 0), ld_ut(cc, 1, 1)};
+        ut1[0] = ld_ut(cc, 1, 0);
+        ut1[1] = ld_ut(cc, 1, 1);
         store_o();
 
+        // fragments are loaded one step ahead of the MFMAs that use them
+        SplitOp F[4], N[4];
+        load_wq(buf0, 0, lane, F);
         SplitOp sb[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
         // U0 = Ut - W S and O = (e(t,-1) q) S: four accumulators, each MFMA
-        // pass issued for all four before the next
-        // (scales: U accumulates at 2^8 from -W, O at 2^12 from the scaled q
-        // and P, the next state at 2^12 from the scaled k)
+        // pass issued for all four before the next.  Scales: U accumulates
+        // at 2^8 from -W, O at 2^12 from the scaled q and P, the next state
+        // at 2^12 from the scaled k.
         f32x4_t acc[4] = {ut0[0] * kScW, ut0[1] * kScW, f32x4_t{0.f, 0.f, 0.f, 0.f},
                           f32x4_t{0.f, 0.f, 0.f, 0.f}};
+        SplitOp fk[8], fp[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const SplitOp fa[4] = {ld_frag(buf0, frag_w(0, kb), lane), ld_frag(buf0, frag_w(1, kb), lane),
-                                   ld_frag(buf0, frag_q(0, kb), lane), ld_frag(buf0, frag_q(1, kb), lane)};
+            if (kb < 3) {
+                load_wq(buf0, kb + 1, lane, N);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf0, frag_k(ct), lane);
+                fp[0] = ld_frag(buf0, frag_p(0, 0, 0), lane);
+                fp[1] = ld_frag(buf0, frag_p(0, 1, 0), lane);
+            }
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(fa[i], sb[kb], acc[i]);
+                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(F[i], sb[kb], acc[i]);
             });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) F[i] = N[i];
         }
         const SplitOp ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
         f32x4_t O[2] = {acc[2], acc[3]};
         f32x4_t Sn[8];
-        {
-            const SplitOp fp[2] = {ld_frag(buf0, frag_p(0, 0, 0), lane), ld_frag(buf0, frag_p(0, 1, 0), lane)};
-            SplitOp fk[8];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                fk[ct] = ld_frag(buf0, frag_k(ct), lane);
-                Sn[ct] = gm[ct] * S[ct] * kSc;
-            }
-            three_passes([&](auto P) {
+        for (int ct = 0; ct < 8; ++ct) Sn[ct] = gm[ct] * S[ct] * kSc;
+        three_passes([&](auto P) {
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub0, Sn[ct]);
+            for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub0, Sn[ct]);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
-            });
-        }
+            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
+        });
         Oprev[0] = O[0] * kInvSc;
         Oprev[1] = O[1] * kInvSc;
         orow0 = cc * PC;
 
         // ---- second half: tokens 32..63
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(ut1[0]), "+v"(ut1[1]) : : "memory");
         __syncthreads();
+        load_wq(buf1, 0, lane, F);
         if (cc + 1 < nch) {
             dma_half(cws(cc + 1), buf0, wave, lane);
             ut0[0] = ld_ut(cc + 1, 0, 0);
@@ -924,31 +952,35 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         acc[3] = acc[2];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const SplitOp fa[4] = {ld_frag(buf1, frag_w(0, kb), lane), ld_frag(buf1, frag_w(1, kb), lane),
-                                   ld_frag(buf1, frag_q(0, kb), lane), ld_frag(buf1, frag_q(1, kb), lane)};
+            if (kb < 3) {
+                load_wq(buf1, kb + 1, lane, N);
+            } else {
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf1, frag_k(ct), lane);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    fp[u] = ld_frag(buf1, frag_p(1, u, 0), lane);
+                    fp[2 + u] = ld_frag(buf1, frag_p(1, u, 1), lane);
+                }
+            }
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(fa[i], sb[kb], acc[i]);
+                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(F[i], sb[kb], acc[i]);
             });
+#pragma unroll
+            for (int i = 0; i < 4; ++i) F[i] = N[i];
         }
         const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
         O[0] = acc[2];
         O[1] = acc[3];
-        {
-            const SplitOp fp[4] = {ld_frag(buf1, frag_p(1, 0, 0), lane), ld_frag(buf1, frag_p(1, 1, 0), lane),
-                                   ld_frag(buf1, frag_p(1, 0, 1), lane), ld_frag(buf1, frag_p(1, 1, 1), lane)};
-            SplitOp fk[8];
+        three_passes([&](auto P) {
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf1, frag_k(ct), lane);
-            three_passes([&](auto P) {
+            for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub1, Sn[ct]);
 #pragma unroll
-                for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub1, Sn[ct]);
+            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[2 + u], ub1, O[u]);
-            });
-        }
+            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[2 + u], ub1, O[u]);
+        });
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
         Oprev[0] = O[0] * kInvSc;
