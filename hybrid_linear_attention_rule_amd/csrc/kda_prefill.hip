@@ -37,8 +37,9 @@
 //          sequence's chunks): U, O and the next state on the matrix cores,
 //          the state slice in registers, each chunk's operands streamed into
 //          LDS in two halves by direct global-to-LDS loads, double-buffered;
-//          O is written unnormalised; the final state is stored once and the
-//          ring gets the sequence's last raw tokens;
+//          per 16-column slice one wave updates U and the state and another
+//          forms O; O is written unnormalised; the final state is stored
+//          once and the ring gets the sequence's last raw tokens;
 //   finish (per token x head): the gated RMSNorm of O.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -68,13 +69,15 @@ constexpr float kScW = 256.f, kInvScW = 1.f / 256.f;
 // MFMA operand for a wave: 64 lanes x 8 fp16 hi values, then 64 x 8 lo.
 // Half h of a chunk (tokens 32h..32h+31 for the token-indexed operands)
 // holds, in this order: -W tiles (2 x 4), scaled-Q tiles (2 x 4), scaled-K
-// tiles for that half of the tokens (8), and the P tiles of its rows.
+// tiles for that half of the tokens (8), and the P tiles of its rows (2 in
+// half 0, 4 in half 1); half 0's slot 26 holds the chunk's total decay
+// (FP32 [PD]).  Ut follows in FP32, in the state kernel's D-tile order.
 constexpr int FRAG_B = 2048;
 constexpr int HALF_FRAGS = 28;
 constexpr int HALF_B = HALF_FRAGS * FRAG_B;
-constexpr int UT_OFF = 2 * HALF_B;             // Ut, FP32, D-tile order
-constexpr int GAM_OFF = UT_OFF + PC * PD * 4;  // total decay of the chunk [PD]
-constexpr int WS_B = GAM_OFF + PD * 4;
+constexpr int GAM_OFF = 26 * FRAG_B;           // in half 0
+constexpr int UT_OFF = 2 * HALF_B;
+constexpr int WS_B = UT_OFF + PC * PD * 4;
 
 __device__ __forceinline__ int frag_w(int u, int kb) { return 4 * u + kb; }
 __device__ __forceinline__ int frag_q(int u, int kb) { return 8 + 4 * u + kb; }
@@ -751,15 +754,6 @@ __device__ __forceinline__ SplitOp ld_frag(const char* buf, int f, int lane) {
     return o;
 }
 
-// The four fragments of step kb of a half: -W rows (two tiles), scaled-q
-// rows (two tiles).
-__device__ __forceinline__ void load_wq(const char* buf, int kb, int lane, SplitOp (&f)[4]) {
-    f[0] = ld_frag(buf, frag_w(0, kb), lane);
-    f[1] = ld_frag(buf, frag_w(1, kb), lane);
-    f[2] = ld_frag(buf, frag_q(0, kb), lane);
-    f[3] = ld_frag(buf, frag_q(1, kb), lane);
-}
-
 // body(P) for the three passes P = 0, 1, 2 of a split product.
 template <class F>
 __device__ __forceinline__ void three_passes(F&& body) {
@@ -770,16 +764,16 @@ __device__ __forceinline__ void three_passes(F&& body) {
 
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-// One half of a chunk's fragments into LDS: 56 pieces of 1 KB, wave w
-// copies pieces w, w+4, ...; lane l moves 16 bytes straight from global
-// memory to LDS (M0 holds the wave's LDS destination).  Issued as inline
-// assembly: the compiler would otherwise wait for these loads before every
-// LDS read of the other buffer.  The caller waits for them explicitly
+// One half of a chunk's fragments into LDS: 56 pieces of 1 KB, wave w of
+// the eight copies pieces w, w+8, ...; lane l moves 16 bytes straight from
+// global memory to LDS (M0 holds the wave's LDS destination).  Issued as
+// inline assembly: the compiler would otherwise wait for these loads before
+// every LDS read of the other buffer.  The caller waits for them explicitly
 // (s_waitcnt vmcnt(0)) before the barrier that publishes the buffer.
 __device__ __forceinline__ void dma_half(const char* src, char* dst, int wave, int lane) {
 #pragma unroll
-    for (int q = 0; q < HALF_B / 1024 / 4; ++q) {
-        const int piece = wave + 4 * q;
+    for (int q = 0; q < HALF_B / 1024 / 8; ++q) {
+        const int piece = wave + 8 * q;
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                      :
                      : "v"(src + piece * 1024 + lane * 16),
@@ -788,13 +782,40 @@ __device__ __forceinline__ void dma_half(const char* src, char* dst, int wave, i
     }
 }
 
+// Split operands a column slice's U/S wave hands to its O wave through LDS:
+// the chunk's start state as the B operand (k = key channel, four 32-deep
+// blocks) and the current half's U (k = token).
+struct SliceX {
+    f16x8_t sb_hi[4][64], sb_lo[4][64];
+    f16x8_t ub_hi[64], ub_lo[64];
+};
+
+__device__ __forceinline__ void put_split(f16x8_t* hi, f16x8_t* lo, int lane, const SplitOp& x) {
+    hi[lane] = x.hi;
+    lo[lane] = x.lo;
+}
+__device__ __forceinline__ SplitOp get_split(const f16x8_t* hi, const f16x8_t* lo, int lane) {
+    return SplitOp{hi[lane], lo[lane]};
+}
+
+// State pass.  Two 512-thread workgroups per (sequence, head), 64 value
+// columns each, in four 16-column slices.  Each slice has two waves on one
+// SIMD: the U/S wave (waves 0-3) holds the slice's state and computes
+// U = Ut - W S and S <- Diag(gamma) S + Kc^T U; the O wave (waves 4-7)
+// computes O = Qg S + P U from the split S and U the U/S wave publishes.  So
+// every fragment of a chunk has one reader per slice, and each SIMD runs
+// two waves.  Per half: barrier H (the half's fragments are in LDS), U and
+// Qg S, barrier X (U is published), the state update and P U.
 template <int ACT, int ST>
-__global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char buf0[HALF_B];
     __shared__ __attribute__((aligned(16))) char buf1[HALF_B];
+    __shared__ SliceX X[4];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
+    const int slice = wave & 3;
+    const bool uw = wave < 4;                     // wave-uniform role
     const int H = a.H;
     // The buffers are filled only by the assembly loads above; this store,
     // which never runs (num_seqs >= 1), keeps the compiler from treating
@@ -803,9 +824,8 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         buf0[tid] = 0;
         buf1[tid] = 0;
     }
-    // two workgroups per (sequence, head), 64 value columns each (wave w
-    // owns 16); the two sit eight workgroups apart, so both land on the same
-    // XCD and share its L2
+    // the two column halves of one (sequence, head) sit eight workgroups
+    // apart, so both land on the same XCD and share its L2
     const int G = a.num_seqs * H;
     const int r16 = blockIdx.x & 15;
     const int half = r16 >> 3;
@@ -815,9 +835,10 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
     SeqView v;
     if (!seq_view(a, s, false, v)) return;
     if (v.len == 0) return;
-    const int j16 = 4 * half + wave;
+    const int j16 = 4 * half + slice;
     const int jc = 16 * j16 + n;
     const size_t head_off = ((size_t)v.slot * H + h) * PD * PD;
+    SliceX& xs = X[slice];
 
     auto cws = [&](int c) -> const char* {
         return static_cast<const char*>(a.workspace) +
@@ -827,34 +848,38 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
                                                  ((((hh * 8 + j16) * 2 + u) * 64 + lane) * 16));
     };
-    auto ld_gam = [&](int c, int ct) -> f32x4_t {
-        return *reinterpret_cast<const f32x4_t*>(cws(c) + GAM_OFF + (16 * ct + 4 * g) * 4);
-    };
 
     const int nch = (v.len + PC - 1) / PC;
     dma_half(cws(0), buf0, wave, lane);
-    f32x4_t ut0[2] = {ld_ut(0, 0, 0), ld_ut(0, 0, 1)};
-    f32x4_t gm[8];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) gm[ct] = ld_gam(0, ct);
 
-    // state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
-    f32x4_t S[8];
+    // U/S wave: state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
+    f32x4_t S[8], Sn[8];
+    f32x4_t ut0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, ut1[2] = {ut0[0], ut0[1]};
+    SplitOp sb[4];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (v.pos > 0) {
+    if (uw) {
+        ut0[0] = ld_ut(0, 0, 0);
+        ut0[1] = ld_ut(0, 0, 1);
+        if (v.pos > 0) {
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+            for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
-                S[ct][r] = ST == kF32 ? static_cast<const float*>(a.pool)[e]
-                                      : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[e]);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
+                    S[ct][r] = ST == kF32 ? static_cast<const float*>(a.pool)[e]
+                                          : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[e]);
+                }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
+            put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
+        }
     }
 
-    // O of the previous half, stored after the next barrier so that the
-    // store latency overlaps the next half's work
+    // O wave: O of the previous half, stored after the next barrier H so that
+    // the store latency overlaps the next half's work
     f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     int orow0 = -1;
     auto store_o = [&]() {
@@ -872,134 +897,170 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
     // compiler does not count: registers loaded before such a wait are passed
     // through it, so that the compiler sees them as ready and inserts no
     // counted wait of its own (which would also wait on the newer DMA).
-    f32x4_t ut1[2];
+    SplitOp ub0;
     for (int cc = 0; cc < nch; ++cc) {
-        // ---- first half: tokens 0..31 of the chunk
-        asm volatile("s_waitcnt vmcnt(0)"
-                     : "+v"(ut0[0]), "+v"(ut0[1]), "+v"(gm[0]), "+v"(gm[1]), "+v"(gm[2]),
-                       "+v"(gm[3]), "+v"(gm[4]), "+v"(gm[5]), "+v"(gm[6]), "+v"(gm[7])
-                     :
-                     : "memory");
+        // ======== first half: tokens 0..31 of the chunk ========
+        asm volatile("s_waitcnt vmcnt(0)" : "+v"(ut0[0]), "+v"(ut0[1]) : : "memory");
         asm volatile("" : "+v"(S[0]), "+v"(S[1]), "+v"(S[2]), "+v"(S[3]), "+v"(S[4]), "+v"(S[5]),
                           "+v"(S[6]), "+v"(S[7]));
-        __syncthreads();
+        __syncthreads();                                           // H0
         dma_half(cws(cc) + HALF_B, buf1, wave, lane);
-        ut1[0] = ld_ut(cc, 1, 0);
-        ut1[1] = ld_ut(cc, 1, 1);
-        store_o();
-
-        // fragments are loaded one step ahead of the MFMAs that use them
-        SplitOp F[4], N[4];
-        load_wq(buf0, 0, lane, F);
-        SplitOp sb[4];
+        f32x4_t O[2];
+        if (uw) {
+            ut1[0] = ld_ut(cc, 1, 0);
+            ut1[1] = ld_ut(cc, 1, 1);
+            // U0 = Ut - W S (accumulated at 2^8)
+            f32x4_t acc[2] = {ut0[0] * kScW, ut0[1] * kScW};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
-        // U0 = Ut - W S and O = (e(t,-1) q) S: four accumulators, each MFMA
-        // pass issued for all four before the next.  Scales: U accumulates
-        // at 2^8 from -W, O at 2^12 from the scaled q and P, the next state
-        // at 2^12 from the scaled k.
-        f32x4_t acc[4] = {ut0[0] * kScW, ut0[1] * kScW, f32x4_t{0.f, 0.f, 0.f, 0.f},
-                          f32x4_t{0.f, 0.f, 0.f, 0.f}};
-        SplitOp fk[8], fp[4];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (kb < 3) {
-                load_wq(buf0, kb + 1, lane, N);
-            } else {
-#pragma unroll
-                for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf0, frag_k(ct), lane);
-                fp[0] = ld_frag(buf0, frag_p(0, 0, 0), lane);
-                fp[1] = ld_frag(buf0, frag_p(0, 1, 0), lane);
+            for (int kb = 0; kb < 4; ++kb) {
+                const SplitOp f0 = ld_frag(buf0, frag_w(0, kb), lane);
+                const SplitOp f1 = ld_frag(buf0, frag_w(1, kb), lane);
+                three_passes([&](auto P) {
+                    acc[0] = mma_pass<decltype(P)::value>(f0, sb[kb], acc[0]);
+                    acc[1] = mma_pass<decltype(P)::value>(f1, sb[kb], acc[1]);
+                });
             }
-            three_passes([&](auto P) {
+            ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
+            put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
+        } else {
+            store_o();
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(F[i], sb[kb], acc[i]);
-            });
+            for (int kb = 0; kb < 4; ++kb) sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
+            // O = (e(t,-1) q) S (accumulated at 2^12)
+            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            O[1] = O[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) F[i] = N[i];
+            for (int kb = 0; kb < 4; ++kb) {
+                const SplitOp f0 = ld_frag(buf0, frag_q(0, kb), lane);
+                const SplitOp f1 = ld_frag(buf0, frag_q(1, kb), lane);
+                three_passes([&](auto P) {
+                    O[0] = mma_pass<decltype(P)::value>(f0, sb[kb], O[0]);
+                    O[1] = mma_pass<decltype(P)::value>(f1, sb[kb], O[1]);
+                });
+            }
         }
-        const SplitOp ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
-        f32x4_t O[2] = {acc[2], acc[3]};
-        f32x4_t Sn[8];
+        __syncthreads();                                           // X0
+        if (uw) {
+            // S <- gamma S + Kc^T U0 (accumulated at 2^12); gamma sits in buf0
+            const float* gam = reinterpret_cast<const float*>(buf0 + GAM_OFF);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) Sn[ct] = gm[ct] * S[ct] * kSc;
-        three_passes([&](auto P) {
+            for (int ct = 0; ct < 8; ++ct)
+                Sn[ct] = *reinterpret_cast<const f32x4_t*>(&gam[16 * ct + 4 * g]) * S[ct] * kSc;
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub0, Sn[ct]);
+            for (int c2 = 0; c2 < 8; c2 += 4) {
+                SplitOp fk[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
-        });
-        Oprev[0] = O[0] * kInvSc;
-        Oprev[1] = O[1] * kInvSc;
-        orow0 = cc * PC;
+                for (int i = 0; i < 4; ++i) fk[i] = ld_frag(buf0, frag_k(c2 + i), lane);
+                three_passes([&](auto P) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Sn[c2 + i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[c2 + i]);
+                });
+            }
+        } else {
+            ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            const SplitOp fp0 = ld_frag(buf0, frag_p(0, 0, 0), lane);
+            const SplitOp fp1 = ld_frag(buf0, frag_p(0, 1, 0), lane);
+            three_passes([&](auto P) {
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
+            orow0 = cc * PC;
+        }
 
-        // ---- second half: tokens 32..63
+        // ======== second half: tokens 32..63 ========
         asm volatile("s_waitcnt vmcnt(0)" : "+v"(ut1[0]), "+v"(ut1[1]) : : "memory");
-        __syncthreads();
-        load_wq(buf1, 0, lane, F);
-        if (cc + 1 < nch) {
-            dma_half(cws(cc + 1), buf0, wave, lane);
-            ut0[0] = ld_ut(cc + 1, 0, 0);
-            ut0[1] = ld_ut(cc + 1, 0, 1);
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct) gm[ct] = ld_gam(cc + 1, ct);
-        }
-        store_o();
-
-        acc[0] = ut1[0] * kScW;
-        acc[1] = ut1[1] * kScW;
-        acc[2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc[3] = acc[2];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            if (kb < 3) {
-                load_wq(buf1, kb + 1, lane, N);
-            } else {
-#pragma unroll
-                for (int ct = 0; ct < 8; ++ct) fk[ct] = ld_frag(buf1, frag_k(ct), lane);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    fp[u] = ld_frag(buf1, frag_p(1, u, 0), lane);
-                    fp[2 + u] = ld_frag(buf1, frag_p(1, u, 1), lane);
-                }
+        __syncthreads();                                           // H1
+        if (cc + 1 < nch) dma_half(cws(cc + 1), buf0, wave, lane);
+        if (uw) {
+            if (cc + 1 < nch) {
+                ut0[0] = ld_ut(cc + 1, 0, 0);
+                ut0[1] = ld_ut(cc + 1, 0, 1);
             }
+            f32x4_t acc[2] = {ut1[0] * kScW, ut1[1] * kScW};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const SplitOp f0 = ld_frag(buf1, frag_w(0, kb), lane);
+                const SplitOp f1 = ld_frag(buf1, frag_w(1, kb), lane);
+                three_passes([&](auto P) {
+                    acc[0] = mma_pass<decltype(P)::value>(f0, sb[kb], acc[0]);
+                    acc[1] = mma_pass<decltype(P)::value>(f1, sb[kb], acc[1]);
+                });
+            }
+            const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
+            put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
+            ub0 = ub1;                    // the U/S wave's next update uses U1
+        } else {
+            store_o();
+            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            O[1] = O[0];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const SplitOp f0 = ld_frag(buf1, frag_q(0, kb), lane);
+                const SplitOp f1 = ld_frag(buf1, frag_q(1, kb), lane);
+                three_passes([&](auto P) {
+                    O[0] = mma_pass<decltype(P)::value>(f0, sb[kb], O[0]);
+                    O[1] = mma_pass<decltype(P)::value>(f1, sb[kb], O[1]);
+                });
+            }
+            const SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 0), lane);
+            const SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 0), lane);
             three_passes([&](auto P) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = mma_pass<decltype(P)::value>(F[i], sb[kb], acc[i]);
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
             });
-#pragma unroll
-            for (int i = 0; i < 4; ++i) F[i] = N[i];
         }
-        const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
-        O[0] = acc[2];
-        O[1] = acc[3];
-        three_passes([&](auto P) {
+        __syncthreads();                                           // X1
+        if (uw) {
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) Sn[ct] = mma_pass<decltype(P)::value>(fk[ct], ub1, Sn[ct]);
+            for (int c2 = 0; c2 < 8; c2 += 4) {
+                SplitOp fk[4];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[u], ub0, O[u]);
+                for (int i = 0; i < 4; ++i) fk[i] = ld_frag(buf1, frag_k(c2 + i), lane);
+                three_passes([&](auto P) {
 #pragma unroll
-            for (int u = 0; u < 2; ++u) O[u] = mma_pass<decltype(P)::value>(fp[2 + u], ub1, O[u]);
-        });
+                    for (int i = 0; i < 4; ++i)
+                        Sn[c2 + i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[c2 + i]);
+                });
+            }
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
-        Oprev[0] = O[0] * kInvSc;
-        Oprev[1] = O[1] * kInvSc;
-        orow0 = cc * PC + 32;
+            for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
+            // the next chunk's S, split, for both waves of the slice
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
+                put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
+            }
+        } else {
+            const SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            const SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 1), lane);
+            const SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 1), lane);
+            three_passes([&](auto P) {
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub1, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub1, O[1]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
+            orow0 = cc * PC + 32;
+        }
     }
-    store_o();
+    if (!uw) store_o();
 
     // typed store of the final state, once
+    if (uw) {
 #pragma unroll
-    for (int ct = 0; ct < 8; ++ct)
+        for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
-            if (ST == kF32)
-                static_cast<float*>(a.pool)[e] = S[ct][r];
-            else
-                static_cast<uint16_t*>(a.pool)[e] = (uint16_t)f32_to_bf16_rne(S[ct][r]);
-        }
+            for (int r = 0; r < 4; ++r) {
+                const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
+                if (ST == kF32)
+                    static_cast<float*>(a.pool)[e] = S[ct][r];
+                else
+                    static_cast<uint16_t*>(a.pool)[e] = (uint16_t)f32_to_bf16_rne(S[ct][r]);
+            }
+    }
 
     // ring: the sequence's last min(3, len) raw tokens (the chunk kernel,
     // which read the old entries, has finished)
@@ -1010,7 +1071,7 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
         for (int pp = pfirst; pp < pend; ++pp) {
             const int64_t row = v.lo + (pp - v.pos);
             const int64_t dst = (((int64_t)v.slot * kConvW + (pp & (kConvW - 1))) * H + h) * C;
-            for (int ch = tid; ch < C; ch += 256) {
+            for (int ch = tid; ch < C; ch += 512) {
                 const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
                 st_act_bits<ACT>(a.ring, dst + ch,
                                  ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
@@ -1021,16 +1082,34 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- finish
 
-// Gated RMSNorm of O in place: 32 lanes per (token, head) row, four values
-// per lane.  Rows of sequences that are skipped are left untouched.
+// Gated RMSNorm of O in place: one workgroup per (token, 8 heads), 32 lanes
+// per head row, four values per lane.  Rows of sequences that are skipped
+// are left untouched.  The rows' O, gates and weights are requested first;
+// the sequence lookup (uniform over the workgroup, so scalar loads) that
+// decides whether they are written overlaps those loads.
 template <int ACT>
 __global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, l32 = tid & 31;
-    const int64_t rows = a.total_tokens * a.H;
-    const int64_t row = (int64_t)blockIdx.x * 8 + (tid >> 5);
-    bool ok = row < rows;
-    const int64_t token = ok ? row / a.H : 0;
-    const int h = ok ? (int)(row % a.H) : 0;
+    const int64_t token = blockIdx.x;
+    const int h_raw = 8 * (int)blockIdx.y + (tid >> 5);
+    const bool in = h_raw < a.H;
+    const int h = in ? h_raw : a.H - 1;
+    const int64_t row = token * a.H + h;
+    float* y = a.y + row * PD + 4 * l32;
+    const float4 o = *reinterpret_cast<const float4*>(y);
+    float gv[4];
+    if constexpr (ACT == kF32) {
+        const float4 g4 =
+            *reinterpret_cast<const float4*>(static_cast<const float*>(a.g) + row * PD + 4 * l32);
+        gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
+    } else {
+        const uint2 g2 =
+            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.g) + row * PD + 4 * l32);
+        gv[0] = __uint_as_float(g2.x << 16); gv[1] = __uint_as_float(g2.x & 0xffff0000u);
+        gv[2] = __uint_as_float(g2.y << 16); gv[3] = __uint_as_float(g2.y & 0xffff0000u);
+    }
+    const float4 w = a.norm_w ? *reinterpret_cast<const float4*>(a.norm_w + 4 * l32)
+                              : make_float4(1.f, 1.f, 1.f, 1.f);
     // the sequence holding the token (cu_seqlens is monotone for valid input)
     int lo_s = 0, hi_s = a.num_seqs;
     while (hi_s - lo_s > 1) {
@@ -1038,23 +1117,15 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
         if (a.cu_seqlens[mid] <= token) lo_s = mid; else hi_s = mid;
     }
     SeqView v;
-    ok = ok && seq_view(a, lo_s, false, v) && token >= v.lo && token < v.lo + v.len;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-    float* y = a.y + (ok ? row : 0) * PD + 4 * l32;
-    if (ok) o = *reinterpret_cast<const float4*>(y);
+    const bool ok = in && seq_view(a, lo_s, false, v) && token >= v.lo && token < v.lo + v.len;
     float ss = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
     ss = row16_sum(ss);
     ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));  // lane ^ 16
     if (!ok) return;
     const float rr = 1.0f / sqrtf(ss / (float)PD + a.norm_eps);
-    const float4 w = a.norm_w ? *reinterpret_cast<const float4*>(a.norm_w + 4 * l32)
-                              : make_float4(1.f, 1.f, 1.f, 1.f);
-    const int64_t gi = (token * a.H + h) * PD + 4 * l32;
-    const float g0 = ld_act<ACT>(a.g, gi), g1 = ld_act<ACT>(a.g, gi + 1);
-    const float g2 = ld_act<ACT>(a.g, gi + 2), g3 = ld_act<ACT>(a.g, gi + 3);
     *reinterpret_cast<float4*>(y) =
-        make_float4(w.x * (o.x * rr) * gate_fn(a.gate, g0), w.y * (o.y * rr) * gate_fn(a.gate, g1),
-                    w.z * (o.z * rr) * gate_fn(a.gate, g2), w.w * (o.w * rr) * gate_fn(a.gate, g3));
+        make_float4(w.x * (o.x * rr) * gate_fn(a.gate, gv[0]), w.y * (o.y * rr) * gate_fn(a.gate, gv[1]),
+                    w.z * (o.z * rr) * gate_fn(a.gate, gv[2]), w.w * (o.w * rr) * gate_fn(a.gate, gv[3]));
 }
 
 template <int ACT, int ST>
@@ -1063,16 +1134,16 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const int64_t nchunk = (int64_t)cps * a.num_seqs * a.H;
     const int64_t G = (int64_t)a.num_seqs * a.H;
     const int64_t sgrid = (G + 7) / 8 * 16;
-    const int64_t frows = (a.total_tokens * a.H + 7) / 8;
+    const int hgroups = (a.H + 7) / 8;
     if (nchunk > 0)
         hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)nchunk), dim3(256), 0,
                            stream, a, cps);
     if (sgrid > 0)
-        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid), dim3(512), 0,
                            stream, a);
-    if (frows > 0)
-        hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)frows), dim3(256), 0,
-                           stream, a);
+    if (a.total_tokens > 0)
+        hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.total_tokens, hgroups),
+                           dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
