@@ -121,6 +121,15 @@ __device__ __forceinline__ void store_state(void* head_base, int r, int c,
     }
 }
 
+// Store of the thread's state slice kept packed (BF16 storage, decode).
+template <int DV, int RPT, int VEC>
+__device__ __forceinline__ void store_packed(void* head_base, int r, int c,
+                                             const uint4 (&raw)[RPT]) {
+    char* base = static_cast<char*>(head_base) + ((size_t)(r * RPT) * DV + (size_t)c * VEC) * 2;
+#pragma unroll
+    for (int p = 0; p < RPT; ++p) st_stream(base + (size_t)p * DV * 2, raw[p]);
+}
+
 // FP32 record store, [dk][dv] like the pool.
 template <int DV, int RPT, int VEC>
 __device__ __forceinline__ void store_record(float* rec, int r, int c,
@@ -153,11 +162,12 @@ __device__ __forceinline__ float act_from_bits(uint32_t bits) {
 // The raw token is copied to the ring (decode: entry pos mod 4) or to
 // draft_conv (verify).  Also loads alpha, beta and g, writes the conv of v to
 // LDS and the per-wave partial sums of |c_q|^2, |c_k|^2 and c_q . c_k.
-template <int DK, int DV, int ACT, bool VERIFY>
+template <int DK, int DV, int ACT, bool VERIFY, class Issue>
 __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
                                         int slot, int pos, float4 w4a, float4 w4b,
                                         float* vt_s, float (*red_s)[4], float& ca,
-                                        float& cb, float& al, float& beta, float& gv) {
+                                        float& cb, float& al, float& beta, float& gv,
+                                        Issue&& issue_more) {
     constexpr int C = 2 * DK + DV;
     constexpr size_t ESZ = (ACT == kF32) ? 4 : 2;
     const int tid = threadIdx.x;
@@ -185,9 +195,9 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
 
     ca = 0.f;
     cb = 0.f;
+    const size_t ring_slot = (size_t)slot * kConvW;       // ring [slot][4][H][C]
+    uint32_t bA[kConvW], bB[kConvW];
     if (qk || isv) {
-        const size_t ring_slot = (size_t)slot * kConvW;   // ring [slot][4][H][C]
-        uint32_t bA[kConvW], bB[kConvW];
 #pragma unroll
         for (int j = 0; j < kConvW; ++j) {
             const int rel = t - (kConvW - 1) + j;          // draft-token index
@@ -207,6 +217,11 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
             bA[j] = ld_act_bits<ACT>(pa, lc);
             bB[j] = ld_act_bits<ACT>(pb, lc);
         }
+    }
+    // further loads (the state stream on a call's first token) go out behind
+    // the conv taps, so the conv below waits only for the taps
+    issue_more();
+    if (qk || isv) {
         float xa[kConvW], xb[kConvW];
 #pragma unroll
         for (int j = 0; j < kConvW; ++j) {
@@ -280,11 +295,15 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     const float4 w4b = *reinterpret_cast<const float4*>(wB);
     const float norm_w = (tid < DV) ? (a.norm_w ? a.norm_w[tid] : 1.0f) : 0.0f;
 
+    // both row parameters are tested before any store can happen, so they
+    // stay scalar loads and nothing waits on vector memory before the state
+    // stream is issued
     const int slot = a.slot_ids[b];
     const int pos = a.positions[b];
     if (slot < 0) return;
-    if (slot >= a.num_slots) {
-        if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_SLOT);
+    if (slot >= a.num_slots || pos < 0) {
+        if (tid == 0 && a.status)
+            atomicOr(a.status, slot >= a.num_slots ? KDA_STATUS_BAD_SLOT : KDA_STATUS_BAD_POSITION);
         return;
     }
 
@@ -294,25 +313,47 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     const size_t head_off = ((size_t)slot * H + h) * head_elems;
     const void* pool_head = static_cast<const char*>(a.pool) +
                             head_off * (ST == kF32 ? 4 : 2);
+    // token 0: conv taps first, then the state stream; phase A's math and
+    // phase B overlap the state loads, and the unpack waits for them
     uint4 raw[RPT];
-    load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw);
-    if (pos < 0) {
-        if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_POSITION);
-        return;
-    }
-
-    // token 0's phase A overlaps the state loads; the unpack then waits for them
     float ca, cb, al, beta, gv;
     phase_a<DK, DV, ACT, VERIFY>(a, b, h, 0, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
-                                 beta, gv);
-    float s[RPT][VEC];
-    unpack_state<ST, RPT, VEC>(raw, s);
-    if (pos == 0) {
+                                 beta, gv,
+                                 [&] { load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw); });
+    // A decode call with BF16 storage keeps the state packed as loaded and
+    // widens one row at a time where it is used: the FP32 values are exact
+    // and the update rounds once on the way out, as with a widened copy,
+    // but 16 fewer registers stay live.  Verify and FP32 storage hold the
+    // FP32 state.
+    constexpr bool PACKED = !VERIFY && ST == kBF16;
+    float s[PACKED ? 1 : RPT][VEC];
+    if constexpr (PACKED) {
+        if (pos == 0) {
 #pragma unroll
-        for (int p = 0; p < RPT; ++p)
+            for (int p = 0; p < RPT; ++p) raw[p] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    } else {
+        unpack_state<ST, RPT, VEC>(raw, s);
+        if (pos == 0) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) s[p][e] = 0.f;
+            for (int p = 0; p < RPT; ++p)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) s[p][e] = 0.f;
+        }
     }
+    auto srow = [&](int p, float (&sv)[VEC]) {
+        if constexpr (PACKED) {
+            const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sv[2 * e] = bf16_to_f32(w[e] & 0xffffu);
+                sv[2 * e + 1] = bf16_to_f32(w[e] >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) sv[e] = s[p][e];
+        }
+    };
 
 #pragma unroll 1
     for (int t = 0; t < n; ++t) {
@@ -320,7 +361,7 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
         // ---------------- A. conv, raw copy, norm partial sums -----------
         if (t > 0)
             phase_a<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
-                                         al, beta, gv);
+                                         al, beta, gv, [] {});
         __syncthreads();
 
         // ---------------- B. normalised keys and queries ----------------
@@ -355,12 +396,15 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
                 const float akv[4] = {ak4.x, ak4.y, ak4.z, ak4.w};
                 const float aqv[4] = {aq4.x, aq4.y, aq4.z, aq4.w};
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q) {
+                    float sv[VEC];
+                    srow(p4 + q, sv);
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) {
-                        u[e] = fmaf(s[p4 + q][e], akv[q], u[e]);
-                        o[e] = fmaf(s[p4 + q][e], aqv[q], o[e]);
+                        u[e] = fmaf(sv[e], akv[q], u[e]);
+                        o[e] = fmaf(sv[e], aqv[q], o[e]);
                     }
+                }
             }
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
@@ -406,10 +450,19 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
                 const float alv[4] = {al4.x, al4.y, al4.z, al4.w};
                 const float khv[4] = {kh4.x, kh4.y, kh4.z, kh4.w};
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
+                for (int q = 0; q < 4; ++q) {
+                    float sv[VEC];
+                    srow(p4 + q, sv);
 #pragma unroll
-                    for (int e = 0; e < VEC; ++e)
-                        s[p4 + q][e] = fmaf(khv[q], d[e], s[p4 + q][e] * alv[q]);
+                    for (int e = 0; e < VEC; ++e) sv[e] = fmaf(khv[q], d[e], sv[e] * alv[q]);
+                    if constexpr (PACKED) {
+                        raw[p4 + q] = make_uint4(pack_bf16x2(sv[0], sv[1]), pack_bf16x2(sv[2], sv[3]),
+                                                 pack_bf16x2(sv[4], sv[5]), pack_bf16x2(sv[6], sv[7]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < VEC; ++e) s[p4 + q][e] = sv[e];
+                    }
+                }
             }
         }
         if constexpr (VERIFY) {
@@ -427,7 +480,9 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
         // reading before this token's last barrier or in its own phase E.
     }
 
-    if constexpr (!VERIFY) {
+    if constexpr (PACKED) {
+        store_packed<DV, RPT, VEC>(const_cast<void*>(pool_head), r, c, raw);
+    } else if constexpr (!VERIFY) {
         store_state<ST, DV, RPT, VEC>(const_cast<void*>(pool_head), r, c, s);
     }
 }
