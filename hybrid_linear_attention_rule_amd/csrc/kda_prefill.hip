@@ -798,6 +798,51 @@ __device__ __forceinline__ SplitOp get_split(const f16x8_t* hi, const f16x8_t* l
     return SplitOp{hi[lane], lo[lane]};
 }
 
+// Every operand a product step reads from LDS is requested first and then
+// pinned by one empty assembly statement, so the wave waits once for all of
+// them instead of once per fragment (the compiler otherwise places each read
+// right before its first matrix instruction and waits for it there).
+__device__ __forceinline__ void pin(SplitOp (&f)[8]) {
+    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
+                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
+                      "+v"(f[4].hi), "+v"(f[4].lo), "+v"(f[5].hi), "+v"(f[5].lo),
+                      "+v"(f[6].hi), "+v"(f[6].lo), "+v"(f[7].hi), "+v"(f[7].lo));
+}
+__device__ __forceinline__ void pin(SplitOp (&f)[8], SplitOp (&b)[4]) {
+    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
+                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
+                      "+v"(f[4].hi), "+v"(f[4].lo), "+v"(f[5].hi), "+v"(f[5].lo),
+                      "+v"(f[6].hi), "+v"(f[6].lo), "+v"(f[7].hi), "+v"(f[7].lo),
+                      "+v"(b[0].hi), "+v"(b[0].lo), "+v"(b[1].hi), "+v"(b[1].lo),
+                      "+v"(b[2].hi), "+v"(b[2].lo), "+v"(b[3].hi), "+v"(b[3].lo));
+}
+__device__ __forceinline__ void pin(SplitOp& x, SplitOp& y, SplitOp& z) {
+    asm volatile("" : "+v"(x.hi), "+v"(x.lo), "+v"(y.hi), "+v"(y.lo), "+v"(z.hi), "+v"(z.lo));
+}
+
+// acc[t] += sum over four 32-deep k blocks of fa[2 kb + t] * b[kb] for two
+// row tiles t, with one accumulator per (pass, tile): six independent chains
+// keep the matrix pipe busy.  The hi*hi pass starts from acc.
+__device__ __forceinline__ void prod2x4(const SplitOp (&fa)[8], const SplitOp (&b)[4],
+                                        f32x4_t (&acc)[2]) {
+    f32x4_t pa[3][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        pa[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pa[1][t] = pa[0][t];
+        pa[2][t] = acc[t];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        three_passes([&](auto P) {
+            constexpr int pp = decltype(P)::value;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) pa[pp][t] = mma_pass<pp>(fa[2 * kb + t], b[kb], pa[pp][t]);
+        });
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t] = pa[2][t] + pa[1][t] + pa[0][t];
+}
+
 // State pass.  Two 512-thread workgroups per (sequence, head), 64 value
 // columns each, in four 16-column slices.  Each slice has two waves on one
 // SIMD: the U/S wave (waves 0-3) holds the slice's state and computes
@@ -878,8 +923,9 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
         }
     }
 
-    // O wave: O of the previous half, stored after the next barrier H so that
-    // the store latency overlaps the next half's work
+    // O wave: O of the previous half, stored during the next half, after that
+    // half's first product (issued right after barrier H, the stores would
+    // queue behind the half's DMA loads and hold up the wave)
     f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     int orow0 = -1;
     auto store_o = [&]() {
@@ -910,57 +956,52 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
             ut1[0] = ld_ut(cc, 1, 0);
             ut1[1] = ld_ut(cc, 1, 1);
             // U0 = Ut - W S (accumulated at 2^8)
-            f32x4_t acc[2] = {ut0[0] * kScW, ut0[1] * kScW};
+            SplitOp fw[8];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const SplitOp f0 = ld_frag(buf0, frag_w(0, kb), lane);
-                const SplitOp f1 = ld_frag(buf0, frag_w(1, kb), lane);
-                three_passes([&](auto P) {
-                    acc[0] = mma_pass<decltype(P)::value>(f0, sb[kb], acc[0]);
-                    acc[1] = mma_pass<decltype(P)::value>(f1, sb[kb], acc[1]);
-                });
+                fw[2 * kb] = ld_frag(buf0, frag_w(0, kb), lane);
+                fw[2 * kb + 1] = ld_frag(buf0, frag_w(1, kb), lane);
             }
+            pin(fw);
+            f32x4_t acc[2] = {ut0[0] * kScW, ut0[1] * kScW};
+            prod2x4(fw, sb, acc);
             ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
         } else {
-            store_o();
+            SplitOp fq[8];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
+            for (int kb = 0; kb < 4; ++kb) {
+                sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
+                fq[2 * kb] = ld_frag(buf0, frag_q(0, kb), lane);
+                fq[2 * kb + 1] = ld_frag(buf0, frag_q(1, kb), lane);
+            }
+            pin(fq, sb);
             // O = (e(t,-1) q) S (accumulated at 2^12)
             O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             O[1] = O[0];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const SplitOp f0 = ld_frag(buf0, frag_q(0, kb), lane);
-                const SplitOp f1 = ld_frag(buf0, frag_q(1, kb), lane);
-                three_passes([&](auto P) {
-                    O[0] = mma_pass<decltype(P)::value>(f0, sb[kb], O[0]);
-                    O[1] = mma_pass<decltype(P)::value>(f1, sb[kb], O[1]);
-                });
-            }
+            prod2x4(fq, sb, O);
+            store_o();
         }
         __syncthreads();                                           // X0
         if (uw) {
             // S <- gamma S + Kc^T U0 (accumulated at 2^12); gamma sits in buf0
+            SplitOp fk[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) fk[i] = ld_frag(buf0, frag_k(i), lane);
             const float* gam = reinterpret_cast<const float*>(buf0 + GAM_OFF);
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
                 Sn[ct] = *reinterpret_cast<const f32x4_t*>(&gam[16 * ct + 4 * g]) * S[ct] * kSc;
+            pin(fk);
+            three_passes([&](auto P) {
 #pragma unroll
-            for (int c2 = 0; c2 < 8; c2 += 4) {
-                SplitOp fk[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) fk[i] = ld_frag(buf0, frag_k(c2 + i), lane);
-                three_passes([&](auto P) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Sn[c2 + i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[c2 + i]);
-                });
-            }
+                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[i]);
+            });
         } else {
             ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            const SplitOp fp0 = ld_frag(buf0, frag_p(0, 0, 0), lane);
-            const SplitOp fp1 = ld_frag(buf0, frag_p(0, 1, 0), lane);
+            SplitOp fp0 = ld_frag(buf0, frag_p(0, 0, 0), lane);
+            SplitOp fp1 = ld_frag(buf0, frag_p(0, 1, 0), lane);
+            pin(ub0, fp0, fp1);
             three_passes([&](auto P) {
                 O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
                 O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
@@ -979,34 +1020,33 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 ut0[0] = ld_ut(cc + 1, 0, 0);
                 ut0[1] = ld_ut(cc + 1, 0, 1);
             }
-            f32x4_t acc[2] = {ut1[0] * kScW, ut1[1] * kScW};
+            SplitOp fw[8];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const SplitOp f0 = ld_frag(buf1, frag_w(0, kb), lane);
-                const SplitOp f1 = ld_frag(buf1, frag_w(1, kb), lane);
-                three_passes([&](auto P) {
-                    acc[0] = mma_pass<decltype(P)::value>(f0, sb[kb], acc[0]);
-                    acc[1] = mma_pass<decltype(P)::value>(f1, sb[kb], acc[1]);
-                });
+                fw[2 * kb] = ld_frag(buf1, frag_w(0, kb), lane);
+                fw[2 * kb + 1] = ld_frag(buf1, frag_w(1, kb), lane);
             }
+            pin(fw);
+            f32x4_t acc[2] = {ut1[0] * kScW, ut1[1] * kScW};
+            prod2x4(fw, sb, acc);
             const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
             ub0 = ub1;                    // the U/S wave's next update uses U1
         } else {
-            store_o();
-            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            O[1] = O[0];
+            SplitOp fq[8];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
-                const SplitOp f0 = ld_frag(buf1, frag_q(0, kb), lane);
-                const SplitOp f1 = ld_frag(buf1, frag_q(1, kb), lane);
-                three_passes([&](auto P) {
-                    O[0] = mma_pass<decltype(P)::value>(f0, sb[kb], O[0]);
-                    O[1] = mma_pass<decltype(P)::value>(f1, sb[kb], O[1]);
-                });
+                fq[2 * kb] = ld_frag(buf1, frag_q(0, kb), lane);
+                fq[2 * kb + 1] = ld_frag(buf1, frag_q(1, kb), lane);
             }
-            const SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 0), lane);
-            const SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 0), lane);
+            SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 0), lane);
+            SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 0), lane);
+            pin(fq);
+            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            O[1] = O[0];
+            prod2x4(fq, sb, O);
+            store_o();
+            pin(ub0, fp0, fp1);
             three_passes([&](auto P) {
                 O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
                 O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
@@ -1014,17 +1054,14 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
         }
         __syncthreads();                                           // X1
         if (uw) {
+            SplitOp fk[8];
 #pragma unroll
-            for (int c2 = 0; c2 < 8; c2 += 4) {
-                SplitOp fk[4];
+            for (int i = 0; i < 8; ++i) fk[i] = ld_frag(buf1, frag_k(i), lane);
+            pin(fk);
+            three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) fk[i] = ld_frag(buf1, frag_k(c2 + i), lane);
-                three_passes([&](auto P) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Sn[c2 + i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[c2 + i]);
-                });
-            }
+                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[i]);
+            });
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
             // the next chunk's S, split, for both waves of the slice
@@ -1034,9 +1071,10 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
             }
         } else {
-            const SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            const SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 1), lane);
-            const SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 1), lane);
+            SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 1), lane);
+            SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 1), lane);
+            pin(ub1, fp0, fp1);
             three_passes([&](auto P) {
                 O[0] = mma_pass<decltype(P)::value>(fp0, ub1, O[0]);
                 O[1] = mma_pass<decltype(P)::value>(fp1, ub1, O[1]);
