@@ -101,24 +101,28 @@ struct SeqView {
 };
 
 // Validates sequence s.  Returns false when it must be skipped; `report`
-// selects the one thread in the grid that ORs the status bits.
+// selects the one thread in the grid that ORs the status bits.  All four
+// values are read before the status update can happen, so that for a
+// uniform s they stay scalar loads.
 __device__ __forceinline__ bool seq_view(const PrefillArgs& a, int s, bool report, SeqView& v) {
     const int lo = a.cu_seqlens[s], hi = a.cu_seqlens[s + 1];
+    const int slot = a.slot_ids[s], pos = a.positions[s];
+    int bits = 0;
+    bool ok = true;
     if (!(lo >= 0 && lo <= hi && hi <= a.total_tokens && hi - lo <= a.max_seqlen)) {
-        if (report && a.status) atomicOr(a.status, KDA_STATUS_BAD_SEQLENS);
-        return false;
+        bits = KDA_STATUS_BAD_SEQLENS;
+        ok = false;
+    } else if (slot < 0) {
+        ok = false;                              // inactive: skipped, not an error
+    } else if (slot >= a.num_slots) {
+        bits = KDA_STATUS_BAD_SLOT;
+        ok = false;
+    } else if (pos < 0) {
+        bits = KDA_STATUS_BAD_POSITION;
+        ok = false;
     }
-    const int slot = a.slot_ids[s];
-    if (slot < 0) return false;
-    if (slot >= a.num_slots) {
-        if (report && a.status) atomicOr(a.status, KDA_STATUS_BAD_SLOT);
-        return false;
-    }
-    const int pos = a.positions[s];
-    if (pos < 0) {
-        if (report && a.status) atomicOr(a.status, KDA_STATUS_BAD_POSITION);
-        return false;
-    }
+    if (bits != 0 && report && a.status) atomicOr(a.status, bits);
+    if (!ok) return false;
     v = SeqView{lo, hi - lo, slot, pos};
     return true;
 }
@@ -186,18 +190,18 @@ __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v
 }
 
 // Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
-// [c0, c0 + 8), from the seven raw tokens tb-3..tb+3; zero for tokens at or
-// past L.
+// [c0, c0 + 8), from the seven raw tokens tb-3..tb+3 and the channels' four
+// taps; zero for tokens at or past L.
 template <int ACT>
 __device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[7],
-                                        const float* w, int h, int c0, int tb, int L,
+                                        const float4 (&wt)[8], int tb, int L,
                                         float (&c)[4][8]) {
     float x[7][8];
 #pragma unroll
     for (int m = 0; m < 7; ++m) unpack8<ACT>(r[m], ok[m], x[m]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-        const float4 w4 = *reinterpret_cast<const float4*>(w + ((size_t)h * PD + c0 + q) * kConvW);
+        const float4 w4 = wt[q];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float acc = w4.x * x[e][q];
@@ -210,11 +214,12 @@ __device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok
 }
 
 // Index of (channel c, token t) in a [PD][PC] transposed tile whose 4-token
-// chunks are permuted by channel, so that the 16 lanes of a matrix-core lane
-// group reading 4 consecutive tokens of 16 consecutive channels hit distinct
-// LDS banks.
+// chunks are permuted by channel bits 0-3 and 4-7, so that both the 16 lanes
+// of a matrix-core lane group reading 4 consecutive tokens of 16 consecutive
+// channels and the 16 lanes writing 4 tokens of channels 8 apart hit
+// distinct LDS banks.
 __device__ __forceinline__ int swz(int c, int t) {
-    return c * PC + ((((t >> 2) ^ (c & 15)) << 2) | (t & 3));
+    return c * PC + ((((t >> 2) ^ (c & 15) ^ ((c >> 4) & 15)) << 2) | (t & 3));
 }
 
 // Sum over each row of 16 lanes; every lane of the row gets the same value.
@@ -239,6 +244,15 @@ __device__ __forceinline__ void st_frag(char* dst, int lane, const SplitOp& sp) 
 }
 
 // ---------------------------------------------------------------- chunk
+
+// Workgroup barrier for LDS data only: each wave waits for its own LDS
+// accesses, not for its global loads and stores (no wave of the chunk kernel
+// reads global memory another wave wrote), so stores to the workspace drain
+// while the next step runs.  The memory clobber keeps the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <int ACT>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int cps) {
@@ -294,6 +308,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         Raw8<ACT> rq[7], rk[7], rv[7], ra[4];
         bool okm[7];
         float rb[4];
+        float4 wtq[8], wtk[8], wtv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const size_t wi = ((size_t)h * PD + c0 + q) * kConvW;
+            wtq[q] = *reinterpret_cast<const float4*>(a.wq + wi);
+            wtk[q] = *reinterpret_cast<const float4*>(a.wk + wi);
+            wtv[q] = *reinterpret_cast<const float4*>(a.wv + wi);
+        }
 #pragma unroll
         for (int m = 0; m < 7; ++m) {
             rq[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.q, c0, c0, okm[m]);
@@ -308,8 +330,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             rb[e] = ld_act<ACT>(a.beta, row);
         }
 
+        // the scheduler may not sink any of them below this point (it would
+        // otherwise interleave later loads with the conv of earlier ones)
+        __builtin_amdgcn_sched_barrier(0);
+
         float qh[4][8], kh[4][8], al[4][8];
-        conv4x8<ACT>(rq, okm, a.wq, h, c0, tb, L, qh);
+        conv4x8<ACT>(rq, okm, wtq, tb, L, qh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sq = 0.f;
@@ -319,7 +345,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
-        conv4x8<ACT>(rk, okm, a.wk, h, c0, tb, L, kh);
+        conv4x8<ACT>(rk, okm, wtk, tb, L, kh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sk = 0.f;
@@ -337,7 +363,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             for (int q = 0; q < 8; ++q) al[e][q] = in ? al[e][q] : 1.f;
             bt[e] = in ? rb[e] : 0.f;
         }
-        conv4x8<ACT>(rv, okm, a.wv, h, c0, tb, L, cv);
+        conv4x8<ACT>(rv, okm, wtv, tb, L, cv);
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
         float pp[10], pa[6];
@@ -432,24 +458,31 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         *reinterpret_cast<float4*>(&T4[tb >> 2][c0 + 4]) =
             make_float4(D4[3][4], D4[3][5], D4[3][6], D4[3][7]);
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 2a. wave w >= 1: suffix table AUX[o + j] = alpha over sub-blocks
     // j+1 .. 4w-1, for j < 4w (the column factors of the tiles left of the
     // diagonal block)
     const int aux_o = 2 * wave * (wave - 1);
     if (wave > 0) {
+        const int nj = 4 * wave;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int c = lane + 64 * half;
+            float t4v[12];
+#pragma unroll
+            for (int jj = 0; jj < 12; ++jj) t4v[jj] = T4[jj][c];   // all reads in flight at once
             float run = 1.f;
-            for (int jj = 4 * wave - 1; jj >= 0; --jj) {
-                AUX[aux_o + jj][c] = run;
-                run *= T4[jj][c];
+#pragma unroll
+            for (int jj = 11; jj >= 0; --jj) {
+                if (jj < nj) {
+                    AUX[aux_o + jj][c] = run;
+                    run *= t4v[jj];
+                }
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 2b. cross-sub-block entries of A and P on the matrix cores; wave w
     // owns row block w.  Diagonal 16x16 block: adjacent sub-blocks through
@@ -556,7 +589,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 3a. prefix / suffix products over whole sub-blocks, and the
     // chunk's total decay
@@ -577,7 +610,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
             run *= T4[jj][c];
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 3b. wave 0: T_bb = (I + A_bb)^-1 for the four diagonal blocks,
     // in place (lane = block * 16 + column).  Waves 1..3: scaled-Q,
@@ -603,59 +636,82 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
         for (int t = 0; t < 16; ++t) Am[16 * b + t][16 * b + ic] = x[t];
     } else {
-        for (int f = wave - 1; f < 38; f += 3) {
+        // Static, unrolled loops (no branch between fragments) so that the
+        // LDS reads of later fragments overlap the work of earlier ones.
+        // Wave 1 + w1 takes fragments w1, w1 + 3, ... of each kind; an index
+        // past the last fragment is clamped to it and rewrites the same
+        // bytes.
+        const int w1 = wave - 1;
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {          // (e(t,-1) * qh) rows, A operand
+            const int f = min(w1 + 3 * i, 15);
+            const int tt = f >> 2, kb = f & 3;
+            const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
+            float qd[8], pr[8], x[8];
+            ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
+            ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q] * kSc;
+            st_frag(ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B, lane, split_op(x));
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {          // (e(last,t) * kh)^T, A operand
+            const int f = min(w1 + 3 * i, 15);
+            const int ct = f & 7, kb = f >> 3;
+            const int c = 16 * ct + n;
             float x[8];
-            char* dst;
-            if (f < 16) {                      // (e(t,-1) * qh) rows, A operand
-                const int tt = f >> 2, kb = f & 3;
-                const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
-                float qd[8], pr[8];
-                ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
-                ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q] * kSc;
-                dst = ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B;
-            } else if (f < 32) {               // (e(last,t) * kh)^T, A operand
-                const int ct = (f - 16) & 7, kb = (f - 16) >> 3;
-                const int c = 16 * ct + n;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const int ts = 32 * kb + kslot(g, q);
-                    x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c] * kSc;
-                }
-                dst = ws + kb * HALF_B + frag_k(ct) * FRAG_B;
-            } else {                           // P rows, A operand
-                const int p = f - 32;
-                const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
-                const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
-                ld4x2(&Pm[t][cb], &Pm[t][cb + 16], x);
-#pragma unroll
-                for (int q = 0; q < 8; ++q) x[q] *= kSc;
-                dst = ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B;
+            for (int q = 0; q < 8; ++q) {
+                const int ts = 32 * kb + kslot(g, q);
+                x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c] * kSc;
             }
-            st_frag(dst, lane, split_op(x));
+            st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {          // P rows, A operand
+            const int p = w1 + 3 * i;
+            const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
+            const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
+            float x[8];
+            ld4x2(&Pm[t][cb], &Pm[t][cb + 16], x);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) x[q] *= kSc;
+            st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(x));
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- X. beta_t K_G = beta_t kh_t e(t,-1) and beta_t V, transposed to
     // [channel][token] (swizzled) so that the solve reads 4 tokens at once
     {
         const int c = tid & (PD - 1), th = tid >> 7;
+        float kd[8][4], bq[8][4], pre[8];
 #pragma unroll
         for (int t4 = 0; t4 < 8; ++t4) {
             const int t = 32 * th + 4 * t4;
-            const float pre = AUX[t >> 2][c];
+            pre[t4] = AUX[t >> 2][c];
+            const float4 b4 = *reinterpret_cast<const float4*>(&bet[t]);
+            bq[t4][0] = b4.x; bq[t4][1] = b4.y; bq[t4][2] = b4.z; bq[t4][3] = b4.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kd[t4][e] = KD[t + e][c];
+        }
+        // every read above is issued before the first write below (the
+        // compiler cannot tell the written region from the ones read, and
+        // would otherwise wait for each read before the next write)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t4 = 0; t4 < 8; ++t4) {
+            const int t = 32 * th + 4 * t4;
             *reinterpret_cast<float4*>(&RWt[swz(c, t)]) =
-                make_float4(bet[t] * KD[t][c] * pre, bet[t + 1] * KD[t + 1][c] * pre,
-                            bet[t + 2] * KD[t + 2][c] * pre, bet[t + 3] * KD[t + 3][c] * pre);
+                make_float4(bq[t4][0] * kd[t4][0] * pre[t4], bq[t4][1] * kd[t4][1] * pre[t4],
+                            bq[t4][2] * kd[t4][2] * pre[t4], bq[t4][3] * kd[t4][3] * pre[t4]);
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             *reinterpret_cast<float4*>(&VT[swz(c0 + q, tb)]) =
                 make_float4(bt[0] * cv[0][q], bt[1] * cv[1][q], bt[2] * cv[2][q], bt[3] * cv[3][q]);
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
     // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns
@@ -729,7 +785,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
                 }
         }
     }
-    __syncthreads();
+    lds_sync();
 
     // ---- 5. -W fragments (A operand, k = key channel in pairing order)
 #pragma unroll
