@@ -45,6 +45,7 @@
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace kda {
@@ -100,31 +101,46 @@ struct SeqView {
     int lo, len, slot, pos;
 };
 
+// Checks a sequence's bounds, slot and position.  Returns false when it must
+// be skipped; `bits` gets the status bits to report (0 for an inactive slot).
+__device__ __forceinline__ bool seq_ok(const PrefillArgs& a, int lo, int hi, int slot, int pos,
+                                       int& bits) {
+    bits = 0;
+    if (!(lo >= 0 && lo <= hi && hi <= a.total_tokens && hi - lo <= a.max_seqlen))
+        bits = KDA_STATUS_BAD_SEQLENS;
+    else if (slot < 0)
+        return false;                            // inactive: skipped, not an error
+    else if (slot >= a.num_slots)
+        bits = KDA_STATUS_BAD_SLOT;
+    else if (pos < 0)
+        bits = KDA_STATUS_BAD_POSITION;
+    return bits == 0;
+}
+
 // Validates sequence s.  Returns false when it must be skipped; `report`
-// selects the one thread in the grid that ORs the status bits.  All four
-// values are read before the status update can happen, so that for a
-// uniform s they stay scalar loads.
+// selects the threads that OR the status bits.  All four values are read
+// before the status update can happen, so that for a uniform s they stay
+// scalar loads.
 __device__ __forceinline__ bool seq_view(const PrefillArgs& a, int s, bool report, SeqView& v) {
     const int lo = a.cu_seqlens[s], hi = a.cu_seqlens[s + 1];
     const int slot = a.slot_ids[s], pos = a.positions[s];
-    int bits = 0;
-    bool ok = true;
-    if (!(lo >= 0 && lo <= hi && hi <= a.total_tokens && hi - lo <= a.max_seqlen)) {
-        bits = KDA_STATUS_BAD_SEQLENS;
-        ok = false;
-    } else if (slot < 0) {
-        ok = false;                              // inactive: skipped, not an error
-    } else if (slot >= a.num_slots) {
-        bits = KDA_STATUS_BAD_SLOT;
-        ok = false;
-    } else if (pos < 0) {
-        bits = KDA_STATUS_BAD_POSITION;
-        ok = false;
-    }
+    int bits;
+    const bool ok = seq_ok(a, lo, hi, slot, pos, bits);
     if (bits != 0 && report && a.status) atomicOr(a.status, bits);
     if (!ok) return false;
     v = SeqView{lo, hi - lo, slot, pos};
     return true;
+}
+
+// A 32-bit read through the scalar data cache, waited for at once, of a
+// value the kernel never writes.  For uniform reads inside a loop that also
+// stores to global memory, where the compiler would make a vector load
+// (assuming a store may alias it) and wait behind every outstanding vector
+// access, stores included.
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
+    int32_t v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    return v;
 }
 
 // Eight consecutive activations of one token, as loaded (16-byte aligned).
@@ -148,6 +164,20 @@ __device__ __forceinline__ Raw8<ACT> ld_raw8(const void* base, int64_t idx) {
         r.b = p[1];
     } else {
         r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    }
+    return r;
+}
+
+// The same at byte offset `off` from `base`.
+template <int ACT>
+__device__ __forceinline__ Raw8<ACT> ld_raw8_at(const char* base, uint32_t off) {
+    Raw8<ACT> r;
+    if constexpr (ACT == kF32) {
+        const float4* p = reinterpret_cast<const float4*>(base + off);
+        r.a = p[0];
+        r.b = p[1];
+    } else {
+        r.u = *reinterpret_cast<const uint4*>(base + off);
     }
     return r;
 }
@@ -254,8 +284,122 @@ __device__ __forceinline__ void lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One (chunk, head) work item of the chunk kernel.  Chunk c of sequence s
+// owns workspace slot floor(lo / 64) + s + c; item i is head i % H of slot
+// n_slots - 1 - i / H, so later slots come first, and the few slots that no
+// chunk owns (at most one per sequence) are the only items without work.
+struct ChunkItem {
+    int64_t idx;                     // -1: none left
+    int cc, s, h, t0, L;
+    SeqView v;
+};
+
+// The first item at index i, i + step, ... that has work.  The owner of a
+// slot is the last sequence whose first slot is not above it (first slots
+// grow with s when cu_seqlens is monotone); its bounds are then checked.
+__device__ __forceinline__ ChunkItem next_item(const PrefillArgs& a, int n_slots, int64_t i,
+                                               int64_t step) {
+    const int64_t total = (int64_t)n_slots * a.H;
+    ChunkItem it;
+    it.idx = -1;
+    for (; i < total; i += step) {
+        const int slot = n_slots - 1 - (int)(i / a.H);
+        const int h = (int)(i % a.H);
+        int lo = 0, hi = a.num_seqs - 1, s = -1;
+        while (lo <= hi) {
+            const int mid = (lo + hi) >> 1;
+            if (sload_i32(a.cu_seqlens + mid) / PC + mid <= slot) {
+                s = mid;
+                lo = mid + 1;
+            } else {
+                hi = mid - 1;
+            }
+        }
+        if (s < 0) continue;
+        const int lo_t = sload_i32(a.cu_seqlens + s), hi_t = sload_i32(a.cu_seqlens + s + 1);
+        const int slot_s = sload_i32(a.slot_ids + s), pos = sload_i32(a.positions + s);
+        int bits;
+        if (!seq_ok(a, lo_t, hi_t, slot_s, pos, bits)) continue;
+        const SeqView v{lo_t, hi_t - lo_t, slot_s, pos};
+        const int cc = slot - (v.lo / PC + s);
+        if (cc < 0 || cc * PC >= v.len) continue;
+        it = ChunkItem{i, cc, s, h, cc * PC, min(PC, v.len - cc * PC), v};
+        break;
+    }
+    return it;
+}
+
+// A lane's raw inputs for one item: q, k, v for its seven conv tokens, alpha
+// and beta for its four tokens.
 template <int ACT>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int cps) {
+struct ChunkIn {
+    Raw8<ACT> rq[7], rk[7], rv[7], ra[4];
+    uint32_t rb[4];                  // bits, widened where used (no wait here)
+    bool okm[7];
+};
+
+template <int ACT>
+__device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkItem& it, int tb,
+                                              int c0, ChunkIn<ACT>& in) {
+    const int h = it.h, t0 = it.t0, L = it.L;
+    if (it.cc >= 1 && L == PC) {
+        // Interior chunk: every conv token lies inside the sequence.  Each
+        // load is a uniform row base plus one per-lane byte offset (lane's
+        // first token, head and channels), so the addressing is scalar.
+        constexpr size_t ESZ = ACT == kF32 ? 4 : 2;
+        const size_t row_b = (size_t)a.H * PD * ESZ;             // bytes per token row
+        const int64_t row0 = (int64_t)it.v.lo + t0 - 3;          // token of conv tap 0, lane 0
+        const uint32_t off = (uint32_t)((size_t)tb * row_b + ((size_t)h * PD + c0) * ESZ);
+        const char* qb = static_cast<const char*>(a.q) + row0 * row_b;
+        const char* kb = static_cast<const char*>(a.k) + row0 * row_b;
+        const char* vb = static_cast<const char*>(a.v) + row0 * row_b;
+        const char* ab = static_cast<const char*>(a.alpha) + (row0 + 3) * row_b;
+#pragma unroll
+        for (int m = 0; m < 7; ++m) {
+            in.rq[m] = ld_raw8_at<ACT>(qb + m * row_b, off);
+            in.rk[m] = ld_raw8_at<ACT>(kb + m * row_b, off);
+            in.rv[m] = ld_raw8_at<ACT>(vb + m * row_b, off);
+            in.okm[m] = true;
+        }
+        const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * ESZ;
+        const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * ESZ);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            in.ra[e] = ld_raw8_at<ACT>(ab + e * row_b, off);
+            in.rb[e] = ACT == kF32 ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * ESZ + offb)
+                                   : *reinterpret_cast<const uint16_t*>(bb + e * a.H * ESZ + offb);
+        }
+        return;
+    }
+#pragma unroll
+    for (int m = 0; m < 7; ++m) {
+        in.rq[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.q, c0, c0, in.okm[m]);
+        in.rk[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, in.okm[m]);
+        in.rv[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, in.okm[m]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
+        const int64_t row = (int64_t)(it.v.lo + t0 + min(tb + e, L - 1)) * a.H + h;
+        in.ra[e] = ld_raw8<ACT>(a.alpha, row * PD + c0);
+        in.rb[e] = ld_act_bits<ACT>(a.beta, row);
+    }
+}
+
+// The conv taps of channels [c0, c0 + 8) of head h, for q, k and v.
+__device__ __forceinline__ void load_taps(const PrefillArgs& a, int h, int c0, float4 (&wq)[8],
+                                          float4 (&wk)[8], float4 (&wv)[8]) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const size_t wi = ((size_t)h * PD + c0 + q) * kConvW;
+        wq[q] = *reinterpret_cast<const float4*>(a.wq + wi);
+        wk[q] = *reinterpret_cast<const float4*>(a.wk + wi);
+        wv[q] = *reinterpret_cast<const float4*>(a.wv + wi);
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n_slots) {
     // LDS regions (bytes), reused as the steps go:
     //   RA  kh * D4 [PC][LR]                    -> -W [PC][LR] (step 4)
     //   RB  qh * D4 [PC][LR]                    -> beta K_G transposed (step X)
@@ -283,59 +427,51 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
     float* RWt = reinterpret_cast<float*>(lds + RB);
     float* VT = reinterpret_cast<float*>(lds + RC);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int n = lane & 15, g = lane >> 4;
     const int H = a.H;
-    const int per_c = a.num_seqs * H;
-    // later chunks first, so the first chunks are the most recently written
-    const int cc = cps - 1 - (int)(blockIdx.x / per_c);
-    const int rem = (int)(blockIdx.x % per_c);
-    const int s = rem / H, h = rem % H;
-    SeqView v;
-    if (!seq_view(a, s, cc == 0 && h == 0 && tid == 0, v)) return;
-    const int t0 = cc * PC;
-    if (t0 >= v.len) return;
-    const int L = min(PC, v.len - t0);
-    char* ws = static_cast<char*>(a.workspace) + ((size_t)chunk_slot(v.lo, s, cc) * H + h) * WS_B;
+
+    // Persistent: the workgroup takes items blockIdx.x, + gridDim.x, ...
+    // The next item's inputs are requested as soon as the current item's
+    // convolutions have consumed theirs, so they arrive during steps 2-5.
+    constexpr bool kEarlyTaps = ACT == kBF16;
+    ChunkItem it;
+    ChunkIn<ACT> in;
+    float4 wtq[8], wtk[8], wtv[8];             // conv taps of the lane's channels
+    {
+        const int tid = threadIdx.x, lane = tid & 63;
+        // workgroup 0 validates every sequence once and reports the bad ones
+        if (blockIdx.x == 0)
+            for (int sq = tid; sq < a.num_seqs; sq += 256) {
+                SeqView sv;
+                seq_view(a, sq, true, sv);
+            }
+        it = next_item(a, n_slots, blockIdx.x, gridDim.x);
+        if (it.idx < 0) return;
+        load_chunk_in<ACT>(a, it, 16 * (tid >> 6) + 4 * (lane >> 4), 8 * (lane & 15), in);
+        if constexpr (kEarlyTaps) load_taps(a, it.h, 8 * (lane & 15), wtq, wtk, wtv);
+    }
+    for (;;) {
+    // The thread index is passed through an empty assembly statement on each
+    // item, so that the index arithmetic of every step is redone per item
+    // instead of being hoisted out of the loop and held in registers.
+    int tid_v = threadIdx.x;
+    asm volatile("" : "+v"(tid_v));
+    const int tid = tid_v, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int tb = 16 * wave + 4 * g;          // this lane's sub-block (step 1)
+    const int c0 = 8 * n;                      // and channels
+    const int h = it.h, t0 = it.t0, L = it.L;
+    const SeqView v = it.v;
+    char* ws = static_cast<char*>(a.workspace) + ((size_t)chunk_slot(v.lo, it.s, it.cc) * H + h) * WS_B;
+    ChunkItem nx;
 
     // ---- 1. per lane: sub-block j = g of row block `wave` (tokens tb..tb+3),
     // channels c0..c0+7: conv, L2 norms, decay products, in-sub-block pairs
-    const int tb = 16 * wave + 4 * g;
-    const int c0 = 8 * n;
     float cv[4][8], bt[4];
     {
-        // every load first, so that one memory latency covers them all
-        Raw8<ACT> rq[7], rk[7], rv[7], ra[4];
-        bool okm[7];
-        float rb[4];
-        float4 wtq[8], wtk[8], wtv[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const size_t wi = ((size_t)h * PD + c0 + q) * kConvW;
-            wtq[q] = *reinterpret_cast<const float4*>(a.wq + wi);
-            wtk[q] = *reinterpret_cast<const float4*>(a.wk + wi);
-            wtv[q] = *reinterpret_cast<const float4*>(a.wv + wi);
-        }
-#pragma unroll
-        for (int m = 0; m < 7; ++m) {
-            rq[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.q, c0, c0, okm[m]);
-            rk[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, okm[m]);
-            rv[m] = raw8<ACT>(a, v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, okm[m]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
-            const int64_t row = (int64_t)(v.lo + t0 + min(tb + e, L - 1)) * H + h;
-            ra[e] = ld_raw8<ACT>(a.alpha, row * PD + c0);
-            rb[e] = ld_act<ACT>(a.beta, row);
-        }
-
-        // the scheduler may not sink any of them below this point (it would
-        // otherwise interleave later loads with the conv of earlier ones)
-        __builtin_amdgcn_sched_barrier(0);
-
+        if constexpr (!kEarlyTaps) load_taps(a, h, c0, wtq, wtk, wtv);
         float qh[4][8], kh[4][8], al[4][8];
-        conv4x8<ACT>(rq, okm, wtq, tb, L, qh);
+        conv4x8<ACT>(in.rq, in.okm, wtq, tb, L, qh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sq = 0.f;
@@ -345,7 +481,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
-        conv4x8<ACT>(rk, okm, wtk, tb, L, kh);
+        conv4x8<ACT>(in.rk, in.okm, wtk, tb, L, kh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sk = 0.f;
@@ -357,13 +493,18 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool in = tb + e < L;
-            unpack8<ACT>(ra[e], true, al[e]);
+            const bool live = tb + e < L;
+            unpack8<ACT>(in.ra[e], true, al[e]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) al[e][q] = in ? al[e][q] : 1.f;
-            bt[e] = in ? rb[e] : 0.f;
+            for (int q = 0; q < 8; ++q) al[e][q] = live ? al[e][q] : 1.f;
+            const float bv = ACT == kF32 ? __uint_as_float(in.rb[e]) : bf16_to_f32(in.rb[e]);
+            bt[e] = live ? bv : 0.f;
         }
-        conv4x8<ACT>(rv, okm, wtv, tb, L, cv);
+        conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, cv);
+
+        // every input of this item is consumed: find the next item (its
+        // inputs are requested at the start of step 2b)
+        nx = next_item(a, n_slots, it.idx + gridDim.x, gridDim.x);
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
         float pp[10], pa[6];
@@ -483,6 +624,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
         }
     }
     lds_sync();
+
+    // The next item's inputs.  Requested here rather than right after the
+    // convolutions: by now the previous item's workspace stores have
+    // drained, and the loads still have steps 2b-5 to arrive.
+    if (nx.idx >= 0) load_chunk_in<ACT>(a, nx, tb, c0, in);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2b. cross-sub-block entries of A and P on the matrix cores; wave w
     // owns row block w.  Diagonal 16x16 block: adjacent sub-blocks through
@@ -713,6 +860,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
     }
     lds_sync();
 
+    // the next item's conv taps (this item's were last used in step 1); FP32
+    // inputs take twice the registers, and there the taps are loaded in step 1
+    if (kEarlyTaps && nx.idx >= 0) load_taps(a, nx.h, c0, wtq, wtk, wtv);
+
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
     // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns
     // column tiles 4w..4w+3 of the 256 columns (waves 0-1: W, 2-3: Ut).
@@ -798,6 +949,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int c
 #pragma unroll
         for (int q = 0; q < 8; ++q) x[q] *= kScW;
         st_frag(ws + (tt >> 1) * HALF_B + frag_w(tt & 1, kb) * FRAG_B, lane, split_op(x));
+    }
+    if (nx.idx < 0) break;
+    lds_sync();                                // step 5's reads before the next step 1's writes
+    it = nx;
     }
 }
 
@@ -1222,16 +1377,45 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
                     w.z * (o.z * rr) * gate_fn(a.gate, gv[2]), w.w * (o.w * rr) * gate_fn(a.gate, gv[3]));
 }
 
+static bool is_prime(int64_t x) {
+    if (x < 2) return false;
+    for (int64_t d = 2; d * d <= x; ++d)
+        if (x % d == 0) return false;
+    return true;
+}
+
+// One chunk workgroup per compute unit of the current device (the kernel's
+// LDS allows no more), looked up once per device.
+static int chunk_grid() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int ACT, int ST>
 static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
-    const int cps = (a.max_seqlen + PC - 1) / PC;
-    const int64_t nchunk = (int64_t)cps * a.num_seqs * a.H;
+    const int64_t n_slots = (a.total_tokens + PC - 1) / PC + a.num_seqs;
+    const int64_t nchunk = n_slots * a.H;
     const int64_t G = (int64_t)a.num_seqs * a.H;
     const int64_t sgrid = (G + 7) / 8 * 16;
     const int hgroups = (a.H + 7) / 8;
-    if (nchunk > 0)
-        hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)nchunk), dim3(256), 0,
-                           stream, a, cps);
+    if (nchunk > 0) {
+        // Workgroup b takes items b, b + grid, ...  A prime grid keeps the
+        // items without work (periodic for regular batches) from piling up
+        // on some workgroups.
+        int64_t grid = std::min<int64_t>(nchunk, chunk_grid());
+        while (grid > 2 && !is_prime(grid)) --grid;
+        hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)grid), dim3(256), 0,
+                           stream, a, (int)n_slots);
+    }
     if (sgrid > 0)
         hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid), dim3(512), 0,
                            stream, a);
