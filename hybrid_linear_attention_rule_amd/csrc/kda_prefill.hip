@@ -1054,6 +1054,25 @@ __device__ __forceinline__ void prod2x4(const SplitOp (&fa)[8], const SplitOp (&
     for (int t = 0; t < 2; ++t) acc[t] = pa[2][t] + pa[1][t] + pa[0][t];
 }
 
+// One-way hand-off of a half's U from a slice's U/S wave to its O wave: the
+// U/S wave writes the split U to LDS, waits for those writes, then stores
+// the half's number (never 0) in the slice's flag; the O wave polls the flag
+// before reading U.  The U/S wave never waits for the O wave here (the
+// barriers at each half's start keep both in step), so the hand-off cannot
+// block.  The poll is bounded all the same.
+__device__ __forceinline__ void publish_half(int* flag, int epoch) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    *reinterpret_cast<volatile int*>(flag) = epoch;
+}
+__device__ __forceinline__ void await_half(const int* flag, int epoch) {
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        const int f = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(flag));
+        if (f == epoch) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");
+}
+
 // State pass.  Two 512-thread workgroups per (sequence, head), 64 value
 // columns each, in four 16-column slices.  Each slice has two waves on one
 // SIMD: the U/S wave (waves 0-3) holds the slice's state and computes
@@ -1067,6 +1086,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char buf0[HALF_B];
     __shared__ __attribute__((aligned(16))) char buf1[HALF_B];
     __shared__ SliceX X[4];
+    __shared__ int xflag[4];                      // per slice: last half whose U is published
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
@@ -1076,6 +1096,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
     // The buffers are filled only by the assembly loads above; this store,
     // which never runs (num_seqs >= 1), keeps the compiler from treating
     // them as never written.
+    if (tid < 4) xflag[tid] = 0;                 // visible after the first barrier
     if (a.num_seqs < 0) {
         buf0[tid] = 0;
         buf1[tid] = 0;
@@ -1178,6 +1199,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
             prod2x4(fw, sb, acc);
             ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
+            publish_half(&xflag[slice], 2 * cc + 1);
         } else {
             SplitOp fq[8];
 #pragma unroll
@@ -1193,7 +1215,6 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
             prod2x4(fq, sb, O);
             store_o();
         }
-        __syncthreads();                                           // X0
         if (uw) {
             // S <- gamma S + Kc^T U0 (accumulated at 2^12); gamma sits in buf0
             SplitOp fk[8];
@@ -1209,6 +1230,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[i]);
             });
         } else {
+            await_half(&xflag[slice], 2 * cc + 1);
             ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
             SplitOp fp0 = ld_frag(buf0, frag_p(0, 0, 0), lane);
             SplitOp fp1 = ld_frag(buf0, frag_p(0, 1, 0), lane);
@@ -1242,6 +1264,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
             prod2x4(fw, sb, acc);
             const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
+            publish_half(&xflag[slice], 2 * cc + 2);
             ub0 = ub1;                    // the U/S wave's next update uses U1
         } else {
             SplitOp fq[8];
@@ -1263,7 +1286,6 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
             });
         }
-        __syncthreads();                                           // X1
         if (uw) {
             SplitOp fk[8];
 #pragma unroll
@@ -1282,6 +1304,7 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
             }
         } else {
+            await_half(&xflag[slice], 2 * cc + 2);
             SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
             SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 1), lane);
             SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 1), lane);

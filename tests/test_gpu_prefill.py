@@ -92,6 +92,49 @@ def test_prefill_strong_decay_stays_finite():
     check_prefill(case)
 
 
+def test_prefill_many_sequences_several_items_per_workgroup():
+    """37 sequences of 1..300 tokens over 16 heads continuing stored states:
+    more chunk items than workgroups, so each workgroup runs several items
+    and prefetches the next one's inputs; first, interior and partial chunks
+    mix, and the unused slot between sequences is skipped."""
+    need_gpu()
+    rng = np.random.default_rng(37)
+    lens = [int(x) for x in rng.integers(1, 301, 37)]
+    case = wl.make_prefill(84, lens=lens, H=16, dk=128, dv=128, act="bf16", state="f32",
+                           init="random", slice_len=64, name="prefill_many_seqs")
+    check_prefill(case, full_outputs=True)
+
+
+def test_prefill_inactive_and_bad_rows_among_many():
+    """Inactive sequences scattered among active ones are untouched, a bad
+    slot is reported once and skipped, and the others still match."""
+    torch = need_gpu()
+    lens = [70, 1, 200, 64, 3, 129, 40, 90]
+    case = wl.make_prefill(85, lens=lens, H=4, dk=128, dv=128, act="bf16", state="f32",
+                           init="random", slice_len=32, name="prefill_mixed_rows")
+    ds = dev.make_state(case)
+    slots = ds.slots.copy()
+    skip = [1, 4, 6]
+    keep_pool = {i: ds.pool[ds.slots[i]].clone() for i in skip}
+    slots[1] = -1
+    slots[4] = -1
+    slots[6] = ds.num_slots + 5            # out of range: reported and skipped
+    ds, y, status = run_prefill_gpu(case, ds, slots=slots)
+    assert status == kda.STATUS_BAD_SLOT
+    y_ref, S_ref, _ = oracle.prefill_case(case)
+    got = dev.read_states(ds)
+    cu = case.cu_seqlens
+    for i in range(len(lens)):
+        rows = slice(int(cu[i]), int(cu[i + 1]))
+        if i in skip:
+            assert np.isnan(y[rows]).all()
+            assert torch.equal(ds.pool[ds.slots[i]].view(torch.uint8),
+                               keep_pool[i].view(torch.uint8))
+        else:
+            assert_parity(got[i], S_ref[i], tol_for(case.state), f"state of sequence {i}")
+            assert_parity(y[rows], y_ref[rows], 2e-5, f"outputs of sequence {i}")
+
+
 def test_config4_chunked_prefill():
     need_gpu()
     check_prefill(wl.config(4))
