@@ -976,21 +976,51 @@ __device__ __forceinline__ void three_passes(F&& body) {
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 // One half of a chunk's fragments into LDS: 56 pieces of 1 KB, wave w of
-// the eight copies pieces w, w+8, ...; lane l moves 16 bytes straight from
+// the NW copies pieces w, w+NW, ...; lane l moves 16 bytes straight from
 // global memory to LDS (M0 holds the wave's LDS destination).  Issued as
 // inline assembly: the compiler would otherwise wait for these loads before
 // every LDS read of the other buffer.  The caller waits for them explicitly
 // (s_waitcnt vmcnt(0)) before the barrier that publishes the buffer.
+template <int NW>
 __device__ __forceinline__ void dma_half(const char* src, char* dst, int wave, int lane) {
+    static_assert((HALF_B / 1024) % NW == 0, "pieces per wave");
 #pragma unroll
-    for (int q = 0; q < HALF_B / 1024 / 8; ++q) {
-        const int piece = wave + 8 * q;
+    for (int q = 0; q < HALF_B / 1024 / NW; ++q) {
+        const int piece = wave + NW * q;
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                      :
                      : "v"(src + piece * 1024 + lane * 16),
                        "{m0}"((lds_char_t*)(dst + piece * 1024))
                      : "memory");
     }
+}
+
+// Pulls a later half into the L2 ahead of its DMA: one 4-byte load per
+// 128-byte line of the half's fragments (448 lines) and of the workgroup's
+// 4 KB of Ut (32 lines), two loads per lane over four waves, aimed at a small
+// LDS sink whose contents are never read.  The half's DMA into a working
+// buffer then finds its lines in the L2 instead of waiting on HBM.
+__device__ __forceinline__ void prefetch_lines(const char* frag, const char* ut, char* sink,
+                                               int wave, int lane) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int line = wave * 64 + lane + 256 * r;               // 0..511
+        const char* src = line < HALF_B / 128 ? frag + line * 128
+                                              : ut + min(line - HALF_B / 128, 31) * 128;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                     :
+                     : "v"(src), "{m0}"((lds_char_t*)(sink + wave * 256))
+                     : "memory");
+    }
+}
+
+// One 1 KB piece from global memory to LDS (the wave's 64 lanes, 16 bytes
+// each), the same kind of load.
+__device__ __forceinline__ void dma_1k(const char* src, char* dst, int lane) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src + lane * 16), "{m0}"((lds_char_t*)dst)
+                 : "memory");
 }
 
 // Split operands a column slice's U/S wave hands to its O wave through LDS:
@@ -1060,13 +1090,17 @@ __device__ __forceinline__ void prod2x4(const SplitOp (&fa)[8], const SplitOp (&
 // before reading U.  The U/S wave never waits for the O wave here (the
 // barriers at each half's start keep both in step), so the hand-off cannot
 // block.  The poll is bounded all the same.
+// The flag is accessed through an LDS-typed pointer: through a generic one
+// the volatile access becomes a flat store, which also counts as a vector
+// memory operation and makes the compiler wait for every outstanding load.
+typedef __attribute__((address_space(3))) volatile int lds_vint_t;
 __device__ __forceinline__ void publish_half(int* flag, int epoch) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    *reinterpret_cast<volatile int*>(flag) = epoch;
+    *(lds_vint_t*)flag = epoch;
 }
-__device__ __forceinline__ void await_half(const int* flag, int epoch) {
+__device__ __forceinline__ void await_half(int* flag, int epoch) {
     for (int spin = 0; spin < (1 << 22); ++spin) {
-        const int f = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(flag));
+        const int f = __builtin_amdgcn_readfirstlane(*(lds_vint_t*)flag);
         if (f == epoch) break;
         __builtin_amdgcn_s_sleep(1);
     }
@@ -1081,38 +1115,47 @@ __device__ __forceinline__ void await_half(const int* flag, int epoch) {
 // every fragment of a chunk has one reader per slice, and each SIMD runs
 // two waves.  Per half: barrier H (the half's fragments are in LDS), U and
 // Qg S, barrier X (U is published), the state update and P U.
-template <int ACT, int ST>
-__global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
+template <int ACT, int ST, int NS>
+__global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) {
+    constexpr int NQ = 8 / NS;                    // column groups per (sequence, head)
     __shared__ __attribute__((aligned(16))) char buf0[HALF_B];
     __shared__ __attribute__((aligned(16))) char buf1[HALF_B];
-    __shared__ SliceX X[4];
-    __shared__ int xflag[4];                      // per slice: last half whose U is published
+    __shared__ SliceX X[NS];
+    __shared__ int xflag[NS];                     // per slice: last half whose U is published
+    __shared__ __attribute__((aligned(16))) char pf_sink[2 * NS * 256];
+    // Ut of the workgroup's columns for each half: slice, tile u, 64 lanes x 16 B
+    __shared__ __attribute__((aligned(16))) char utbuf[2][2 * NS * 1024];
+    static_assert(NS == 2, "the line prefetch covers four waves");
+    constexpr int kPF = 2;                        // prefetch loads per wave and half
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
     const int n = lane & 15, g = lane >> 4;
-    const int slice = wave & 3;
-    const bool uw = wave < 4;                     // wave-uniform role
+    const int slice = wave % NS;
+    const bool uw = wave < NS;                    // wave-uniform role
     const int H = a.H;
     // The buffers are filled only by the assembly loads above; this store,
     // which never runs (num_seqs >= 1), keeps the compiler from treating
     // them as never written.
-    if (tid < 4) xflag[tid] = 0;                 // visible after the first barrier
+    if (tid < NS) xflag[tid] = 0;                // visible after the first barrier
     if (a.num_seqs < 0) {
         buf0[tid] = 0;
         buf1[tid] = 0;
+        utbuf[0][tid] = 0;
+        utbuf[1][tid] = 0;
     }
-    // the two column halves of one (sequence, head) sit eight workgroups
-    // apart, so both land on the same XCD and share its L2
+    // the column groups of one (sequence, head) sit eight workgroups apart,
+    // so they land on the same XCD and share its L2
     const int G = a.num_seqs * H;
-    const int r16 = blockIdx.x & 15;
-    const int half = r16 >> 3;
-    const int p = (int)(blockIdx.x >> 4) * 8 + (r16 & 7);
+    const int rr = (int)(blockIdx.x % (8 * NQ));
+    const int grp = rr >> 3;
+    const int p = (int)(blockIdx.x / (8 * NQ)) * 8 + (rr & 7);
     if (p >= G) return;
     const int s = p / H, h = p % H;
     SeqView v;
     if (!seq_view(a, s, false, v)) return;
     if (v.len == 0) return;
-    const int j16 = 4 * half + slice;
+    const int j16 = NS * grp + slice;
     const int jc = 16 * j16 + n;
     const size_t head_off = ((size_t)v.slot * H + h) * PD * PD;
     SliceX& xs = X[slice];
@@ -1121,23 +1164,26 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
         return static_cast<const char*>(a.workspace) +
                ((size_t)chunk_slot(v.lo, s, c) * H + h) * WS_B;
     };
-    auto ld_ut = [&](int c, int hh, int u) -> f32x4_t {
-        return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
-                                                 ((((hh * 8 + j16) * 2 + u) * 64 + lane) * 16));
+    // wave w moves Ut piece w of a half: slice w / 2, tile w % 2
+    const int ut_j16 = NS * grp + (wave >> 1);
+    auto ut_src = [&](int c, int hh) -> const char* {
+        return cws(c) + UT_OFF + (((hh * 8 + ut_j16) * 2 + (wave & 1)) * 64) * 16;
+    };
+    auto ld_ut = [&](int hb, int u) -> f32x4_t {
+        return *reinterpret_cast<const f32x4_t*>(&utbuf[hb][(slice * 2 + u) * 1024 + lane * 16]);
     };
 
     const int nch = (v.len + PC - 1) / PC;
-    dma_half(cws(0), buf0, wave, lane);
+    dma_half<2 * NS>(cws(0), buf0, wave, lane);
+    dma_1k(ut_src(0, 0), &utbuf[0][wave * 1024], lane);
 
     // U/S wave: state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
     f32x4_t S[8], Sn[8];
-    f32x4_t ut0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, ut1[2] = {ut0[0], ut0[1]};
+
     SplitOp sb[4];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (uw) {
-        ut0[0] = ld_ut(0, 0, 0);
-        ut0[1] = ld_ut(0, 0, 1);
         if (v.pos > 0) {
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
@@ -1176,17 +1222,27 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
     // through it, so that the compiler sees them as ready and inserts no
     // counted wait of its own (which would also wait on the newer DMA).
     SplitOp ub0;
+    bool pf = false;                              // prefetch loads outstanding
     for (int cc = 0; cc < nch; ++cc) {
         // ======== first half: tokens 0..31 of the chunk ========
-        asm volatile("s_waitcnt vmcnt(0)" : "+v"(ut0[0]), "+v"(ut0[1]) : : "memory");
+        // Wait for this half's fragments.  The prefetches issued last (kPF per
+        // wave after the DMA) may stay in flight: loads complete in order.
+        if (pf)
+            asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kPF) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("" : "+v"(S[0]), "+v"(S[1]), "+v"(S[2]), "+v"(S[3]), "+v"(S[4]), "+v"(S[5]),
                           "+v"(S[6]), "+v"(S[7]));
         __syncthreads();                                           // H0
-        dma_half(cws(cc) + HALF_B, buf1, wave, lane);
+        // the next half's DMA, then the prefetch of the half after it
+        dma_half<2 * NS>(cws(cc) + HALF_B, buf1, wave, lane);
+        dma_1k(ut_src(cc, 1), &utbuf[1][wave * 1024], lane);
+        pf = cc + 1 < nch;
+        if (pf)                                   // the next chunk's first half
+            prefetch_lines(cws(cc + 1), cws(cc + 1) + UT_OFF + ((NS * grp) * 2 * 64) * 16,
+                           pf_sink, wave, lane);
         f32x4_t O[2];
         if (uw) {
-            ut1[0] = ld_ut(cc, 1, 0);
-            ut1[1] = ld_ut(cc, 1, 1);
             // U0 = Ut - W S (accumulated at 2^8)
             SplitOp fw[8];
 #pragma unroll
@@ -1195,8 +1251,10 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 fw[2 * kb + 1] = ld_frag(buf0, frag_w(1, kb), lane);
             }
             pin(fw);
-            f32x4_t acc[2] = {ut0[0] * kScW, ut0[1] * kScW};
+            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             prod2x4(fw, sb, acc);
+            acc[0] += ld_ut(0, 0) * kScW;
+            acc[1] += ld_ut(0, 1) * kScW;
             ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
             publish_half(&xflag[slice], 2 * cc + 1);
@@ -1245,14 +1303,21 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
         }
 
         // ======== second half: tokens 32..63 ========
-        asm volatile("s_waitcnt vmcnt(0)" : "+v"(ut1[0]), "+v"(ut1[1]) : : "memory");
+        if (pf)
+            asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kPF) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();                                           // H1
-        if (cc + 1 < nch) dma_half(cws(cc + 1), buf0, wave, lane);
+        pf = cc + 1 < nch;
+        if (pf) {
+            dma_half<2 * NS>(cws(cc + 1), buf0, wave, lane);
+            dma_1k(ut_src(cc + 1, 0), &utbuf[0][wave * 1024], lane);
+            // the next chunk's second half
+            prefetch_lines(cws(cc + 1) + HALF_B,
+                           cws(cc + 1) + UT_OFF + (((8 + NS * grp) * 2) * 64) * 16, pf_sink,
+                           wave, lane);
+        }
         if (uw) {
-            if (cc + 1 < nch) {
-                ut0[0] = ld_ut(cc + 1, 0, 0);
-                ut0[1] = ld_ut(cc + 1, 0, 1);
-            }
             SplitOp fw[8];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
@@ -1260,8 +1325,10 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
                 fw[2 * kb + 1] = ld_frag(buf1, frag_w(1, kb), lane);
             }
             pin(fw);
-            f32x4_t acc[2] = {ut1[0] * kScW, ut1[1] * kScW};
+            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             prod2x4(fw, sb, acc);
+            acc[0] += ld_ut(1, 0) * kScW;
+            acc[1] += ld_ut(1, 1) * kScW;
             const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
             publish_half(&xflag[slice], 2 * cc + 2);
@@ -1336,14 +1403,14 @@ __global__ __launch_bounds__(512) void prefill_state_kernel(PrefillArgs a) {
 
     // ring: the sequence's last min(3, len) raw tokens (the chunk kernel,
     // which read the old entries, has finished)
-    if (half == 0) {
+    if (grp == 0) {
         constexpr int C = 3 * PD;
         const int pend = v.pos + v.len;
         const int pfirst = max(v.pos, pend - (kConvW - 1));
         for (int pp = pfirst; pp < pend; ++pp) {
             const int64_t row = v.lo + (pp - v.pos);
             const int64_t dst = (((int64_t)v.slot * kConvW + (pp & (kConvW - 1))) * H + h) * C;
-            for (int ch = tid; ch < C; ch += 512) {
+            for (int ch = tid; ch < C; ch += 128 * NS) {
                 const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
                 st_act_bits<ACT>(a.ring, dst + ch,
                                  ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
@@ -1407,6 +1474,9 @@ static bool is_prime(int64_t x) {
     return true;
 }
 
+// 16-column slices per state-pass workgroup (two waves each).
+constexpr int kStateSlices = 2;
+
 // One chunk workgroup per compute unit of the current device (the kernel's
 // LDS allows no more), looked up once per device.
 static int chunk_grid() {
@@ -1428,7 +1498,8 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const int64_t n_slots = (a.total_tokens + PC - 1) / PC + a.num_seqs;
     const int64_t nchunk = n_slots * a.H;
     const int64_t G = (int64_t)a.num_seqs * a.H;
-    const int64_t sgrid = (G + 7) / 8 * 16;
+    constexpr int NS = kStateSlices;
+    const int64_t sgrid = (G + 7) / 8 * 8 * (8 / NS);
     const int hgroups = (a.H + 7) / 8;
     if (nchunk > 0) {
         // Workgroup b takes items b, b + grid, ...  A prime grid keeps the
@@ -1440,8 +1511,8 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            stream, a, (int)n_slots);
     }
     if (sgrid > 0)
-        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid), dim3(512), 0,
-                           stream, a);
+        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST, NS>), dim3((unsigned)sgrid),
+                           dim3(128 * NS), 0, stream, a);
     if (a.total_tokens > 0)
         hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.total_tokens, hgroups),
                            dim3(256), 0, stream, a);
