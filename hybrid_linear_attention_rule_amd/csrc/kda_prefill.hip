@@ -297,14 +297,23 @@ struct ChunkItem {
 // The first item at index i, i + step, ... that has work.  The owner of a
 // slot is the last sequence whose first slot is not above it (first slots
 // grow with s when cu_seqlens is monotone); its bounds are then checked.
+// `prev` (a checked item, or idx < 0) answers slots of its own sequence
+// without any load.
 __device__ __forceinline__ ChunkItem next_item(const PrefillArgs& a, int n_slots, int64_t i,
-                                               int64_t step) {
+                                               int64_t step, const ChunkItem& prev) {
     const int64_t total = (int64_t)n_slots * a.H;
     ChunkItem it;
     it.idx = -1;
     for (; i < total; i += step) {
         const int slot = n_slots - 1 - (int)(i / a.H);
         const int h = (int)(i % a.H);
+        if (prev.idx >= 0) {
+            const int cc = slot - (prev.v.lo / PC + prev.s);
+            if (cc >= 0 && cc * PC < prev.v.len) {
+                it = ChunkItem{i, cc, prev.s, h, cc * PC, min(PC, prev.v.len - cc * PC), prev.v};
+                break;
+            }
+        }
         int lo = 0, hi = a.num_seqs - 1, s = -1;
         while (lo <= hi) {
             const int mid = (lo + hi) >> 1;
@@ -444,7 +453,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 SeqView sv;
                 seq_view(a, sq, true, sv);
             }
-        it = next_item(a, n_slots, blockIdx.x, gridDim.x);
+        ChunkItem none;
+        none.idx = -1;
+        it = next_item(a, n_slots, blockIdx.x, gridDim.x, none);
         if (it.idx < 0) return;
         load_chunk_in<ACT>(a, it, 16 * (tid >> 6) + 4 * (lane >> 4), 8 * (lane & 15), in);
         if constexpr (kEarlyTaps) load_taps(a, it.h, 8 * (lane & 15), wtq, wtk, wtv);
@@ -504,7 +515,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 
         // every input of this item is consumed: find the next item (its
         // inputs are requested at the start of step 2b)
-        nx = next_item(a, n_slots, it.idx + gridDim.x, gridDim.x);
+        nx = next_item(a, n_slots, it.idx + gridDim.x, gridDim.x, it);
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
         float pp[10], pa[6];
@@ -687,19 +698,27 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 Am[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
                 Pm[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
             }
-        if (wave > 0) {
+        // Tiles left of the diagonal, spread so that no wave does more than
+        // two: wave 0 takes (2,0), (2,1); wave 1 (1,0); wave 2 (3,0); wave 3
+        // (3,1), (3,2).
+        const int rb = wave == 0 ? 2 : (wave == 1 ? 1 : 3);     // row block
+        const int bi0 = wave == 3 ? 1 : 0;
+        const int bi1 = wave == 0 ? 2 : (wave == 3 ? 3 : 1);   // exclusive
+        {
             // row operand: scaled to the row block's first token
+            const int tr0 = 16 * rb + n;
             const int jtl = n >> 2;
+            const int aux_rb = 2 * rb * (rb - 1);              // row block rb's suffix table
             SplitOp xk[4], xq[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int cb = 32 * kb + 8 * g;
                 float rk[8], rq[8], t0f[8], t1f[8], t2f[8];
-                ld4x2(&KD[t][cb], &KD[t][cb + 4], rk);
-                ld4x2(&QD[t][cb], &QD[t][cb + 4], rq);
-                ld4x2(&T4[4 * wave][cb], &T4[4 * wave][cb + 4], t0f);
-                ld4x2(&T4[4 * wave + 1][cb], &T4[4 * wave + 1][cb + 4], t1f);
-                ld4x2(&T4[4 * wave + 2][cb], &T4[4 * wave + 2][cb + 4], t2f);
+                ld4x2(&KD[tr0][cb], &KD[tr0][cb + 4], rk);
+                ld4x2(&QD[tr0][cb], &QD[tr0][cb + 4], rq);
+                ld4x2(&T4[4 * rb][cb], &T4[4 * rb][cb + 4], t0f);
+                ld4x2(&T4[4 * rb + 1][cb], &T4[4 * rb + 1][cb + 4], t1f);
+                ld4x2(&T4[4 * rb + 2][cb], &T4[4 * rb + 2][cb + 4], t2f);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
                     float f = jtl >= 1 ? t0f[q] : 1.f;
@@ -711,7 +730,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 xk[kb] = split_op(rk);
                 xq[kb] = split_op(rq);
             }
-            for (int bi = 0; bi < wave; ++bi) {
+            for (int bi = bi0; bi < bi1; ++bi) {
                 const int ic = 16 * bi + n;
                 const int ji = ic >> 2;
                 f32x4_t A = {0.f, 0.f, 0.f, 0.f}, P = A;
@@ -720,7 +739,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                     const int cb = 32 * kb + 8 * g;
                     float ck[8], sf[8];
                     ld4x2(&KE[ic][cb], &KE[ic][cb + 4], ck);
-                    ld4x2(&AUX[aux_o + ji][cb], &AUX[aux_o + ji][cb + 4], sf);
+                    ld4x2(&AUX[aux_rb + ji][cb], &AUX[aux_rb + ji][cb + 4], sf);
 #pragma unroll
                     for (int q = 0; q < 8; ++q) ck[q] *= sf[q] * kSc;
                     const SplitOp sck = split_op(ck);
@@ -729,7 +748,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int tr = 16 * wave + 4 * g + r;
+                    const int tr = 16 * rb + 4 * g + r;
                     Am[tr][ic] = bet[tr] * (A[r] * kInvSc2);
                     Pm[tr][ic] = P[r] * kInvSc2;
                 }
@@ -760,8 +779,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     lds_sync();
 
     // ---- 3b. wave 0: T_bb = (I + A_bb)^-1 for the four diagonal blocks,
-    // in place (lane = block * 16 + column).  Waves 1..3: scaled-Q,
-    // scaled-K and P fragments to the workspace.
+    // in place (lane = block * 16 + column), then the P fragments.  Waves
+    // 1..3: scaled-Q and scaled-K fragments to the workspace.
     if (wave == 0) {
         const int b = lane >> 4, ic = lane & 15;
         float x[16];
@@ -782,6 +801,17 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) Am[16 * b + t][16 * b + ic] = x[t];
+        // then the six P fragments (rows, A operand)
+#pragma unroll
+        for (int p = 0; p < 6; ++p) {
+            const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
+            const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
+            float xp[8];
+            ld4x2(&Pm[t][cb], &Pm[t][cb + 16], xp);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) xp[q] *= kSc;
+            st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(xp));
+        }
     } else {
         // Static, unrolled loops (no branch between fragments) so that the
         // LDS reads of later fragments overlap the work of earlier ones.
@@ -813,17 +843,6 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c] * kSc;
             }
             st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {          // P rows, A operand
-            const int p = w1 + 3 * i;
-            const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
-            const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
-            float x[8];
-            ld4x2(&Pm[t][cb], &Pm[t][cb + 16], x);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] *= kSc;
-            st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(x));
         }
     }
     lds_sync();
