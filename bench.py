@@ -144,12 +144,13 @@ def decode_traffic():
 
 # ------------------------------------------------------------ helpers
 
-def timed_loop(torch, launch, K, W, per_graph):
-    """Capture `per_graph` consecutive launches in one HIP graph, replay it
-    until K launches have run (after W warm-up launches outside the graph),
-    with HIP events on the launch stream around the replays and a device
-    synchronisation on both sides.  Returns (total seconds, seconds per
-    launch, launches timed)."""
+def timed_loop(torch, launch, K, W, per_graph, repeats=5):
+    """Capture `per_graph` consecutive launches in one HIP graph and replay it
+    until K launches have run (after W warm-up launches outside the graph and
+    one untimed replay).  The replays are split over `repeats` timed groups,
+    each bracketed by HIP events on the launch stream with a device
+    synchronisation on both sides.  Returns (total seconds, median seconds
+    per launch over the groups, launches timed, spread)."""
     for i in range(W):
         launch(i)
     torch.cuda.synchronize()
@@ -157,19 +158,49 @@ def timed_loop(torch, launch, K, W, per_graph):
     with torch.cuda.graph(graph):
         for i in range(per_graph):
             launch(W + i)
-    reps = max(1, (K + per_graph - 1) // per_graph)
+    n_replays = max(1, (K + per_graph - 1) // per_graph)
+    repeats = min(repeats, n_replays)
+    groups = [n_replays // repeats + (1 if g < n_replays % repeats else 0)
+              for g in range(repeats)]
     graph.replay()                       # one untimed replay
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    total, per = 0.0, []
+    for reps in groups:
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        dt = t0.elapsed_time(t1) / 1e3
+        total += dt
+        per.append(dt / (reps * per_graph))
+    per.sort()
+    med = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
+    spread = {"repeats": len(per), "min_us": per[0] * 1e6, "max_us": per[-1] * 1e6}
+    return total, med, n_replays * per_graph, spread
+
+
+def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
+    """Achievable device-memory bandwidth: a plain device-to-device copy of
+    `nbytes` (reads and writes nbytes each), timed with HIP events."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
     for _ in range(reps):
-        graph.replay()
+        dst.copy_(src)
     t1.record()
     torch.cuda.synchronize()
-    total = t0.elapsed_time(t1) / 1e3
-    n = reps * per_graph
-    return total, total / n, n
+    dt = t0.elapsed_time(t1) / 1e3
+    del src, dst
+    return 2.0 * nbytes * reps / dt / 1e9
 
 
 def rel_err(got, ref):
@@ -216,7 +247,7 @@ def run_decode_mode(torch, case, K, W, layers):
     # restore layer 0 so that every layer starts from the same state
     pools[0] = dev.make_state(case, spare_slots=0, fill_nan=False)
 
-    total, per_launch, n_timed = timed_loop(torch, launch, K, W, layers * 4)
+    total, per_launch, n_timed, spread = timed_loop(torch, launch, K, W, layers * 4)
     act_b = 2 if case.act == "bf16" else 4
     st_b = 2 if case.state == "bf16" else 4
     n_active = int(case.active.sum(axis=1).mean())
@@ -230,7 +261,7 @@ def run_decode_mode(torch, case, K, W, layers):
         th_per_s=th_per_step / per_launch, bytes_per_launch=bytes_launch,
         hbm_gbs=bytes_launch / per_launch / 1e9,
         hbm_frac=bytes_launch / per_launch / 1e9 / HBM_PEAK_GBS,
-        parity_rel_err={"y": e_y, "state": e_s})
+        spread=spread, parity_rel_err={"y": e_y, "state": e_s})
 
 
 # ------------------------------------------------------------ verify
@@ -263,7 +294,7 @@ def run_verify_mode(torch, case, K, W, layers):
     e_y = rel_err(y.cpu().numpy(), y_ref)
     e_r = rel_err(recs[0].cpu().numpy(), rec_ref)
     assert e_y <= 2e-5 and e_r <= 2e-5, f"verify parity failed: {e_y} {e_r}"
-    total, v_launch, _ = timed_loop(torch, verify, K, W, layers * 2)
+    total, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
     act_b = 2 if case.act == "bf16" else 4
     st_b = 2 if case.state == "bf16" else 4
     per_head = verify_bytes_per_head(n, dk, dv, act_b, st_b)
@@ -274,7 +305,7 @@ def run_verify_mode(torch, case, K, W, layers):
         d = pools[i % layers]
         kda.commit_accepted(d.shape, slot_t, pos_t, acc_t, recs[0], dconv, d.pool,
                             d.ring)
-    c_total, c_launch, _ = timed_loop(torch, commit, K, W, layers * 2)
+    c_total, c_launch, _, c_spread = timed_loop(torch, commit, K, W, layers * 2)
     m = case.accepted
     commit_bytes = int((m > 0).sum()) * H * (dk * dv * 4 + dk * dv * st_b) + \
         int(np.minimum(m, 4).sum()) * H * 2 * C * act_b
@@ -285,6 +316,7 @@ def run_verify_mode(torch, case, K, W, layers):
         hbm_frac=bytes_launch / v_launch / 1e9 / HBM_PEAK_GBS,
         commit_kernel_us=c_launch * 1e6, commit_bytes=commit_bytes,
         commit_hbm_gbs=commit_bytes / c_launch / 1e9,
+        verify_spread=v_spread, commit_spread=c_spread,
         parity_rel_err={"y": e_y, "records": e_r})
 
 
@@ -318,8 +350,8 @@ def run_prefill_mode(torch, case, K, W):
     tol = 2e-5 if case.state == "f32" else 1e-2
     e_s = rel_err(dev.read_states(ds), S_ref)
     assert e_y <= 2e-5 and e_s <= tol, f"prefill parity failed: {e_y} {e_s}"
-    n_timed_req = max(4, K // 32)
-    total, per_launch, n_timed = timed_loop(torch, launch, n_timed_req, max(2, W // 8), 4)
+    n_timed_req = max(10, K // 16)
+    total, per_launch, n_timed, spread = timed_loop(torch, launch, n_timed_req, max(2, W // 8), 2)
     act_b = 2 if case.act == "bf16" else 4
     st_b = 2 if case.state == "bf16" else 4
     lens = np.asarray(case.lens)
@@ -343,32 +375,38 @@ def run_prefill_mode(torch, case, K, W):
         bytes_per_launch=nbytes, hbm_gbs=nbytes / per_launch / 1e9,
         hbm_frac=nbytes / per_launch / 1e9 / HBM_PEAK_GBS,
         roofline_floor_us=floor_s * 1e6, roofline_frac=floor_s / per_launch,
-        parity_rel_err={"y": e_y, "state": e_s})
+        spread=spread, parity_rel_err={"y": e_y, "state": e_s})
 
 
 # ------------------------------------------------------------ CPU oracle
 
 def cpu_baseline(case, seconds):
     """The oracle as it stands, threaded over (sequence, head), on the same
-    workload: whole passes over its decode steps until `seconds` elapse."""
+    workload: whole passes over its decode steps until `seconds` elapse; then
+    one pass on a single thread."""
     import oracle
     from oracle.ref import default_threads
+
+    def passes(th, secs):
+        done, n = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode_case(case, threads=th)
+            n += 1
+            done += int(case.active.sum()) * case.H
+            if time.perf_counter() - t0 >= secs:
+                break
+        return done / (time.perf_counter() - t0), n, time.perf_counter() - t0
+
     th = default_threads()
-    done = 0
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        oracle.decode_case(case, threads=th)
-        passes += 1
-        done += int(case.active.sum()) * case.H
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": done / dt, "unit": "token-head updates/s", "cores": th,
+    rate, n, dt = passes(th, seconds)
+    rate1, n1, dt1 = passes(1, 0.0)
+    return {"value": rate, "unit": "token-head updates/s", "cores": th,
             "kind": "oracle",
-            "sample": f"{passes} full pass(es) of the {case.name} workload "
+            "sample": f"{n} full pass(es) of the {case.name} workload "
                       f"({case.steps} decode steps x {case.batch} rows x {case.H} heads), "
-                      f"fp64 C oracle on {th} threads, {dt:.1f} s"}
+                      f"fp64 C oracle on {th} threads, {dt:.1f} s",
+            "single_thread": {"value": rate1, "sample": f"{n1} pass on 1 thread, {dt1:.1f} s"}}
 
 
 def main():
@@ -396,6 +434,9 @@ def main():
             dst.copy_(src)        # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
+
+    copy_gbs = copy_bandwidth(torch)
+    print(f"# device copy of 1 GiB: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
     case1 = wl.config(1)
     print(f"# decode {case1.name}: steps={args.steps} warmup={args.warmup} "
@@ -447,7 +488,10 @@ def main():
                      "frac": head["hbm_frac"], "traffic": decode_traffic(),
                      "kernel": "kda::token_kernel<128,128,bf16,f32,decode>",
                      "kernel_us": head["kernel_us"],
-                     "bytes_per_launch": head["bytes_per_launch"]},
+                     "kernel_us_spread": head["spread"],
+                     "bytes_per_launch": head["bytes_per_launch"],
+                     "achievable_copy_gbs": copy_gbs,
+                     "frac_of_copy": head["hbm_gbs"] / copy_gbs},
         "cpu_baseline": cpu,
         "parity_rel_err": head["parity_rel_err"],
         "modes": modes,

@@ -1126,26 +1126,72 @@ __device__ __forceinline__ void await_half(int* flag, int epoch) {
     asm volatile("" ::: "memory");
 }
 
-// State pass.  Two 512-thread workgroups per (sequence, head), 64 value
-// columns each, in four 16-column slices.  Each slice has two waves on one
-// SIMD: the U/S wave (waves 0-3) holds the slice's state and computes
-// U = Ut - W S and S <- Diag(gamma) S + Kc^T U; the O wave (waves 4-7)
-// computes O = Qg S + P U from the split S and U the U/S wave publishes.  So
-// every fragment of a chunk has one reader per slice, and each SIMD runs
-// two waves.  Per half: barrier H (the half's fragments are in LDS), U and
-// Qg S, barrier X (U is published), the state update and P U.
+// A fragment straight from the workspace (same layout as in LDS).
+__device__ __forceinline__ SplitOp ld_frag_g(const char* half, int f, int lane) {
+    SplitOp o;
+    o.hi = *reinterpret_cast<const f16x8_t*>(half + f * FRAG_B + lane * 16);
+    o.lo = *reinterpret_cast<const f16x8_t*>(half + f * FRAG_B + 1024 + lane * 16);
+    return o;
+}
+
+// The O waves' share of a half, moved into LDS: the scaled-Q fragments
+// (workspace fragments 8-15) then the P fragments and their neighbours
+// (24-27), 24 pieces of 1 KB, twelve per O wave.
+constexpr int OB_B = 24 * 1024;
+__device__ __forceinline__ void dma_o_half(const char* half, char* dst, int ow, int lane) {
+#pragma unroll
+    for (int q = 0; q < 12; ++q) {
+        const int piece = ow + 2 * q;                        // 0..23
+        const int src_piece = piece < 16 ? 16 + piece : 48 + (piece - 16);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(half + src_piece * 1024 + lane * 16),
+                       "{m0}"((lds_char_t*)(dst + piece * 1024))
+                     : "memory");
+    }
+}
+__device__ __forceinline__ SplitOp ld_ofrag(const char* buf, int f, int lane) {
+    // f: workspace fragment index (8-15 or 24-27)
+    return ld_frag(buf, f < 16 ? f - 8 : 8 + (f - 24), lane);
+}
+
+// Pulls a later half into the L2: one 4-byte load per 128-byte line of its
+// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), four
+// loads per lane of the two O waves, aimed at a small LDS sink whose
+// contents are never read.
+__device__ __forceinline__ void prefetch_half_lines(const char* half, const char* ut, char* sink,
+                                                    int ow, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int line = ow * 64 + lane + 128 * r;               // 0..511
+        const char* src = line < HALF_B / 128 ? half + line * 128
+                                              : ut + min(line - HALF_B / 128, 31) * 128;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
+                     :
+                     : "v"(src), "{m0}"((lds_char_t*)(sink + ow * 256))
+                     : "memory");
+    }
+}
+
+// State pass.  Four 256-thread workgroups per (sequence, head), 32 value
+// columns each in two 16-column slices; each slice has a U/S wave and an O
+// wave, one per SIMD.  The U/S wave holds the slice's 128x16 state and
+// computes U = Ut - W S and S <- Diag(gamma) S + Kc^T U with every operand
+// loaded from the workspace into registers (a half ahead for W, Ut and the
+// decay, at the half's start for Kc); it has no other memory traffic, so the
+// compiler's own waits are exact.  The O wave computes O = Qg S + P U: its
+// fragments stream into LDS by direct loads, double-buffered, and it also
+// pulls each half into the L2 two halves before use.  The two roles run
+// separate loops with the same barriers (one per half, LDS only); U reaches
+// the O wave through LDS and a flag.
 template <int ACT, int ST, int NS>
 __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) {
+    static_assert(NS == 2, "two slices, four waves");
     constexpr int NQ = 8 / NS;                    // column groups per (sequence, head)
-    __shared__ __attribute__((aligned(16))) char buf0[HALF_B];
-    __shared__ __attribute__((aligned(16))) char buf1[HALF_B];
+    __shared__ __attribute__((aligned(16))) char obuf[2][OB_B];
     __shared__ SliceX X[NS];
     __shared__ int xflag[NS];                     // per slice: last half whose U is published
-    __shared__ __attribute__((aligned(16))) char pf_sink[2 * NS * 256];
-    // Ut of the workgroup's columns for each half: slice, tile u, 64 lanes x 16 B
-    __shared__ __attribute__((aligned(16))) char utbuf[2][2 * NS * 1024];
-    static_assert(NS == 2, "the line prefetch covers four waves");
-    constexpr int kPF = 2;                        // prefetch loads per wave and half
+    __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
@@ -1153,15 +1199,13 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
     const int slice = wave % NS;
     const bool uw = wave < NS;                    // wave-uniform role
     const int H = a.H;
-    // The buffers are filled only by the assembly loads above; this store,
-    // which never runs (num_seqs >= 1), keeps the compiler from treating
-    // them as never written.
     if (tid < NS) xflag[tid] = 0;                // visible after the first barrier
+    // The O buffers are filled only by assembly loads; this store, which
+    // never runs (num_seqs >= 1), keeps the compiler from treating them as
+    // never written.
     if (a.num_seqs < 0) {
-        buf0[tid] = 0;
-        buf1[tid] = 0;
-        utbuf[0][tid] = 0;
-        utbuf[1][tid] = 0;
+        obuf[0][tid] = 0;
+        obuf[1][tid] = 0;
     }
     // the column groups of one (sequence, head) sit eight workgroups apart,
     // so they land on the same XCD and share its L2
@@ -1178,31 +1222,24 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
     const int jc = 16 * j16 + n;
     const size_t head_off = ((size_t)v.slot * H + h) * PD * PD;
     SliceX& xs = X[slice];
+    const int nch = (v.len + PC - 1) / PC;
 
     auto cws = [&](int c) -> const char* {
         return static_cast<const char*>(a.workspace) +
                ((size_t)chunk_slot(v.lo, s, c) * H + h) * WS_B;
     };
-    // wave w moves Ut piece w of a half: slice w / 2, tile w % 2
-    const int ut_j16 = NS * grp + (wave >> 1);
-    auto ut_src = [&](int c, int hh) -> const char* {
-        return cws(c) + UT_OFF + (((hh * 8 + ut_j16) * 2 + (wave & 1)) * 64) * 16;
-    };
-    auto ld_ut = [&](int hb, int u) -> f32x4_t {
-        return *reinterpret_cast<const f32x4_t*>(&utbuf[hb][(slice * 2 + u) * 1024 + lane * 16]);
+    // this workgroup's Ut pieces of half hh (two slices x two tiles, 4 KB)
+    auto ut_grp = [&](int c, int hh) -> const char* {
+        return cws(c) + UT_OFF + (((hh * 8 + NS * grp) * 2) * 64) * 16;
     };
 
-    const int nch = (v.len + PC - 1) / PC;
-    dma_half<2 * NS>(cws(0), buf0, wave, lane);
-    dma_1k(ut_src(0, 0), &utbuf[0][wave * 1024], lane);
-
-    // U/S wave: state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
-    f32x4_t S[8], Sn[8];
-
-    SplitOp sb[4];
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (uw) {
+        // ---------------------------------------------------------- U/S wave
+        // state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
+        f32x4_t S[8], Sn[8];
+        SplitOp sb[4];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (v.pos > 0) {
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
@@ -1218,168 +1255,71 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
             sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
             put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
         }
-    }
-
-    // O wave: O of the previous half, stored during the next half, after that
-    // half's first product (issued right after barrier H, the stores would
-    // queue behind the half's DMA loads and hold up the wave)
-    f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    int orow0 = -1;
-    auto store_o = [&]() {
-        if (orow0 < 0) return;
+        auto ld_ut = [&](int c, int hh, int u) -> f32x4_t {
+            return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
+                                                     ((((hh * 8 + j16) * 2 + u) * 64 + lane) * 16));
+        };
+        // Set A: half 0's -W and scaled-K fragments, Ut and the chunk's decay;
+        // set B: half 1's.  Each is loaded a half before use (set A for the
+        // next chunk at the start of half 1, from a clamped chunk index so
+        // that the load is unconditional), and every load of a half is
+        // issued before its first product.
+        SplitOp wA[8], kA[8], wB[8], kB[8];
+        f32x4_t utA[2], utB[2], gmA[8];
+        auto load_A = [&](int c) {
+            const char* h0 = cws(c);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
+            for (int i = 0; i < 8; ++i) wA[i] = ld_frag_g(h0, frag_w(i & 1, i >> 1), lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tl = orow0 + 16 * u + 4 * g + r;
-                if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[u][r];
-            }
-    };
-
-    // The explicit waits below also cover the assembly DMA loads, which the
-    // compiler does not count: registers loaded before such a wait are passed
-    // through it, so that the compiler sees them as ready and inserts no
-    // counted wait of its own (which would also wait on the newer DMA).
-    SplitOp ub0;
-    bool pf = false;                              // prefetch loads outstanding
-    for (int cc = 0; cc < nch; ++cc) {
-        // ======== first half: tokens 0..31 of the chunk ========
-        // Wait for this half's fragments.  The prefetches issued last (kPF per
-        // wave after the DMA) may stay in flight: loads complete in order.
-        if (pf)
-            asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kPF) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        asm volatile("" : "+v"(S[0]), "+v"(S[1]), "+v"(S[2]), "+v"(S[3]), "+v"(S[4]), "+v"(S[5]),
-                          "+v"(S[6]), "+v"(S[7]));
-        __syncthreads();                                           // H0
-        // the next half's DMA, then the prefetch of the half after it
-        dma_half<2 * NS>(cws(cc) + HALF_B, buf1, wave, lane);
-        dma_1k(ut_src(cc, 1), &utbuf[1][wave * 1024], lane);
-        pf = cc + 1 < nch;
-        if (pf)                                   // the next chunk's first half
-            prefetch_lines(cws(cc + 1), cws(cc + 1) + UT_OFF + ((NS * grp) * 2 * 64) * 16,
-                           pf_sink, wave, lane);
-        f32x4_t O[2];
-        if (uw) {
-            // U0 = Ut - W S (accumulated at 2^8)
-            SplitOp fw[8];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                fw[2 * kb] = ld_frag(buf0, frag_w(0, kb), lane);
-                fw[2 * kb + 1] = ld_frag(buf0, frag_w(1, kb), lane);
-            }
-            pin(fw);
-            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            prod2x4(fw, sb, acc);
-            acc[0] += ld_ut(0, 0) * kScW;
-            acc[1] += ld_ut(0, 1) * kScW;
-            ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
-            put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
-            publish_half(&xflag[slice], 2 * cc + 1);
-        } else {
-            SplitOp fq[8];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
-                fq[2 * kb] = ld_frag(buf0, frag_q(0, kb), lane);
-                fq[2 * kb + 1] = ld_frag(buf0, frag_q(1, kb), lane);
-            }
-            pin(fq, sb);
-            // O = (e(t,-1) q) S (accumulated at 2^12)
-            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            O[1] = O[0];
-            prod2x4(fq, sb, O);
-            store_o();
-        }
-        if (uw) {
-            // S <- gamma S + Kc^T U0 (accumulated at 2^12); gamma sits in buf0
-            SplitOp fk[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) fk[i] = ld_frag(buf0, frag_k(i), lane);
-            const float* gam = reinterpret_cast<const float*>(buf0 + GAM_OFF);
+            for (int i = 0; i < 8; ++i) kA[i] = ld_frag_g(h0, frag_k(i), lane);
+            utA[0] = ld_ut(c, 0, 0);
+            utA[1] = ld_ut(c, 0, 1);
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct)
-                Sn[ct] = *reinterpret_cast<const f32x4_t*>(&gam[16 * ct + 4 * g]) * S[ct] * kSc;
-            pin(fk);
+                gmA[ct] = *reinterpret_cast<const f32x4_t*>(h0 + GAM_OFF + (16 * ct + 4 * g) * 4);
+        };
+        auto load_B = [&](int c) {
+            const char* h1 = cws(c) + HALF_B;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wB[i] = ld_frag_g(h1, frag_w(i & 1, i >> 1), lane);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kB[i] = ld_frag_g(h1, frag_k(i), lane);
+            utB[0] = ld_ut(c, 1, 0);
+            utB[1] = ld_ut(c, 1, 1);
+        };
+        load_A(0);
+        for (int cc = 0; cc < nch; ++cc) {
+            // ======== first half: tokens 0..31 of the chunk ========
+            lds_sync();                                            // H0
+            load_B(cc);
+            __builtin_amdgcn_sched_barrier(0);
+            // U0 = Ut - W S (accumulated at 2^8)
+            f32x4_t acc[2] = {utA[0] * kScW, utA[1] * kScW};
+            prod2x4(wA, sb, acc);
+            const SplitOp ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
+            put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
+            publish_half(&xflag[slice], 2 * cc + 1);
+            // S <- gamma S + Kc^T U0 (accumulated at 2^12)
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) Sn[ct] = gmA[ct] * S[ct] * kSc;
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[i]);
+                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(kA[i], ub0, Sn[i]);
             });
-        } else {
-            await_half(&xflag[slice], 2 * cc + 1);
-            ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            SplitOp fp0 = ld_frag(buf0, frag_p(0, 0, 0), lane);
-            SplitOp fp1 = ld_frag(buf0, frag_p(0, 1, 0), lane);
-            pin(ub0, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
-            });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
-            orow0 = cc * PC;
-        }
 
-        // ======== second half: tokens 32..63 ========
-        if (pf)
-            asm volatile("s_waitcnt vmcnt(%0)" : : "n"(kPF) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();                                           // H1
-        pf = cc + 1 < nch;
-        if (pf) {
-            dma_half<2 * NS>(cws(cc + 1), buf0, wave, lane);
-            dma_1k(ut_src(cc + 1, 0), &utbuf[0][wave * 1024], lane);
-            // the next chunk's second half
-            prefetch_lines(cws(cc + 1) + HALF_B,
-                           cws(cc + 1) + UT_OFF + (((8 + NS * grp) * 2) * 64) * 16, pf_sink,
-                           wave, lane);
-        }
-        if (uw) {
-            SplitOp fw[8];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                fw[2 * kb] = ld_frag(buf1, frag_w(0, kb), lane);
-                fw[2 * kb + 1] = ld_frag(buf1, frag_w(1, kb), lane);
-            }
-            pin(fw);
-            f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            prod2x4(fw, sb, acc);
-            acc[0] += ld_ut(1, 0) * kScW;
-            acc[1] += ld_ut(1, 1) * kScW;
+            // ======== second half: tokens 32..63 ========
+            lds_sync();                                            // H1
+            load_A(cc + 1 < nch ? cc + 1 : cc);
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] = utB[0] * kScW;
+            acc[1] = utB[1] * kScW;
+            prod2x4(wB, sb, acc);
             const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
             put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
             publish_half(&xflag[slice], 2 * cc + 2);
-            ub0 = ub1;                    // the U/S wave's next update uses U1
-        } else {
-            SplitOp fq[8];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                fq[2 * kb] = ld_frag(buf1, frag_q(0, kb), lane);
-                fq[2 * kb + 1] = ld_frag(buf1, frag_q(1, kb), lane);
-            }
-            SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 0), lane);
-            SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 0), lane);
-            pin(fq);
-            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            O[1] = O[0];
-            prod2x4(fq, sb, O);
-            store_o();
-            pin(ub0, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
-            });
-        }
-        if (uw) {
-            SplitOp fk[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) fk[i] = ld_frag(buf1, frag_k(i), lane);
-            pin(fk);
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(fk[i], ub0, Sn[i]);
+                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(kB[i], ub1, Sn[i]);
             });
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
@@ -1389,25 +1329,8 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
                 sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
                 put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
             }
-        } else {
-            await_half(&xflag[slice], 2 * cc + 2);
-            SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            SplitOp fp0 = ld_frag(buf1, frag_p(1, 0, 1), lane);
-            SplitOp fp1 = ld_frag(buf1, frag_p(1, 1, 1), lane);
-            pin(ub1, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub1, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub1, O[1]);
-            });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
-            orow0 = cc * PC + 32;
         }
-    }
-    if (!uw) store_o();
-
-    // typed store of the final state, once
-    if (uw) {
+        // typed store of the final state, once
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
@@ -1418,6 +1341,105 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
                 else
                     static_cast<uint16_t*>(a.pool)[e] = (uint16_t)f32_to_bf16_rne(S[ct][r]);
             }
+    } else {
+        // ---------------------------------------------------------- O wave
+        const int ow = wave - NS;                 // 0..1
+        // O of the previous half, stored first thing in the next half, before
+        // this wave's DMA and prefetch loads are issued
+        f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        int orow0 = -1;
+        auto store_o = [&]() {
+            if (orow0 < 0) return;
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tl = orow0 + 16 * u + 4 * g + r;
+                    if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[u][r];
+                }
+        };
+        dma_o_half(cws(0), obuf[0], ow, lane);
+        prefetch_half_lines(cws(0) + HALF_B, ut_grp(0, 1), pf_sink, ow, lane);
+        SplitOp sb[4], ub0;
+        bool pf = true;                           // the youngest loads are prefetches
+        for (int cc = 0; cc < nch; ++cc) {
+            // ======== first half ========
+            // this half's DMA has landed; the prefetch issued after it (four
+            // loads) may stay in flight: loads complete in order
+            if (pf)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_sync();                                            // H0
+            store_o();
+            dma_o_half(cws(cc) + HALF_B, obuf[1], ow, lane);
+            pf = cc + 1 < nch;
+            if (pf) prefetch_half_lines(cws(cc + 1), ut_grp(cc + 1, 0), pf_sink, ow, lane);
+            SplitOp fq[8];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
+                fq[2 * kb] = ld_ofrag(obuf[0], frag_q(0, kb), lane);
+                fq[2 * kb + 1] = ld_ofrag(obuf[0], frag_q(1, kb), lane);
+            }
+            pin(fq, sb);
+            // O = (e(t,-1) q) S (accumulated at 2^12)
+            f32x4_t O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            prod2x4(fq, sb, O);
+            await_half(&xflag[slice], 2 * cc + 1);
+            ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            SplitOp fp0 = ld_ofrag(obuf[0], frag_p(0, 0, 0), lane);
+            SplitOp fp1 = ld_ofrag(obuf[0], frag_p(0, 1, 0), lane);
+            pin(ub0, fp0, fp1);
+            three_passes([&](auto P) {
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
+            orow0 = cc * PC;
+
+            // ======== second half ========
+            if (pf)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_sync();                                            // H1
+            store_o();
+            const bool more = cc + 1 < nch;
+            if (more) dma_o_half(cws(cc + 1), obuf[0], ow, lane);
+            pf = more;
+            if (pf) prefetch_half_lines(cws(cc + 1) + HALF_B, ut_grp(cc + 1, 1), pf_sink, ow, lane);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                fq[2 * kb] = ld_ofrag(obuf[1], frag_q(0, kb), lane);
+                fq[2 * kb + 1] = ld_ofrag(obuf[1], frag_q(1, kb), lane);
+            }
+            fp0 = ld_ofrag(obuf[1], frag_p(1, 0, 0), lane);
+            fp1 = ld_ofrag(obuf[1], frag_p(1, 1, 0), lane);
+            pin(fq);
+            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            O[1] = O[0];
+            prod2x4(fq, sb, O);
+            pin(ub0, fp0, fp1);
+            three_passes([&](auto P) {
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
+            });
+            await_half(&xflag[slice], 2 * cc + 2);
+            SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            fp0 = ld_ofrag(obuf[1], frag_p(1, 0, 1), lane);
+            fp1 = ld_ofrag(obuf[1], frag_p(1, 1, 1), lane);
+            pin(ub1, fp0, fp1);
+            three_passes([&](auto P) {
+                O[0] = mma_pass<decltype(P)::value>(fp0, ub1, O[0]);
+                O[1] = mma_pass<decltype(P)::value>(fp1, ub1, O[1]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
+            orow0 = cc * PC + 32;
+        }
+        store_o();
     }
 
     // ring: the sequence's last min(3, len) raw tokens (the chunk kernel,
