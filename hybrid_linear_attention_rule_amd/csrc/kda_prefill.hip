@@ -1046,7 +1046,7 @@ __device__ __forceinline__ void dma_1k(const char* src, char* dst, int lane) {
 // the chunk's start state as the B operand (k = key channel, four 32-deep
 // blocks) and the current half's U (k = token).
 struct SliceX {
-    f16x8_t sb_hi[4][64], sb_lo[4][64];
+    f16x8_t sb_hi[2][4][64], sb_lo[2][4][64];    // by chunk parity
     f16x8_t ub_hi[64], ub_lo[64];
 };
 
@@ -1076,6 +1076,16 @@ __device__ __forceinline__ void pin(SplitOp (&f)[8], SplitOp (&b)[4]) {
                       "+v"(b[0].hi), "+v"(b[0].lo), "+v"(b[1].hi), "+v"(b[1].lo),
                       "+v"(b[2].hi), "+v"(b[2].lo), "+v"(b[3].hi), "+v"(b[3].lo));
 }
+__device__ __forceinline__ void pin(SplitOp (&f)[4]) {
+    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
+                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo));
+}
+__device__ __forceinline__ void pin(SplitOp (&f)[4], SplitOp (&b)[4]) {
+    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
+                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
+                      "+v"(b[0].hi), "+v"(b[0].lo), "+v"(b[1].hi), "+v"(b[1].lo),
+                      "+v"(b[2].hi), "+v"(b[2].lo), "+v"(b[3].hi), "+v"(b[3].lo));
+}
 __device__ __forceinline__ void pin(SplitOp& x, SplitOp& y, SplitOp& z) {
     asm volatile("" : "+v"(x.hi), "+v"(x.lo), "+v"(y.hi), "+v"(y.lo), "+v"(z.hi), "+v"(z.lo));
 }
@@ -1101,6 +1111,20 @@ __device__ __forceinline__ void prod2x4(const SplitOp (&fa)[8], const SplitOp (&
         });
 #pragma unroll
     for (int t = 0; t < 2; ++t) acc[t] = pa[2][t] + pa[1][t] + pa[0][t];
+}
+
+// acc += sum over four 32-deep k blocks of fa[kb] * b[kb] for one row tile,
+// one accumulator per pass.  The hi*hi pass starts from acc.
+__device__ __forceinline__ void prod1x4(const SplitOp (&fa)[4], const SplitOp (&b)[4],
+                                        f32x4_t& acc) {
+    f32x4_t pa[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, acc};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        three_passes([&](auto P) {
+            constexpr int pp = decltype(P)::value;
+            pa[pp] = mma_pass<pp>(fa[kb], b[kb], pa[pp]);
+        });
+    acc = pa[2] + pa[1] + pa[0];
 }
 
 // One-way hand-off of a half's U from a slice's U/S wave to its O wave: the
@@ -1136,12 +1160,12 @@ __device__ __forceinline__ SplitOp ld_frag_g(const char* half, int f, int lane) 
 
 // The O waves' share of a half, moved into LDS: the scaled-Q fragments
 // (workspace fragments 8-15) then the P fragments and their neighbours
-// (24-27), 24 pieces of 1 KB, twelve per O wave.
+// (24-27), 24 pieces of 1 KB, six per O wave.
 constexpr int OB_B = 24 * 1024;
 __device__ __forceinline__ void dma_o_half(const char* half, char* dst, int ow, int lane) {
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
-        const int piece = ow + 2 * q;                        // 0..23
+    for (int q = 0; q < 6; ++q) {
+        const int piece = ow + 4 * q;                        // 0..23
         const int src_piece = piece < 16 ? 16 + piece : 48 + (piece - 16);
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                      :
@@ -1156,14 +1180,14 @@ __device__ __forceinline__ SplitOp ld_ofrag(const char* buf, int f, int lane) {
 }
 
 // Pulls a later half into the L2: one 4-byte load per 128-byte line of its
-// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), four
-// loads per lane of the two O waves, aimed at a small LDS sink whose
+// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), two
+// loads per lane of the four O waves, aimed at a small LDS sink whose
 // contents are never read.
 __device__ __forceinline__ void prefetch_half_lines(const char* half, const char* ut, char* sink,
                                                     int ow, int lane) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int line = ow * 64 + lane + 128 * r;               // 0..511
+    for (int r = 0; r < 2; ++r) {
+        const int line = ow * 64 + lane + 256 * r;               // 0..511
         const char* src = line < HALF_B / 128 ? half + line * 128
                                               : ut + min(line - HALF_B / 128, 31) * 128;
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -1173,33 +1197,46 @@ __device__ __forceinline__ void prefetch_half_lines(const char* half, const char
     }
 }
 
-// State pass.  Four 256-thread workgroups per (sequence, head), 32 value
-// columns each in two 16-column slices; each slice has a U/S wave and an O
-// wave, one per SIMD.  The U/S wave holds the slice's 128x16 state and
-// computes U = Ut - W S and S <- Diag(gamma) S + Kc^T U with every operand
-// loaded from the workspace into registers (a half ahead for W, Ut and the
-// decay, at the half's start for Kc); it has no other memory traffic, so the
-// compiler's own waits are exact.  The O wave computes O = Qg S + P U: its
-// fragments stream into LDS by direct loads, double-buffered, and it also
-// pulls each half into the L2 two halves before use.  The two roles run
-// separate loops with the same barriers (one per half, LDS only); U reaches
-// the O wave through LDS and a flag.
+// The lane's half (row tile r) of a split U operand: slots 4r..4r+3 of the
+// 16-byte hi and lo words.
+__device__ __forceinline__ void put_half_split(f16x8_t* hi, f16x8_t* lo, int lane, int r,
+                                               const SplitOp4& x) {
+    reinterpret_cast<f16x4_t*>(&hi[lane])[r] = x.hi;
+    reinterpret_cast<f16x4_t*>(&lo[lane])[r] = x.lo;
+}
+
+// State pass.  Four 512-thread workgroups per (sequence, head), 32 value
+// columns each in two 16-column slices.  Each slice has two U/S waves and two
+// O waves, two waves per SIMD.  U/S wave r computes row tile r of
+// U = Ut - W S and holds state channel tiles 4r..4r+3 (channels 64r..64r+63),
+// updating them by S <- Diag(gamma) S + Kc^T U; its operands (-W and
+// scaled-K fragments, Ut, the decay) are loaded from the workspace into
+// registers a half ahead, with no assembly memory operation in its stream,
+// so the compiler's waits are exact.  The split state (the U products' B
+// operand) sits in LDS, double-buffered by chunk parity; each U/S wave writes
+// its two 32-channel blocks.  Each U/S wave publishes its row tile of the
+// split U and sets its flag; the state update and the O waves' P U product
+// wait for both tiles.  O wave r computes row tile r of O = Qg S + P U from
+// scaled-Q and P fragments that stream into LDS by direct loads
+// (double-buffered), and the O waves pull each half into the L2 a half
+// before its first use.  One barrier per half (LDS only).
 template <int ACT, int ST, int NS>
-__global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) {
-    static_assert(NS == 2, "two slices, four waves");
+__global__ __launch_bounds__(256 * NS) void prefill_state_kernel(PrefillArgs a) {
+    static_assert(NS == 2, "two slices, eight waves");
     constexpr int NQ = 8 / NS;                    // column groups per (sequence, head)
     __shared__ __attribute__((aligned(16))) char obuf[2][OB_B];
     __shared__ SliceX X[NS];
-    __shared__ int xflag[NS];                     // per slice: last half whose U is published
-    __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
+    __shared__ int xflag[NS][2];                  // per slice and row tile: last half published
+    __shared__ __attribute__((aligned(16))) char pf_sink[4 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
     const int n = lane & 15, g = lane >> 4;
-    const int slice = wave % NS;
-    const bool uw = wave < NS;                    // wave-uniform role
+    const int slice = wave & 1;
+    const int r = (wave >> 1) & 1;                // row tile (and U/S channel half)
+    const bool uw = wave < 4;                     // wave-uniform role
     const int H = a.H;
-    if (tid < NS) xflag[tid] = 0;                // visible after the first barrier
+    if (tid < 2 * NS) xflag[tid >> 1][tid & 1] = 0;   // visible after the first barrier
     // The O buffers are filled only by assembly loads; this store, which
     // never runs (num_seqs >= 1), keeps the compiler from treating them as
     // never written.
@@ -1232,142 +1269,142 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
     auto ut_grp = [&](int c, int hh) -> const char* {
         return cws(c) + UT_OFF + (((hh * 8 + NS * grp) * 2) * 64) * 16;
     };
+    auto get_sb = [&](int par, SplitOp (&sb)[4]) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sb[kb] = get_split(xs.sb_hi[par][kb], xs.sb_lo[par][kb], lane);
+    };
 
     if (uw) {
         // ---------------------------------------------------------- U/S wave
-        // state slice S[c][jc], c = 16 ct + 4 g + r, in the D-tile layout
-        f32x4_t S[8], Sn[8];
-        SplitOp sb[4];
+        // state channel tiles ct = 4r + i (channels 16 ct + 4 g + e), column jc
+        f32x4_t S[4], Sn[4];
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) S[ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (v.pos > 0) {
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
-                    S[ct][r] = ST == kF32 ? static_cast<const float*>(a.pool)[e]
-                                          : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[e]);
+                for (int e = 0; e < 4; ++e) {
+                    const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc;
+                    S[i][e] = ST == kF32 ? static_cast<const float*>(a.pool)[el]
+                                         : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[el]);
                 }
         }
+        // this wave's 32-channel blocks 2r, 2r+1 of the split state
+        auto put_sb = [&](int par) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
-            put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
-        }
-        auto ld_ut = [&](int c, int hh, int u) -> f32x4_t {
-            return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
-                                                     ((((hh * 8 + j16) * 2 + u) * 64 + lane) * 16));
+            for (int j = 0; j < 2; ++j)
+                put_split(xs.sb_hi[par][2 * r + j], xs.sb_lo[par][2 * r + j], lane,
+                          split_pair(S[2 * j], S[2 * j + 1]));
         };
-        // Set A: half 0's -W and scaled-K fragments, Ut and the chunk's decay;
-        // set B: half 1's.  Each is loaded a half before use (set A for the
-        // next chunk at the start of half 1, from a clamped chunk index so
-        // that the load is unconditional), and every load of a half is
-        // issued before its first product.
-        SplitOp wA[8], kA[8], wB[8], kB[8];
-        f32x4_t utA[2], utB[2], gmA[8];
+        put_sb(0);
+        auto ld_ut = [&](int c, int hh) -> f32x4_t {
+            return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
+                                                     ((((hh * 8 + j16) * 2 + r) * 64 + lane) * 16));
+        };
+        // Set A: half 0's -W (row tile r) and scaled-K (channel tiles 4r..)
+        // fragments, Ut and the decay of those channels; set B: half 1's.
+        SplitOp wA[4], kA[4], wB[4], kB[4];
+        f32x4_t utA, utB, gmA[4];
         auto load_A = [&](int c) {
             const char* h0 = cws(c);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wA[i] = ld_frag_g(h0, frag_w(i & 1, i >> 1), lane);
+            for (int kb = 0; kb < 4; ++kb) wA[kb] = ld_frag_g(h0, frag_w(r, kb), lane);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kA[i] = ld_frag_g(h0, frag_k(i), lane);
-            utA[0] = ld_ut(c, 0, 0);
-            utA[1] = ld_ut(c, 0, 1);
+            for (int i = 0; i < 4; ++i) kA[i] = ld_frag_g(h0, frag_k(4 * r + i), lane);
+            utA = ld_ut(c, 0);
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-                gmA[ct] = *reinterpret_cast<const f32x4_t*>(h0 + GAM_OFF + (16 * ct + 4 * g) * 4);
+            for (int i = 0; i < 4; ++i)
+                gmA[i] = *reinterpret_cast<const f32x4_t*>(h0 + GAM_OFF +
+                                                           (16 * (4 * r + i) + 4 * g) * 4);
         };
         auto load_B = [&](int c) {
             const char* h1 = cws(c) + HALF_B;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) wB[i] = ld_frag_g(h1, frag_w(i & 1, i >> 1), lane);
+            for (int kb = 0; kb < 4; ++kb) wB[kb] = ld_frag_g(h1, frag_w(r, kb), lane);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kB[i] = ld_frag_g(h1, frag_k(i), lane);
-            utB[0] = ld_ut(c, 1, 0);
-            utB[1] = ld_ut(c, 1, 1);
+            for (int i = 0; i < 4; ++i) kB[i] = ld_frag_g(h1, frag_k(4 * r + i), lane);
+            utB = ld_ut(c, 1);
         };
         load_A(0);
         for (int cc = 0; cc < nch; ++cc) {
+            const int par = cc & 1;
             // ======== first half: tokens 0..31 of the chunk ========
             lds_sync();                                            // H0
             load_B(cc);
             __builtin_amdgcn_sched_barrier(0);
-            // U0 = Ut - W S (accumulated at 2^8)
-            f32x4_t acc[2] = {utA[0] * kScW, utA[1] * kScW};
-            prod2x4(wA, sb, acc);
-            const SplitOp ub0 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
-            put_split(xs.ub_hi, xs.ub_lo, lane, ub0);
-            publish_half(&xflag[slice], 2 * cc + 1);
-            // S <- gamma S + Kc^T U0 (accumulated at 2^12)
+            SplitOp sb[4];
+            get_sb(par, sb);
+            // row tile r of U0 = Ut - W S (accumulated at 2^8)
+            f32x4_t acc = utA * kScW;
+            prod1x4(wA, sb, acc);
+            put_half_split(xs.ub_hi, xs.ub_lo, lane, r, split_op4(acc * kInvScW));
+            publish_half(&xflag[slice][r], 2 * cc + 1);
+            // channel tiles 4r.. of S <- gamma S + Kc^T U0 (accumulated at 2^12)
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) Sn[ct] = gmA[ct] * S[ct] * kSc;
+            for (int i = 0; i < 4; ++i) Sn[i] = gmA[i] * S[i] * kSc;
+            await_half(&xflag[slice][1 - r], 2 * cc + 1);
+            SplitOp ub = get_split(xs.ub_hi, xs.ub_lo, lane);
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(kA[i], ub0, Sn[i]);
+                for (int i = 0; i < 4; ++i) Sn[i] = mma_pass<decltype(P)::value>(kA[i], ub, Sn[i]);
             });
 
             // ======== second half: tokens 32..63 ========
             lds_sync();                                            // H1
             load_A(cc + 1 < nch ? cc + 1 : cc);
             __builtin_amdgcn_sched_barrier(0);
-            acc[0] = utB[0] * kScW;
-            acc[1] = utB[1] * kScW;
-            prod2x4(wB, sb, acc);
-            const SplitOp ub1 = split_pair(acc[0] * kInvScW, acc[1] * kInvScW);
-            put_split(xs.ub_hi, xs.ub_lo, lane, ub1);
-            publish_half(&xflag[slice], 2 * cc + 2);
+            get_sb(par, sb);
+            acc = utB * kScW;
+            prod1x4(wB, sb, acc);
+            put_half_split(xs.ub_hi, xs.ub_lo, lane, r, split_op4(acc * kInvScW));
+            publish_half(&xflag[slice][r], 2 * cc + 2);
+            await_half(&xflag[slice][1 - r], 2 * cc + 2);
+            ub = get_split(xs.ub_hi, xs.ub_lo, lane);
             three_passes([&](auto P) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(kB[i], ub1, Sn[i]);
+                for (int i = 0; i < 4; ++i) Sn[i] = mma_pass<decltype(P)::value>(kB[i], ub, Sn[i]);
             });
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) S[ct] = Sn[ct] * kInvSc;
-            // the next chunk's S, split, for both waves of the slice
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                sb[kb] = split_pair(S[2 * kb], S[2 * kb + 1]);
-                put_split(xs.sb_hi[kb], xs.sb_lo[kb], lane, sb[kb]);
-            }
+            for (int i = 0; i < 4; ++i) S[i] = Sn[i] * kInvSc;
+            put_sb(par ^ 1);                              // the next chunk's split state
         }
         // typed store of the final state, once
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const size_t e = head_off + (size_t)(16 * ct + 4 * g + r) * PD + jc;
+            for (int e = 0; e < 4; ++e) {
+                const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc;
                 if (ST == kF32)
-                    static_cast<float*>(a.pool)[e] = S[ct][r];
+                    static_cast<float*>(a.pool)[el] = S[i][e];
                 else
-                    static_cast<uint16_t*>(a.pool)[e] = (uint16_t)f32_to_bf16_rne(S[ct][r]);
+                    static_cast<uint16_t*>(a.pool)[el] = (uint16_t)f32_to_bf16_rne(S[i][e]);
             }
     } else {
         // ---------------------------------------------------------- O wave
-        const int ow = wave - NS;                 // 0..1
-        // O of the previous half, stored first thing in the next half, before
-        // this wave's DMA and prefetch loads are issued
-        f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        const int ow = wave - 4;                  // 0..3
+        // row tile r of O of the previous half, stored first thing in the
+        // next half, before this wave's DMA and prefetch loads are issued
+        f32x4_t Oprev = {0.f, 0.f, 0.f, 0.f};
         int orow0 = -1;
         auto store_o = [&]() {
             if (orow0 < 0) return;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int tl = orow0 + 16 * u + 4 * g + r;
-                    if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[u][r];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int tl = orow0 + 16 * r + 4 * g + e;
+                if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[e];
+            }
         };
         dma_o_half(cws(0), obuf[0], ow, lane);
         prefetch_half_lines(cws(0) + HALF_B, ut_grp(0, 1), pf_sink, ow, lane);
-        SplitOp sb[4], ub0;
         bool pf = true;                           // the youngest loads are prefetches
         for (int cc = 0; cc < nch; ++cc) {
+            const int par = cc & 1;
             // ======== first half ========
-            // this half's DMA has landed; the prefetch issued after it (four
+            // this half's DMA has landed; the prefetch issued after it (two
             // loads) may stay in flight: loads complete in order
             if (pf)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();                                            // H0
@@ -1375,33 +1412,27 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
             dma_o_half(cws(cc) + HALF_B, obuf[1], ow, lane);
             pf = cc + 1 < nch;
             if (pf) prefetch_half_lines(cws(cc + 1), ut_grp(cc + 1, 0), pf_sink, ow, lane);
-            SplitOp fq[8];
+            SplitOp sb[4], fq[4];
+            get_sb(par, sb);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                sb[kb] = get_split(xs.sb_hi[kb], xs.sb_lo[kb], lane);
-                fq[2 * kb] = ld_ofrag(obuf[0], frag_q(0, kb), lane);
-                fq[2 * kb + 1] = ld_ofrag(obuf[0], frag_q(1, kb), lane);
-            }
+            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_ofrag(obuf[0], frag_q(r, kb), lane);
             pin(fq, sb);
             // O = (e(t,-1) q) S (accumulated at 2^12)
-            f32x4_t O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            prod2x4(fq, sb, O);
-            await_half(&xflag[slice], 2 * cc + 1);
-            ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            SplitOp fp0 = ld_ofrag(obuf[0], frag_p(0, 0, 0), lane);
-            SplitOp fp1 = ld_ofrag(obuf[0], frag_p(0, 1, 0), lane);
+            f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+            prod1x4(fq, sb, O);
+            await_half(&xflag[slice][0], 2 * cc + 1);
+            await_half(&xflag[slice][1], 2 * cc + 1);
+            SplitOp ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
+            SplitOp fp0 = ld_ofrag(obuf[0], frag_p(0, r, 0), lane);
+            SplitOp fp1 = fp0;
             pin(ub0, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
-            });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
+            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp0, ub0, O); });
+            Oprev = O * kInvSc;
             orow0 = cc * PC;
 
             // ======== second half ========
             if (pf)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();                                            // H1
@@ -1411,32 +1442,20 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
             pf = more;
             if (pf) prefetch_half_lines(cws(cc + 1) + HALF_B, ut_grp(cc + 1, 1), pf_sink, ow, lane);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                fq[2 * kb] = ld_ofrag(obuf[1], frag_q(0, kb), lane);
-                fq[2 * kb + 1] = ld_ofrag(obuf[1], frag_q(1, kb), lane);
-            }
-            fp0 = ld_ofrag(obuf[1], frag_p(1, 0, 0), lane);
-            fp1 = ld_ofrag(obuf[1], frag_p(1, 1, 0), lane);
+            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_ofrag(obuf[1], frag_q(r, kb), lane);
+            fp0 = ld_ofrag(obuf[1], frag_p(1, r, 0), lane);
+            fp1 = ld_ofrag(obuf[1], frag_p(1, r, 1), lane);
             pin(fq);
-            O[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            O[1] = O[0];
-            prod2x4(fq, sb, O);
+            O = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            prod1x4(fq, sb, O);
             pin(ub0, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub0, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub0, O[1]);
-            });
-            await_half(&xflag[slice], 2 * cc + 2);
+            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp0, ub0, O); });
+            await_half(&xflag[slice][0], 2 * cc + 2);
+            await_half(&xflag[slice][1], 2 * cc + 2);
             SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            fp0 = ld_ofrag(obuf[1], frag_p(1, 0, 1), lane);
-            fp1 = ld_ofrag(obuf[1], frag_p(1, 1, 1), lane);
-            pin(ub1, fp0, fp1);
-            three_passes([&](auto P) {
-                O[0] = mma_pass<decltype(P)::value>(fp0, ub1, O[0]);
-                O[1] = mma_pass<decltype(P)::value>(fp1, ub1, O[1]);
-            });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
+            pin(ub1, fp1, fp0);
+            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp1, ub1, O); });
+            Oprev = O * kInvSc;
             orow0 = cc * PC + 32;
         }
         store_o();
@@ -1451,7 +1470,7 @@ __global__ __launch_bounds__(128 * NS) void prefill_state_kernel(PrefillArgs a) 
         for (int pp = pfirst; pp < pend; ++pp) {
             const int64_t row = v.lo + (pp - v.pos);
             const int64_t dst = (((int64_t)v.slot * kConvW + (pp & (kConvW - 1))) * H + h) * C;
-            for (int ch = tid; ch < C; ch += 128 * NS) {
+            for (int ch = tid; ch < C; ch += 256 * NS) {
                 const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
                 st_act_bits<ACT>(a.ring, dst + ch,
                                  ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
@@ -1553,7 +1572,7 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     }
     if (sgrid > 0)
         hipLaunchKernelGGL((prefill_state_kernel<ACT, ST, NS>), dim3((unsigned)sgrid),
-                           dim3(128 * NS), 0, stream, a);
+                           dim3(256 * NS), 0, stream, a);
     if (a.total_tokens > 0)
         hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.total_tokens, hgroups),
                            dim3(256), 0, stream, a);
