@@ -1158,41 +1158,40 @@ __device__ __forceinline__ SplitOp ld_frag_g(const char* half, int f, int lane) 
     return o;
 }
 
-// The O waves' share of a half, moved into LDS: the scaled-Q fragments
-// (workspace fragments 8-15) then the P fragments and their neighbours
-// (24-27), 24 pieces of 1 KB, six per O wave.
-constexpr int OB_B = 24 * 1024;
-__device__ __forceinline__ void dma_o_half(const char* half, char* dst, int ow, int lane) {
-#pragma unroll
-    for (int q = 0; q < 6; ++q) {
-        const int piece = ow + 4 * q;                        // 0..23
-        const int src_piece = piece < 16 ? 16 + piece : 48 + (piece - 16);
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(half + src_piece * 1024 + lane * 16),
-                       "{m0}"((lds_char_t*)(dst + piece * 1024))
-                     : "memory");
-    }
-}
-__device__ __forceinline__ SplitOp ld_ofrag(const char* buf, int f, int lane) {
-    // f: workspace fragment index (8-15 or 24-27)
-    return ld_frag(buf, f < 16 ? f - 8 : 8 + (f - 24), lane);
-}
-
 // Pulls a later half into the L2: one 4-byte load per 128-byte line of its
-// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), two
-// loads per lane of the four O waves, aimed at a small LDS sink whose
+// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), four
+// loads per lane of the two loader waves, aimed at a small LDS sink whose
 // contents are never read.
 __device__ __forceinline__ void prefetch_half_lines(const char* half, const char* ut, char* sink,
-                                                    int ow, int lane) {
+                                                    int lw, int lane) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int line = ow * 64 + lane + 256 * r;               // 0..511
+    for (int q = 0; q < 4; ++q) {
+        const int line = lw * 64 + lane + 128 * q;               // 0..511
         const char* src = line < HALF_B / 128 ? half + line * 128
                                               : ut + min(line - HALF_B / 128, 31) * 128;
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
                      :
-                     : "v"(src), "{m0}"((lds_char_t*)(sink + ow * 256))
+                     : "v"(src), "{m0}"((lds_char_t*)(sink + lw * 256))
+                     : "memory");
+    }
+}
+
+// One half of a chunk into an LDS buffer: its 56 fragment pieces of 1 KB
+// (same layout as in the workspace) then the workgroup's 4 KB of Ut, 60
+// pieces, loader wave lw (0, 1) taking every other one; lane l moves 16
+// bytes straight from global memory to LDS.
+constexpr int SBUF_PIECES = HALF_B / 1024 + 4;
+constexpr int SBUF_B = SBUF_PIECES * 1024;
+constexpr int SBUF_UT = HALF_B;                   // Ut's offset in the buffer
+__device__ __forceinline__ void dma_state_half(const char* half, const char* ut, char* dst, int lw,
+                                               int lane) {
+#pragma unroll
+    for (int q = 0; q < SBUF_PIECES / 2; ++q) {
+        const int piece = lw + 2 * q;
+        const char* src = piece < HALF_B / 1024 ? half + piece * 1024 : ut + (piece - HALF_B / 1024) * 1024;
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src + lane * 16), "{m0}"((lds_char_t*)(dst + piece * 1024))
                      : "memory");
     }
 }
@@ -1205,257 +1204,317 @@ __device__ __forceinline__ void put_half_split(f16x8_t* hi, f16x8_t* lo, int lan
     reinterpret_cast<f16x4_t*>(&lo[lane])[r] = x.lo;
 }
 
-// State pass.  Four 512-thread workgroups per (sequence, head), 32 value
-// columns each in two 16-column slices.  Each slice has two U/S waves and two
-// O waves, two waves per SIMD.  U/S wave r computes row tile r of
-// U = Ut - W S and holds state channel tiles 4r..4r+3 (channels 64r..64r+63),
-// updating them by S <- Diag(gamma) S + Kc^T U; its operands (-W and
-// scaled-K fragments, Ut, the decay) are loaded from the workspace into
-// registers a half ahead, with no assembly memory operation in its stream,
-// so the compiler's waits are exact.  The split state (the U products' B
-// operand) sits in LDS, double-buffered by chunk parity; each U/S wave writes
-// its two 32-channel blocks.  Each U/S wave publishes its row tile of the
-// split U and sets its flag; the state update and the O waves' P U product
-// wait for both tiles.  O wave r computes row tile r of O = Qg S + P U from
-// scaled-Q and P fragments that stream into LDS by direct loads
-// (double-buffered), and the O waves pull each half into the L2 a half
-// before its first use.  One barrier per half (LDS only).
-template <int ACT, int ST, int NS>
-__global__ __launch_bounds__(256 * NS) void prefill_state_kernel(PrefillArgs a) {
-    static_assert(NS == 2, "two slices, eight waves");
-    constexpr int NQ = 8 / NS;                    // column groups per (sequence, head)
-    __shared__ __attribute__((aligned(16))) char obuf[2][OB_B];
-    __shared__ SliceX X[NS];
-    __shared__ int xflag[NS][2];                  // per slice and row tile: last half published
-    __shared__ __attribute__((aligned(16))) char pf_sink[4 * 256];
+// acc[j] += sum over four 32-deep k blocks of fa[kb] * b[j][kb] for two
+// column tiles j, one accumulator per (pass, tile): six independent chains.
+// The hi*hi pass starts from acc.
+__device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&b)[2][4],
+                                        f32x4_t (&acc)[2]) {
+    f32x4_t pa[3][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        pa[0][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pa[1][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pa[2][j] = acc[j];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        three_passes([&](auto P) {
+            constexpr int pp = decltype(P)::value;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) pa[pp][j] = mma_pass<pp>(fa[kb], b[j][kb], pa[pp][j]);
+        });
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[j] = pa[2][j] + pa[1][j] + pa[0][j];
+}
+
+// Split operands the state pass's waves share through LDS, for the
+// workgroup's two 16-column tiles: the chunk's start state as the B operand
+// (k = key channel, four 32-deep blocks) and the current half's U (k =
+// token).
+struct StateX {
+    f16x8_t sb_hi[2][4][64], sb_lo[2][4][64];     // [column tile][k block]
+    f16x8_t ub_hi[2][64], ub_lo[2][64];           // [column tile]
+};
+
+constexpr int kStateThreads = 384;
+
+// State pass.  Four workgroups per (sequence, head), 32 value columns (two
+// 16-column tiles) each, six waves: two U/S waves, two O waves and two
+// loader waves.
+//
+// The loader waves alone touch global memory for operands: they stream each
+// half of a chunk (all its fragments and the workgroup's Ut) into one of two
+// LDS buffers by direct loads, a half ahead of its use, and pull the half
+// after that into the L2.  The waves that compute never wait on a vector
+// memory issue queue.
+//
+// U/S wave r (0, 1) computes row tile r of U = Ut - W S for both column
+// tiles and holds the state's channels 64r..64r+63 (channel tiles 4r..4r+3)
+// of both, updating them by S <- Diag(gamma) S + Kc^T U.  Its own channel
+// blocks of S feed its U product from registers; the other wave's come
+// through LDS.  Each U/S wave publishes its row tile of the split U and sets
+// its flag; the state update and the O waves' P U product wait for both.
+//
+// O wave r computes row tile r of O = Qg S + P U for both column tiles and
+// stores it.  One barrier per half keeps the buffers in step.
+template <int ACT, int ST>
+__global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) char hbuf[2][SBUF_B];
+    __shared__ StateX X;
+    __shared__ int xflag[2];                      // per row tile: last half published
+    __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
     const int n = lane & 15, g = lane >> 4;
-    const int slice = wave & 1;
-    const int r = (wave >> 1) & 1;                // row tile (and U/S channel half)
-    const bool uw = wave < 4;                     // wave-uniform role
+    const int r = wave & 1;                       // row tile (U/S channel half; loader index)
     const int H = a.H;
-    if (tid < 2 * NS) xflag[tid >> 1][tid & 1] = 0;   // visible after the first barrier
-    // The O buffers are filled only by assembly loads; this store, which
+    if (tid < 2) xflag[tid] = 0;                  // visible after the first barrier
+    // The half buffers are filled only by assembly loads; this store, which
     // never runs (num_seqs >= 1), keeps the compiler from treating them as
     // never written.
-    if (a.num_seqs < 0) {
-        obuf[0][tid] = 0;
-        obuf[1][tid] = 0;
-    }
+    if (a.num_seqs < 0) hbuf[0][tid] = hbuf[1][tid] = 0;
     // the column groups of one (sequence, head) sit eight workgroups apart,
     // so they land on the same XCD and share its L2
     const int G = a.num_seqs * H;
-    const int rr = (int)(blockIdx.x % (8 * NQ));
+    const int rr = (int)(blockIdx.x % 32);
     const int grp = rr >> 3;
-    const int p = (int)(blockIdx.x / (8 * NQ)) * 8 + (rr & 7);
+    const int p = (int)(blockIdx.x / 32) * 8 + (rr & 7);
     if (p >= G) return;
     const int s = p / H, h = p % H;
     SeqView v;
     if (!seq_view(a, s, false, v)) return;
     if (v.len == 0) return;
-    const int j16 = NS * grp + slice;
-    const int jc = 16 * j16 + n;
+    int jc[2];                                    // the lane's value column in each tile
+    jc[0] = 32 * grp + n;
+    jc[1] = 32 * grp + 16 + n;
     const size_t head_off = ((size_t)v.slot * H + h) * PD * PD;
-    SliceX& xs = X[slice];
     const int nch = (v.len + PC - 1) / PC;
 
     auto cws = [&](int c) -> const char* {
         return static_cast<const char*>(a.workspace) +
                ((size_t)chunk_slot(v.lo, s, c) * H + h) * WS_B;
     };
-    // this workgroup's Ut pieces of half hh (two slices x two tiles, 4 KB)
-    auto ut_grp = [&](int c, int hh) -> const char* {
-        return cws(c) + UT_OFF + (((hh * 8 + NS * grp) * 2) * 64) * 16;
-    };
-    auto get_sb = [&](int par, SplitOp (&sb)[4]) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) sb[kb] = get_split(xs.sb_hi[par][kb], xs.sb_lo[par][kb], lane);
+    // half hh of chunk c, and this workgroup's Ut pieces of it (two column
+    // tiles x two row tiles, 4 KB)
+    auto half_src = [&](int hg) -> const char* { return cws(hg >> 1) + (hg & 1) * HALF_B; };
+    auto ut_src = [&](int hg) -> const char* {
+        return cws(hg >> 1) + UT_OFF + ((((hg & 1) * 8 + 2 * grp) * 2) * 64) * 16;
     };
 
-    if (uw) {
+    if (wave >= 4) {
+        // ---------------------------------------------------------- loaders
+        const int nh = 2 * nch;                   // halves, in order
+        dma_state_half(half_src(0), ut_src(0), hbuf[0], r, lane);
+        int npf = 0;                              // prefetch loads issued after the DMA
+        for (int hx = 1; hx <= 2 && hx < nh; ++hx) {
+            prefetch_half_lines(half_src(hx), ut_src(hx), pf_sink, r, lane);
+            npf += 4;
+        }
+        for (int hg = 0; hg < nh; ++hg) {
+            // the DMA of half hg has landed; prefetches issued after it
+            // (loads complete in order) may stay in flight
+            if (npf >= 8)
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else if (npf == 4)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_sync();                           // half hg may be read
+            if (hg + 1 < nh) dma_state_half(half_src(hg + 1), ut_src(hg + 1), hbuf[(hg + 1) & 1], r, lane);
+            npf = 0;
+            if (hg + 3 < nh) {
+                prefetch_half_lines(half_src(hg + 3), ut_src(hg + 3), pf_sink, r, lane);
+                npf = 4;
+            }
+        }
+    } else if (wave < 2) {
         // ---------------------------------------------------------- U/S wave
-        // state channel tiles ct = 4r + i (channels 16 ct + 4 g + e), column jc
-        f32x4_t S[4], Sn[4];
+        // S[j][i]: column tile j, channel tile 4r + i (channels 16 (4r+i) + 4g + e)
+        f32x4_t S[2][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (v.pos > 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const size_t el =
+                            head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc[j];
+                        S[j][i][e] = ST == kF32
+                                         ? static_cast<const float*>(a.pool)[el]
+                                         : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[el]);
+                    }
+        }
+        // the B operands of the U product, own k blocks 2r, 2r+1 in slots 0,
+        // 1 (from registers) and the other wave's in slots 2, 3 (from LDS)
+        SplitOp sb[2][4];
+        auto make_own = [&]() {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    sb[j][m] = split_pair(S[j][2 * m], S[j][2 * m + 1]);
+                    put_split(X.sb_hi[j][2 * r + m], X.sb_lo[j][2 * r + m], lane, sb[j][m]);
+                }
+        };
+        make_own();
+        auto get_other = [&]() {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    sb[j][2 + m] = get_split(X.sb_hi[j][2 * (1 - r) + m],
+                                             X.sb_lo[j][2 * (1 - r) + m], lane);
+        };
+        // row tile r of this half's U (accumulated at 2^8), split, to LDS
+        auto u_tile = [&](const char* buf) {
+            SplitOp w[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                w[m] = ld_frag(buf, frag_w(r, m < 2 ? 2 * r + m : 2 * (1 - r) + m - 2), lane);
+            f32x4_t acc[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[j] = *reinterpret_cast<const f32x4_t*>(buf + SBUF_UT + (2 * j + r) * 1024 +
+                                                           lane * 16) * kScW;
+            prod4x2(w, sb, acc);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                put_half_split(X.ub_hi[j], X.ub_lo[j], lane, r, split_op4(acc[j] * kInvScW));
+        };
+        // channel tiles 4r.. of S += Kc^T U for both column tiles (at 2^12)
+        auto s_update = [&](const char* buf, f32x4_t (&Sn)[2][4]) {
+            SplitOp kf[4], ub[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kf[i] = ld_frag(buf, frag_k(4 * r + i), lane);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ub[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Sn[j][i] = mma_pass<decltype(P)::value>(kf[i], ub[j], Sn[j][i]);
+            });
+        };
+        for (int cc = 0; cc < nch; ++cc) {
+            // ======== first half: tokens 0..31 of the chunk ========
+            lds_sync();                                            // H0
+            get_other();
+            u_tile(hbuf[0]);
+            publish_half(&xflag[r], 2 * cc + 1);
+            f32x4_t Sn[2][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(
+                                       hbuf[0] + GAM_OFF + (16 * (4 * r + i) + 4 * g) * 4) * kSc;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) Sn[j][i] = gm * S[j][i];
+            }
+            await_half(&xflag[1 - r], 2 * cc + 1);
+            s_update(hbuf[0], Sn);
+
+            // ======== second half: tokens 32..63 ========
+            lds_sync();                                            // H1
+            u_tile(hbuf[1]);                              // the other blocks are still held
+            publish_half(&xflag[r], 2 * cc + 2);
+            await_half(&xflag[1 - r], 2 * cc + 2);
+            s_update(hbuf[1], Sn);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * kInvSc;
+            make_own();                                   // the next chunk's split state
+        }
+        // typed store of the final state, once
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc;
-                    S[i][e] = ST == kF32 ? static_cast<const float*>(a.pool)[el]
-                                         : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[el]);
+                    const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc[j];
+                    if (ST == kF32)
+                        static_cast<float*>(a.pool)[el] = S[j][i][e];
+                    else
+                        static_cast<uint16_t*>(a.pool)[el] = (uint16_t)f32_to_bf16_rne(S[j][i][e]);
                 }
-        }
-        // this wave's 32-channel blocks 2r, 2r+1 of the split state
-        auto put_sb = [&](int par) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                put_split(xs.sb_hi[par][2 * r + j], xs.sb_lo[par][2 * r + j], lane,
-                          split_pair(S[2 * j], S[2 * j + 1]));
-        };
-        put_sb(0);
-        auto ld_ut = [&](int c, int hh) -> f32x4_t {
-            return *reinterpret_cast<const f32x4_t*>(cws(c) + UT_OFF +
-                                                     ((((hh * 8 + j16) * 2 + r) * 64 + lane) * 16));
-        };
-        // Set A: half 0's -W (row tile r) and scaled-K (channel tiles 4r..)
-        // fragments, Ut and the decay of those channels; set B: half 1's.
-        SplitOp wA[4], kA[4], wB[4], kB[4];
-        f32x4_t utA, utB, gmA[4];
-        auto load_A = [&](int c) {
-            const char* h0 = cws(c);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) wA[kb] = ld_frag_g(h0, frag_w(r, kb), lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kA[i] = ld_frag_g(h0, frag_k(4 * r + i), lane);
-            utA = ld_ut(c, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                gmA[i] = *reinterpret_cast<const f32x4_t*>(h0 + GAM_OFF +
-                                                           (16 * (4 * r + i) + 4 * g) * 4);
-        };
-        auto load_B = [&](int c) {
-            const char* h1 = cws(c) + HALF_B;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) wB[kb] = ld_frag_g(h1, frag_w(r, kb), lane);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kB[i] = ld_frag_g(h1, frag_k(4 * r + i), lane);
-            utB = ld_ut(c, 1);
-        };
-        load_A(0);
-        for (int cc = 0; cc < nch; ++cc) {
-            const int par = cc & 1;
-            // ======== first half: tokens 0..31 of the chunk ========
-            lds_sync();                                            // H0
-            load_B(cc);
-            __builtin_amdgcn_sched_barrier(0);
-            SplitOp sb[4];
-            get_sb(par, sb);
-            // row tile r of U0 = Ut - W S (accumulated at 2^8)
-            f32x4_t acc = utA * kScW;
-            prod1x4(wA, sb, acc);
-            put_half_split(xs.ub_hi, xs.ub_lo, lane, r, split_op4(acc * kInvScW));
-            publish_half(&xflag[slice][r], 2 * cc + 1);
-            // channel tiles 4r.. of S <- gamma S + Kc^T U0 (accumulated at 2^12)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sn[i] = gmA[i] * S[i] * kSc;
-            await_half(&xflag[slice][1 - r], 2 * cc + 1);
-            SplitOp ub = get_split(xs.ub_hi, xs.ub_lo, lane);
-            three_passes([&](auto P) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Sn[i] = mma_pass<decltype(P)::value>(kA[i], ub, Sn[i]);
-            });
-
-            // ======== second half: tokens 32..63 ========
-            lds_sync();                                            // H1
-            load_A(cc + 1 < nch ? cc + 1 : cc);
-            __builtin_amdgcn_sched_barrier(0);
-            get_sb(par, sb);
-            acc = utB * kScW;
-            prod1x4(wB, sb, acc);
-            put_half_split(xs.ub_hi, xs.ub_lo, lane, r, split_op4(acc * kInvScW));
-            publish_half(&xflag[slice][r], 2 * cc + 2);
-            await_half(&xflag[slice][1 - r], 2 * cc + 2);
-            ub = get_split(xs.ub_hi, xs.ub_lo, lane);
-            three_passes([&](auto P) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) Sn[i] = mma_pass<decltype(P)::value>(kB[i], ub, Sn[i]);
-            });
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[i] = Sn[i] * kInvSc;
-            put_sb(par ^ 1);                              // the next chunk's split state
-        }
-        // typed store of the final state, once
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc;
-                if (ST == kF32)
-                    static_cast<float*>(a.pool)[el] = S[i][e];
-                else
-                    static_cast<uint16_t*>(a.pool)[el] = (uint16_t)f32_to_bf16_rne(S[i][e]);
-            }
     } else {
         // ---------------------------------------------------------- O wave
-        const int ow = wave - 4;                  // 0..3
-        // row tile r of O of the previous half, stored first thing in the
-        // next half, before this wave's DMA and prefetch loads are issued
-        f32x4_t Oprev = {0.f, 0.f, 0.f, 0.f};
+        // row tile r of O of the previous half, stored after the next half's
+        // barrier
+        f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         int orow0 = -1;
         auto store_o = [&]() {
             if (orow0 < 0) return;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tl = orow0 + 16 * r + 4 * g + e;
-                if (tl < v.len) a.y[((int64_t)(v.lo + tl) * H + h) * PD + jc] = Oprev[e];
+                if (tl < v.len) {
+                    float* yrow = a.y + ((int64_t)(v.lo + tl) * H + h) * PD;
+                    yrow[jc[0]] = Oprev[0][e];
+                    yrow[jc[1]] = Oprev[1][e];
+                }
             }
         };
-        dma_o_half(cws(0), obuf[0], ow, lane);
-        prefetch_half_lines(cws(0) + HALF_B, ut_grp(0, 1), pf_sink, ow, lane);
-        bool pf = true;                           // the youngest loads are prefetches
+        SplitOp sb[2][4], fq[4];
         for (int cc = 0; cc < nch; ++cc) {
-            const int par = cc & 1;
             // ======== first half ========
-            // this half's DMA has landed; the prefetch issued after it (two
-            // loads) may stay in flight: loads complete in order
-            if (pf)
-                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();                                            // H0
             store_o();
-            dma_o_half(cws(cc) + HALF_B, obuf[1], ow, lane);
-            pf = cc + 1 < nch;
-            if (pf) prefetch_half_lines(cws(cc + 1), ut_grp(cc + 1, 0), pf_sink, ow, lane);
-            SplitOp sb[4], fq[4];
-            get_sb(par, sb);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_ofrag(obuf[0], frag_q(r, kb), lane);
-            pin(fq, sb);
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    sb[j][kb] = get_split(X.sb_hi[j][kb], X.sb_lo[j][kb], lane);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[0], frag_q(r, kb), lane);
             // O = (e(t,-1) q) S (accumulated at 2^12)
-            f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-            prod1x4(fq, sb, O);
-            await_half(&xflag[slice][0], 2 * cc + 1);
-            await_half(&xflag[slice][1], 2 * cc + 1);
-            SplitOp ub0 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            SplitOp fp0 = ld_ofrag(obuf[0], frag_p(0, r, 0), lane);
-            SplitOp fp1 = fp0;
-            pin(ub0, fp0, fp1);
-            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp0, ub0, O); });
-            Oprev = O * kInvSc;
+            f32x4_t O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            prod4x2(fq, sb, O);
+            SplitOp fp0 = ld_frag(hbuf[0], frag_p(0, r, 0), lane);
+            await_half(&xflag[0], 2 * cc + 1);
+            await_half(&xflag[1], 2 * cc + 1);
+            SplitOp ub0[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ub0[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
             orow0 = cc * PC;
 
             // ======== second half ========
-            if (pf)
-                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             lds_sync();                                            // H1
             store_o();
-            const bool more = cc + 1 < nch;
-            if (more) dma_o_half(cws(cc + 1), obuf[0], ow, lane);
-            pf = more;
-            if (pf) prefetch_half_lines(cws(cc + 1) + HALF_B, ut_grp(cc + 1, 1), pf_sink, ow, lane);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_ofrag(obuf[1], frag_q(r, kb), lane);
-            fp0 = ld_ofrag(obuf[1], frag_p(1, r, 0), lane);
-            fp1 = ld_ofrag(obuf[1], frag_p(1, r, 1), lane);
-            pin(fq);
-            O = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            prod1x4(fq, sb, O);
-            pin(ub0, fp0, fp1);
-            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp0, ub0, O); });
-            await_half(&xflag[slice][0], 2 * cc + 2);
-            await_half(&xflag[slice][1], 2 * cc + 2);
-            SplitOp ub1 = get_split(xs.ub_hi, xs.ub_lo, lane);
-            pin(ub1, fp1, fp0);
-            three_passes([&](auto P) { O = mma_pass<decltype(P)::value>(fp1, ub1, O); });
-            Oprev = O * kInvSc;
+            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[1], frag_q(r, kb), lane);
+            fp0 = ld_frag(hbuf[1], frag_p(1, r, 0), lane);
+            SplitOp fp1 = ld_frag(hbuf[1], frag_p(1, r, 1), lane);
+            O[0] = O[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            prod4x2(fq, sb, O);
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
+            });
+            await_half(&xflag[0], 2 * cc + 2);
+            await_half(&xflag[1], 2 * cc + 2);
+            SplitOp ub1[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ub1[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
+            three_passes([&](auto P) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp1, ub1[j], O[j]);
+            });
+            Oprev[0] = O[0] * kInvSc;
+            Oprev[1] = O[1] * kInvSc;
             orow0 = cc * PC + 32;
         }
         store_o();
@@ -1470,7 +1529,7 @@ __global__ __launch_bounds__(256 * NS) void prefill_state_kernel(PrefillArgs a) 
         for (int pp = pfirst; pp < pend; ++pp) {
             const int64_t row = v.lo + (pp - v.pos);
             const int64_t dst = (((int64_t)v.slot * kConvW + (pp & (kConvW - 1))) * H + h) * C;
-            for (int ch = tid; ch < C; ch += 256 * NS) {
+            for (int ch = tid; ch < C; ch += kStateThreads) {
                 const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
                 st_act_bits<ACT>(a.ring, dst + ch,
                                  ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
@@ -1534,8 +1593,6 @@ static bool is_prime(int64_t x) {
     return true;
 }
 
-// 16-column slices per state-pass workgroup (two waves each).
-constexpr int kStateSlices = 2;
 
 // One chunk workgroup per compute unit of the current device (the kernel's
 // LDS allows no more), looked up once per device.
@@ -1558,8 +1615,7 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const int64_t n_slots = (a.total_tokens + PC - 1) / PC + a.num_seqs;
     const int64_t nchunk = n_slots * a.H;
     const int64_t G = (int64_t)a.num_seqs * a.H;
-    constexpr int NS = kStateSlices;
-    const int64_t sgrid = (G + 7) / 8 * 8 * (8 / NS);
+    const int64_t sgrid = (G + 7) / 8 * 8 * 4;    // four 32-column workgroups each
     const int hgroups = (a.H + 7) / 8;
     if (nchunk > 0) {
         // Workgroup b takes items b, b + grid, ...  A prime grid keeps the
@@ -1571,8 +1627,8 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
                            stream, a, (int)n_slots);
     }
     if (sgrid > 0)
-        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST, NS>), dim3((unsigned)sgrid),
-                           dim3(256 * NS), 0, stream, a);
+        hipLaunchKernelGGL((prefill_state_kernel<ACT, ST>), dim3((unsigned)sgrid),
+                           dim3(kStateThreads), 0, stream, a);
     if (a.total_tokens > 0)
         hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.total_tokens, hgroups),
                            dim3(256), 0, stream, a);
