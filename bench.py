@@ -455,6 +455,11 @@ def main():
         print(f"# verify {case2.name}", file=sys.stderr, flush=True)
         modes["spec_verify_commit"] = run_verify_mode(torch, case2, args.steps,
                                                       args.warmup, 8)
+        for st, layers in (("f32", 32), ("bf16", 64)):
+            casec = wl.compact_heads(st)
+            print(f"# decode {casec.name}", file=sys.stderr, flush=True)
+            modes[f"compact_heads_decode_{st}_state"] = run_decode_mode(
+                torch, casec, args.steps, args.warmup, layers)
         case4 = wl.config(4)
         print(f"# prefill {case4.name}", file=sys.stderr, flush=True)
         modes["chunked_prefill"] = run_prefill_mode(torch, case4, args.steps, args.warmup)

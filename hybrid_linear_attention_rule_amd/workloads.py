@@ -231,3 +231,15 @@ def config(i: int) -> Case:
                             dv=128, act="bf16", state="f32", init="zero",
                             chunk=64, name=CONFIG_NAMES[4])
     raise ValueError(f"no config {i}")
+
+
+COMPACT_HEADS_NAME = "compact_heads_decode_B256_H2_d128_bf16act_{}state"
+
+
+def compact_heads(state: str = "f32") -> Case:
+    """Decode at a small per-GPU head count (two heads, as when the heads are
+    split over many GPUs) with a large batch: 256 rows, 16 steps, inputs and
+    start states drawn as in the batched-decode workload."""
+    return make_decode(5, B=256, H=2, dk=128, dv=128, steps=16, act="bf16", state=state,
+                       init="random", name=COMPACT_HEADS_NAME.format(state))
+

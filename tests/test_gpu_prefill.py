@@ -162,3 +162,36 @@ def test_prefill_bad_seqlens_and_inactive_sequences():
     ds = dev.make_state(case)
     ds, y, status = run_prefill_gpu(case, ds, max_seqlen=32)
     assert status & kda.STATUS_BAD_SEQLENS
+
+
+def test_mixed_launch_decode_rows_as_length_one_sequences():
+    """One kda_prefill launch that mixes decode rows (length-1 sequences
+    continuing a stored state and history) with multi-chunk sequences: every
+    row matches the oracle, and each decode row also matches kda_decode of
+    the same token from the same start."""
+    torch = need_gpu()
+    lens = [1, 200, 1, 1, 70, 1]
+    case = wl.make_prefill(86, lens=lens, H=4, dk=128, dv=128, act="bf16", state="f32",
+                           init="random", slice_len=32, name="prefill_mixed_decode_rows")
+    ds_p = check_prefill(case)
+    _, y_p, _ = run_prefill_gpu(case)          # fresh state, same launch again
+    singles = [i for i, n in enumerate(lens) if n == 1]
+    cu = case.cu_seqlens
+    ds_d = dev.make_state(case)
+    slots = np.where(np.asarray(lens) == 1, ds_d.slots, -1).astype(np.int32)
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    first = torch.from_numpy(cu[:-1].astype(np.int64)).cuda()
+    rows = {k: t.index_select(0, first).contiguous() for k, t in tok.items()}
+    y_d = torch.full((len(lens), case.H, case.dv), float("nan"), device="cuda")
+    kda.decode(ds_d.shape, ds_d.params, torch.from_numpy(slots).cuda(),
+               torch.from_numpy(case.pos0.astype(np.int32)).cuda(), rows["q"], rows["k"],
+               rows["v"], rows["alpha"], rows["beta"], rows["g"], ds_d.pool, ds_d.ring, y_d)
+    torch.cuda.synchronize()
+    y_d = y_d.cpu().numpy()
+    S_p = dev.read_states(ds_p)
+    S_d = dev.read_states(ds_d)
+    for i in singles:
+        assert_parity(y_d[i], y_p[int(cu[i])], 2e-5, f"decode row {i}: output")
+        assert_parity(S_d[i], S_p[i], 2e-5, f"decode row {i}: state")
+    np.testing.assert_array_equal(dev.read_window(ds_d, case.pos0 + 1)[singles],
+                                  dev.read_window(ds_p, case.pos0 + 1)[singles])
