@@ -13,6 +13,10 @@ Distributions, following the workloads the mixer is measured on:
   * initial state        N(0, 0.1) where a workload starts from a random state
   * conv history         N(0, 1)   where a workload starts mid-sequence
 
+A workload with gates="logits" hands the mixer the logits a and b
+themselves (rounded to the activation dtype) in place of alpha and beta;
+the mixer then forms alpha and beta.
+
 Draws are fp64 from numpy's PCG64 and are then rounded to the activation
 dtype: float32 (round to nearest even), or bfloat16 (round to float32, then
 to nearest even on the upper 16 bits).  Conv and norm weights stay float32.
@@ -80,8 +84,8 @@ class TokenInputs:
     q: np.ndarray      # [..., H, dk]
     k: np.ndarray      # [..., H, dk]
     v: np.ndarray      # [..., H, dv]
-    alpha: np.ndarray  # [..., H, dk]
-    beta: np.ndarray   # [..., H]
+    alpha: np.ndarray  # [..., H, dk]  (the logit a when gates == "logits")
+    beta: np.ndarray   # [..., H]      (the logit b when gates == "logits")
     g: np.ndarray      # [..., H, dv]
 
 
@@ -112,6 +116,7 @@ class Case:
     slice_seq: int = -1    # prefill: sequence and start of the checked slice
     slice_start: int = -1
     slice_len: int = 0
+    gates: str = "values"  # "logits": tokens.alpha / tokens.beta hold a and b
 
 
 def _weights(rng, H, dk, dv, W):
@@ -121,12 +126,19 @@ def _weights(rng, H, dk, dv, W):
     return Weights(cq, ck, cv, np.ones(dv, dtype=np.float32))
 
 
-def _tokens(rng, lead, H, dk, dv, act) -> TokenInputs:
+def _tokens(rng, lead, H, dk, dv, act, gates="values") -> TokenInputs:
     q = round_to(rng.standard_normal(lead + (H, dk)), act)
     k = round_to(rng.standard_normal(lead + (H, dk)), act)
     v = round_to(rng.standard_normal(lead + (H, dv)), act)
-    alpha = round_to(np.exp(-_softplus(rng.standard_normal(lead + (H, dk)))), act)
-    beta = round_to(_sigmoid(rng.standard_normal(lead + (H,))), act)
+    a = rng.standard_normal(lead + (H, dk))
+    b = rng.standard_normal(lead + (H,))
+    if gates == "logits":
+        alpha, beta = round_to(a, act), round_to(b, act)
+    elif gates == "values":
+        alpha = round_to(np.exp(-_softplus(a)), act)
+        beta = round_to(_sigmoid(b), act)
+    else:
+        raise ValueError(f"unknown gate inputs {gates!r}")
     g = round_to(rng.standard_normal(lead + (H, dv)), act)
     return TokenInputs(q, k, v, alpha, beta, g)
 
@@ -147,13 +159,14 @@ def _start(rng, B, H, dk, dv, W, act, state, init):
 
 
 def make_decode(seed, *, B, H, dk, dv, steps, act, state, init,
-                active_per_step=None, width=4, name="decode", norm_w=None):
+                active_per_step=None, width=4, name="decode", norm_w=None,
+                gates="values"):
     rng = np.random.Generator(np.random.PCG64(seed))
     w = _weights(rng, H, dk, dv, width)
     if norm_w is not None:
         w.norm_w = round_f32(norm_w)
     S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
-    toks = _tokens(rng, (steps, B), H, dk, dv, act)
+    toks = _tokens(rng, (steps, B), H, dk, dv, act, gates)
     active = np.ones((steps, B), dtype=bool)
     if active_per_step is not None:
         active[:] = False
@@ -161,29 +174,30 @@ def make_decode(seed, *, B, H, dk, dv, steps, act, state, init,
             active[s, rng.permutation(B)[:active_per_step]] = True
     return Case(name=name, mode="decode", H=H, dk=dk, dv=dv, width=width,
                 act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
-                pos0=pos0, steps=steps, tokens=toks, active=active)
+                pos0=pos0, steps=steps, tokens=toks, active=active, gates=gates)
 
 
 def make_verify(seed, *, B, H, dk, dv, n_draft, act, state, init, width=4,
-                name="verify"):
+                name="verify", gates="values"):
     rng = np.random.Generator(np.random.PCG64(seed))
     w = _weights(rng, H, dk, dv, width)
     S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
-    toks = _tokens(rng, (B, n_draft), H, dk, dv, act)
+    toks = _tokens(rng, (B, n_draft), H, dk, dv, act, gates)
     accepted = rng.integers(0, n_draft + 1, size=B).astype(np.int32)
     return Case(name=name, mode="verify", H=H, dk=dk, dv=dv, width=width,
                 act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
-                pos0=pos0, n_draft=n_draft, tokens=toks, accepted=accepted)
+                pos0=pos0, n_draft=n_draft, tokens=toks, accepted=accepted,
+                gates=gates)
 
 
 def make_prefill(seed, *, lens, H, dk, dv, act, state, init="zero", width=4,
-                 chunk=64, slice_len=512, name="prefill"):
+                 chunk=64, slice_len=512, name="prefill", gates="values"):
     rng = np.random.Generator(np.random.PCG64(seed))
     w = _weights(rng, H, dk, dv, width)
     B = len(lens)
     S0, hist0, pos0 = _start(rng, B, H, dk, dv, width, act, state, init)
     total = int(sum(lens))
-    toks = _tokens(rng, (total,), H, dk, dv, act)
+    toks = _tokens(rng, (total,), H, dk, dv, act, gates)
     cu = np.zeros(B + 1, dtype=np.int32)
     cu[1:] = np.cumsum(lens)
     # a slice of consecutive outputs to check at full size
@@ -197,7 +211,7 @@ def make_prefill(seed, *, lens, H, dk, dv, act, state, init="zero", width=4,
                 act=act, state=state, weights=w, batch=B, S0=S0, hist0=hist0,
                 pos0=pos0, tokens=toks, lens=list(lens), cu_seqlens=cu,
                 chunk=chunk, slice_seq=s, slice_start=start,
-                slice_len=slice_len)
+                slice_len=slice_len, gates=gates)
 
 
 # The five measured workloads.  The seed of each is its index.

@@ -50,6 +50,13 @@
  *   (old history || drafts 1..m) the new history; m = 0 changes nothing.
  *   Prefill is steps 1-7 over the whole sequence, stored once at the end.
  *
+ *   Gate inputs.  The decay and write strengths may arrive as logits instead
+ *   (cfg->gates = 1): the mixer fuses the f_b projection that produces them
+ *   (first page, Description), and the plain reading of the per-channel
+ *   decay is alpha = exp(-softplus(a)) in (0, 1), of the per-head write
+ *   strength beta = sigmoid(b) in (0, 1); both are formed before step 4 of
+ *   each token.
+ *
  *   kda_ref_run_chunked restates steps 4-6 in the chunkwise WY/UT form (the
  *   derivation is written out above that function).  It exists so that tests
  *   can check that the chunk algebra reaches the sequential result.
@@ -58,7 +65,8 @@
  *   S      [dk][dv], S[i*dv + j]: row i is key channel i, column j value ch.
  *   hist   [W-1][2dk+dv], oldest first; channels ordered q | k | v.
  *   wconv  [2dk+dv][W] for the head; the same q | k | v channel order.
- *   q, k, alpha [T][dk]; v, g [T][dv]; beta [T]; y [T][dv].
+ *   q, k, alpha [T][dk]; v, g [T][dv]; beta [T]; y [T][dv] (alpha and beta
+ *   hold the logits a and b when cfg->gates = 1).
  *   records [T][dk][dv] (nullable).
  *
  * Return value: 0 on success, -1 on a bad argument, -2 when out of memory.
@@ -75,6 +83,7 @@ typedef struct {
     double q_scale;  /* s in step 3 */
     double l2_eps;   /* eps_l2 in step 3 */
     double norm_eps; /* eps_n in step 7 */
+    int gates;       /* 0: alpha and beta given; 1: their logits a and b */
 } kda_ref_cfg;
 
 /* Nearest bfloat16 value of x, ties to even (IEEE-754 binary16 "brain"
@@ -107,7 +116,35 @@ static double gate_fn(int gate, double x)
 static int cfg_ok(const kda_ref_cfg *cfg)
 {
     return cfg && cfg->dk > 0 && cfg->dv > 0 && cfg->width >= 1 &&
-           (cfg->gate == 0 || cfg->gate == 1);
+           (cfg->gate == 0 || cfg->gate == 1) &&
+           (cfg->gates == 0 || cfg->gates == 1);
+}
+
+/* softplus(x) = log(1 + e^x), split at 0 so that e^x never overflows. */
+static double softplus(double x)
+{
+    return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));
+}
+
+/* The T tokens' alpha [T][dk] and beta [T] from the inputs: copies when they
+ * are given, else alpha = exp(-softplus(a)) and beta = 1 / (1 + e^-b) of the
+ * logits.  Returns 0, or -2 when out of memory (*al, *be then NULL). */
+static int gate_values(const kda_ref_cfg *cfg, int T, const double *alpha,
+                       const double *beta, double **al, double **be)
+{
+    long n = (long)T * cfg->dk, i;
+    *al = malloc(sizeof(double) * (n > 0 ? n : 1));
+    *be = malloc(sizeof(double) * (T > 0 ? T : 1));
+    if (!*al || !*be) {
+        free(*al); free(*be);
+        *al = *be = NULL;
+        return -2;
+    }
+    for (i = 0; i < n; ++i)
+        (*al)[i] = cfg->gates ? exp(-softplus(alpha[i])) : alpha[i];
+    for (i = 0; i < T; ++i)
+        (*be)[i] = cfg->gates ? 1.0 / (1.0 + exp(-beta[i])) : beta[i];
+    return 0;
 }
 
 /* Steps 1-3 for one token: the causal conv over (hist || x_t) and the
@@ -194,27 +231,29 @@ int kda_ref_run(const kda_ref_cfg *cfg, int T, double *S, double *hist,
                 int round_each_token, double *y, double *records)
 {
     int dk, dv, t, i, j;
-    double *qh, *kh, *vt, *u, *o;
+    double *qh, *kh, *vt, *u, *o, *al = NULL, *be = NULL;
 
     if (!cfg_ok(cfg) || T < 0 || !S || !hist || (T > 0 && (!q || !k || !v ||
         !alpha || !beta || !g || !wconv || !y)))
         return -1;
     dk = cfg->dk;
     dv = cfg->dv;
+    if (T > 0 && gate_values(cfg, T, alpha, beta, &al, &be) != 0)
+        return -2;
     qh = malloc(sizeof(double) * dk);
     kh = malloc(sizeof(double) * dk);
     vt = malloc(sizeof(double) * dv);
     u = malloc(sizeof(double) * dv);
     o = malloc(sizeof(double) * dv);
     if (!qh || !kh || !vt || !u || !o) {
-        free(qh); free(kh); free(vt); free(u); free(o);
+        free(qh); free(kh); free(vt); free(u); free(o); free(al); free(be);
         return -2;
     }
 
     for (t = 0; t < T; ++t) {
         const double *xq = q + (long)t * dk, *xk = k + (long)t * dk;
-        const double *xv = v + (long)t * dv, *a = alpha + (long)t * dk;
-        const double b = beta[t];
+        const double *xv = v + (long)t * dv, *a = al + (long)t * dk;
+        const double b = be[t];
 
         conv_and_normalise(cfg, hist, xq, xk, xv, wconv, qh, kh, vt);
 
@@ -253,7 +292,7 @@ int kda_ref_run(const kda_ref_cfg *cfg, int T, double *S, double *hist,
 
         push_history(cfg, hist, xq, xk, xv);
     }
-    free(qh); free(kh); free(vt); free(u); free(o);
+    free(qh); free(kh); free(vt); free(u); free(o); free(al); free(be);
     return 0;
 }
 
@@ -305,16 +344,17 @@ int kda_ref_commit(const kda_ref_cfg *cfg, int n, int m, int store_bf16,
  */
 int kda_ref_run_chunked(const kda_ref_cfg *cfg, int T, int C, double *S,
                         double *hist, const double *q, const double *k,
-                        const double *v, const double *alpha,
-                        const double *beta, const double *g,
+                        const double *v, const double *alpha_in,
+                        const double *beta_in, const double *g,
                         const double *wconv, const double *norm_w, double *y)
 {
     int dk, dv, c0, t, i, j, c, L;
     double *QH, *KH, *VT, *G, *A, *Tm, *Wm, *Ut, *Wr, *O, *S0;
+    double *alpha = NULL, *beta = NULL;
     int ok = 1;
 
     if (!cfg_ok(cfg) || T < 0 || C < 1 || !S || !hist || (T > 0 && (!q ||
-        !k || !v || !alpha || !beta || !g || !wconv || !y)))
+        !k || !v || !alpha_in || !beta_in || !g || !wconv || !y)))
         return -1;
     dk = cfg->dk;
     dv = cfg->dv;
@@ -330,6 +370,8 @@ int kda_ref_run_chunked(const kda_ref_cfg *cfg, int T, int C, double *S,
     O = malloc(sizeof(double) * C * dv);
     S0 = malloc(sizeof(double) * dk * dv);
     if (!QH || !KH || !VT || !G || !A || !Tm || !Wm || !Ut || !Wr || !O || !S0)
+        ok = 0;
+    if (ok && T > 0 && gate_values(cfg, T, alpha_in, beta_in, &alpha, &beta) != 0)
         ok = 0;
 
     for (c0 = 0; ok && c0 < T; c0 += C) {
@@ -418,6 +460,6 @@ int kda_ref_run_chunked(const kda_ref_cfg *cfg, int T, int C, double *S,
                        y + (long)(c0 + t) * dv);
     }
     free(QH); free(KH); free(VT); free(G); free(A); free(Tm); free(Wm);
-    free(Ut); free(Wr); free(O); free(S0);
+    free(Ut); free(Wr); free(O); free(S0); free(alpha); free(beta);
     return ok ? 0 : -2;
 }

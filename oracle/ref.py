@@ -32,7 +32,7 @@ class _Cfg(ctypes.Structure):
     _fields_ = [("dk", ctypes.c_int), ("dv", ctypes.c_int),
                 ("width", ctypes.c_int), ("gate", ctypes.c_int),
                 ("q_scale", ctypes.c_double), ("l2_eps", ctypes.c_double),
-                ("norm_eps", ctypes.c_double)]
+                ("norm_eps", ctypes.c_double), ("gates", ctypes.c_int)]
 
 
 @dataclass(frozen=True)
@@ -44,11 +44,13 @@ class OracleCfg:
     q_scale: float = 1.0
     l2_eps: float = 1e-6
     norm_eps: float = 1e-6
+    gates: str = "values"   # or "logits": alpha, beta arrays hold a and b
 
     def c(self) -> _Cfg:
         return _Cfg(self.dk, self.dv, self.width,
                     {"sigmoid": 0, "silu": 1}[self.gate],
-                    self.q_scale, self.l2_eps, self.norm_eps)
+                    self.q_scale, self.l2_eps, self.norm_eps,
+                    {"values": 0, "logits": 1}[self.gates])
 
 
 def load():
@@ -232,7 +234,7 @@ def commit(cfg: OracleCfg, S, hist, records, toks, accepted, store_bf16):
 # and slots are bookkeeping of the device pool and do not enter the math.
 
 def _cfg_of(case, gate="sigmoid"):
-    return OracleCfg(case.dk, case.dv, case.width, gate)
+    return OracleCfg(case.dk, case.dv, case.width, gate, gates=case.gates)
 
 
 def decode_case(case, *, threads=None, gate="sigmoid", steps=None):

@@ -36,6 +36,9 @@ MUTANTS = {
         "memcpy(S, records + (long)(m < n ? m : m - 1) * dk * dv"),
     "gate_sign": ("double sig = 1.0 / (1.0 + exp(-x));",
                   "double sig = 1.0 / (1.0 + exp(x));"),
+    "logit_decay_sign": ("exp(-softplus(alpha[i]))", "exp(-softplus(-alpha[i]))"),
+    "logit_write_sign": ("1.0 / (1.0 + exp(-beta[i]))", "1.0 / (1.0 + exp(beta[i]))"),
+    "softplus_positive_branch": ("x > 0.0 ? x + log1p(exp(-x))", "x > 0.0 ? log1p(exp(-x))"),
     "readout_before_write": (
         "        /* 6. read-out after the write */",
         "        for (i = 0; i < dk; ++i) for (j = 0; j < dv; ++j)"

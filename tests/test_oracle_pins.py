@@ -396,6 +396,58 @@ def test_chunked_form_strong_decay():
     np.testing.assert_allclose(yc, y, rtol=0, atol=1e-11 * np.abs(y).max())
 
 
+# ----------------------------------------------------------------- gate logits
+
+@pytest.mark.parametrize("chunk", [None, 16])
+def test_gate_logits_match_library_logistic(chunk):
+    """Logit inputs: alpha = exp(-softplus(a)) = logistic(-a) and beta =
+    logistic(b).  A run on logits equals a run on the values scipy's expit
+    (an independent library routine) gives for them, token by token and in
+    the chunk form.  Logits up to |6| reach both sides of softplus's split."""
+    from scipy.special import expit
+    rng = np.random.default_rng(91)
+    dk, dv, T = 8, 6, 40
+    q, k, v, _, _, g = _rand_stream(rng, T, dk, dv)
+    a = rng.normal(0.0, 2.0, (T, dk))
+    b = rng.normal(0.0, 2.0, T)
+    w = rng.normal(0, 0.5, (2 * dk + dv, 4))
+    S0 = rng.normal(0, 0.1, (dk, dv))
+    h0 = rng.standard_normal((3, 2 * dk + dv))
+    cfg_l, cfg_v = OracleCfg(dk, dv, gates="logits"), OracleCfg(dk, dv)
+    if chunk is None:
+        S_l, h_l, y_l, _ = _run(cfg_l, S0, h0, (q, k, v, a, b, g), w)
+        S_v, h_v, y_v, _ = _run(cfg_v, S0, h0, (q, k, v, expit(-a), expit(b), g), w)
+    else:
+        S_l, h_l, S_v, h_v = S0.copy(), h0.copy(), S0.copy(), h0.copy()
+        y_l = ref.run_one_chunked(cfg_l, chunk, S_l, h_l, q, k, v, a, b, g, w, None)
+        y_v = ref.run_one_chunked(cfg_v, chunk, S_v, h_v, q, k, v, expit(-a),
+                                  expit(b), g, w, None)
+    np.testing.assert_allclose(S_l, S_v, rtol=0, atol=1e-13 * np.abs(S_v).max())
+    np.testing.assert_allclose(y_l, y_v, rtol=0, atol=1e-12 * np.abs(y_v).max())
+    np.testing.assert_array_equal(h_l, h_v)
+
+
+def test_gate_logits_special_values():
+    """a = 0 halves the state (alpha = 1/2) and b = 0 writes at beta = 1/2;
+    a = -60 keeps the state (alpha = 1 in fp64) and b = -60 writes nothing
+    measurable (beta ~ 1e-26), so the state stays as it was."""
+    rng = np.random.default_rng(92)
+    dk, dv, T = 6, 5, 4
+    q, k, v, _, _, g = _rand_stream(rng, T, dk, dv)
+    w = rng.normal(0, 0.5, (2 * dk + dv, 4))
+    S0 = rng.normal(0, 0.1, (dk, dv))
+    h0 = np.zeros((3, 2 * dk + dv))
+    cfg_l, cfg_v = OracleCfg(dk, dv, gates="logits"), OracleCfg(dk, dv)
+    S_l, _, y_l, _ = _run(cfg_l, S0, h0, (q, k, v, np.zeros((T, dk)), np.zeros(T), g), w)
+    S_v, _, y_v, _ = _run(cfg_v, S0, h0, (q, k, v, np.full((T, dk), 0.5),
+                                          np.full(T, 0.5), g), w)
+    np.testing.assert_allclose(S_l, S_v, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(y_l, y_v, rtol=1e-13, atol=0)
+    S_k, _, _, _ = _run(cfg_l, S0, h0, (q, k, v, np.full((T, dk), -60.0),
+                                        np.full(T, -60.0), g), w)
+    np.testing.assert_allclose(S_k, S0, rtol=0, atol=1e-20)
+
+
 def test_prefill_case_equals_decode_of_same_tokens():
     case = wl.make_prefill(15, lens=[7, 1, 70], H=2, dk=8, dv=8, act="bf16",
                            state="f32", chunk=16, slice_len=4)
