@@ -24,6 +24,8 @@ int check_shape(const kda_shape* s) {
     if (!s) return KDA_ERR_NULL;
     if (!dtype_ok(s->act_dtype) || !dtype_ok(s->state_dtype)) return KDA_ERR_DTYPE;
     if (s->gate != KDA_GATE_SIGMOID && s->gate != KDA_GATE_SILU) return KDA_ERR_DTYPE;
+    if (s->gate_inputs != KDA_GATES_VALUES && s->gate_inputs != KDA_GATES_LOGITS)
+        return KDA_ERR_DTYPE;
     if (s->num_heads < 1 || s->head_k < 1 || s->head_v < 1) return KDA_ERR_SHAPE;
     if (s->conv_width != kConvW) return KDA_ERR_UNSUPPORTED;
     if (!(s->l2_eps >= 0.0f) || !(s->norm_eps >= 0.0f)) return KDA_ERR_SHAPE;
@@ -192,6 +194,7 @@ static kda::TokenArgs token_args(const kda_shape* s, const kda_params* p,
     a.l2_eps = s->l2_eps;
     a.norm_eps = s->norm_eps;
     a.gate = s->gate;
+    a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
     return a;
 }
 
@@ -317,6 +320,7 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
     a.l2_eps = s->l2_eps;
     a.norm_eps = s->norm_eps;
     a.gate = s->gate;
+    a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
     return kda::launch_prefill(*s, a, stream);
 }
 

@@ -69,6 +69,11 @@ __device__ __forceinline__ uint32_t ld_act_bits(const void* src, int64_t si) {
     }
 }
 
+// Decay and write strengths from their logits: alpha = exp(-softplus(a)),
+// which equals 1 / (1 + e^a), and beta = sigmoid(b) = 1 / (1 + e^-b).
+__device__ __forceinline__ float decay_from_logit(float a) { return 1.0f / (1.0f + expf(a)); }
+__device__ __forceinline__ float write_from_logit(float b) { return 1.0f / (1.0f + expf(-b)); }
+
 __device__ __forceinline__ float gate_fn(int gate, float x) {
     const float sig = 1.0f / (1.0f + expf(-x));
     return gate == kGateSilu ? x * sig : sig;

@@ -38,6 +38,7 @@ struct TokenArgs {
     float l2_eps;
     float norm_eps;
     int32_t gate;
+    int32_t gate_logits;  // alpha, beta hold logits a, b
 };
 
 struct CommitArgs {
@@ -95,6 +96,7 @@ struct PrefillArgs {
     float l2_eps;
     float norm_eps;
     int32_t gate;
+    int32_t gate_logits;  // alpha, beta hold logits a, b
 };
 
 // Each returns KDA_OK, KDA_ERR_UNSUPPORTED (no instantiation) or KDA_ERR_HIP.

@@ -506,9 +506,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         for (int e = 0; e < 4; ++e) {
             const bool live = tb + e < L;
             unpack8<ACT>(in.ra[e], true, al[e]);
+            float bv = ACT == kF32 ? __uint_as_float(in.rb[e]) : bf16_to_f32(in.rb[e]);
+            if (a.gate_logits) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) al[e][q] = decay_from_logit(al[e][q]);
+                bv = write_from_logit(bv);
+            }
 #pragma unroll
             for (int q = 0; q < 8; ++q) al[e][q] = live ? al[e][q] : 1.f;
-            const float bv = ACT == kF32 ? __uint_as_float(in.rb[e]) : bf16_to_f32(in.rb[e]);
             bt[e] = live ? bv : 0.f;
         }
         conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, cv);

@@ -191,6 +191,10 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
                                        (size_t)(tok * H + h) * DV * ESZ, tid < DV ? tid : 0);
     beta = ld_act<ACT>(a.beta, tok * H + h);
     al = qk ? al_ld : 0.f;
+    if (a.gate_logits) {
+        beta = write_from_logit(beta);
+        al = qk ? decay_from_logit(al_ld) : 0.f;
+    }
     gv = (tid < DV) ? g_ld : 0.f;
 
     ca = 0.f;

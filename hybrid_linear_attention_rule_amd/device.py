@@ -28,7 +28,9 @@ def _act(x: np.ndarray, act: str, device) -> torch.Tensor:
 def shape_of(case: Case, gate: str = "sigmoid", q_scale=1.0) -> kda.KdaShape:
     return kda.KdaShape(case.H, case.dk, case.dv, act=case.act, state=case.state,
                         gate={"sigmoid": kda.GATE_SIGMOID, "silu": kda.GATE_SILU}[gate],
-                        q_scale=q_scale)
+                        q_scale=q_scale,
+                        gate_inputs={"values": kda.GATES_VALUES,
+                                     "logits": kda.GATES_LOGITS}[case.gates])
 
 
 def params_of(case: Case, device="cuda") -> kda.KdaParams:

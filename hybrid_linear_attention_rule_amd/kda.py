@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 
 F32, BF16 = 0, 1
 GATE_SIGMOID, GATE_SILU = 0, 1
+GATES_VALUES, GATES_LOGITS = 0, 1
 STATUS_BAD_SLOT = 1
 STATUS_BAD_POSITION = 2
 STATUS_BAD_ACCEPTED = 4
@@ -39,7 +40,8 @@ class _Shape(ctypes.Structure):
                 ("head_v", ctypes.c_int32), ("conv_width", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("q_scale", ctypes.c_float),
-                ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float)]
+                ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float),
+                ("gate_inputs", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
@@ -158,11 +160,12 @@ class KdaShape:
     l2_eps: float = 1e-6
     norm_eps: float = 1e-6
     conv_width: int = 4
+    gate_inputs: int = GATES_VALUES
 
     def c(self) -> _Shape:
         return _Shape(self.num_heads, self.head_k, self.head_v, self.conv_width,
                       _DT[self.act], _DT[self.state], self.gate, self.q_scale,
-                      self.l2_eps, self.norm_eps)
+                      self.l2_eps, self.norm_eps, self.gate_inputs)
 
     @property
     def channels(self) -> int:

@@ -9,6 +9,9 @@
  *      activation) over the raw q, k and v channels;
  *   2. L2-normalises q and k: x / sqrt(|x|^2 + l2_eps) (q also times q_scale);
  *   3. decays the rows of S by alpha (one factor per key channel);
+ *      alpha and beta arrive as values, or as logits a and b
+ *      (kda_shape.gate_inputs), from which alpha = exp(-softplus(a)) and
+ *      beta = sigmoid(b) are formed in the kernels;
  *   4. applies the gated delta-rule correction and write,
  *      S <- (I - beta k k^T) Diag(alpha) S + beta k v^T;
  *   5. reads out o = S^T q after the write;
@@ -92,6 +95,13 @@ enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 typedef enum { KDA_GATE_SIGMOID = 0, KDA_GATE_SILU = 1 } kda_gate;
+/* What the alpha and beta buffers hold.  LOGITS: the decay logit a per key
+ * channel and the write logit b per head, as the f_b projection the mixer
+ * fuses produces them ("Extend NVIDIA/TensorRT-LLM#19991 ...", Description);
+ * the kernels form alpha = exp(-softplus(a)) = 1 / (1 + e^a) and
+ * beta = sigmoid(b) = 1 / (1 + e^-b) in FP32.  The stored tensors keep the
+ * act dtype either way. */
+typedef enum { KDA_GATES_VALUES = 0, KDA_GATES_LOGITS = 1 } kda_gate_inputs;
 
 /* Host struct, passed by pointer.  Supported: head_k == head_v in {64, 128},
  * conv_width == 4. */
@@ -106,6 +116,7 @@ typedef struct {
     float q_scale;       /* multiplies the normalised q (1 in the usual form) */
     float l2_eps;        /* epsilon of the q/k L2 norms */
     float norm_eps;      /* epsilon of the gated RMSNorm */
+    int32_t gate_inputs; /* kda_gate_inputs of the alpha and beta buffers */
 } kda_shape;
 
 /* Host struct of device pointers to the layer's parameters. */

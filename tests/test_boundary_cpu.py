@@ -91,6 +91,11 @@ def test_decode_host_errors(lib):
     c.gate = 5
     assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
                           *([BOGUS] * 11), None, None) == E_DTYPE
+    for bad_inputs in (2, -1):          # neither values nor logits
+        c = shape().c()
+        c.gate_inputs = bad_inputs
+        assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                              *([BOGUS] * 11), None, None) == E_DTYPE
     assert _decode(lib, shape(head_k=96, head_v=96), _params()) == E_UNSUP
     assert _decode(lib, shape(head_k=64, head_v=128), _params()) == E_UNSUP
     assert _decode(lib, shape(conv_width=3), _params()) == E_UNSUP
