@@ -320,6 +320,64 @@ def run_verify_mode(torch, case, K, W, layers):
         parity_rel_err={"y": e_y, "records": e_r})
 
 
+def run_verify_recompute_mode(torch, case, K, W, layers):
+    """The records-free alternative on the same workload: verify writes only
+    y, and the commit runs the accepted tokens again from the stored state."""
+    from hybrid_linear_attention_rule_amd import device as dev
+    from hybrid_linear_attention_rule_amd import kda
+    import oracle
+
+    pools = [dev.make_state(case, spare_slots=0, fill_nan=False) for _ in range(layers)]
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    B, n, H, dk, dv = case.batch, case.n_draft, case.H, case.dk, case.dv
+    C = 2 * dk + dv
+    y = torch.empty((B, n, H, dv), device="cuda")
+    slot_t = pools[0].slot_ids
+    pos_t = torch.from_numpy(case.pos0.astype(np.int32)).cuda()
+    acc_t = torch.from_numpy(case.accepted.astype(np.int32)).cuda()
+
+    def verify(i):
+        d = pools[i % layers]
+        kda.verify(d.shape, d.params, slot_t, pos_t, tok["q"], tok["k"], tok["v"],
+                   tok["alpha"], tok["beta"], tok["g"], d.pool, d.ring, None, None, y)
+
+    def commit(i):
+        d = pools[i % layers]
+        kda.commit_recompute(d.shape, d.params, slot_t, pos_t, acc_t, tok["q"], tok["k"],
+                             tok["v"], tok["alpha"], tok["beta"], tok["g"], d.pool, d.ring)
+
+    verify(0)
+    commit(0)
+    torch.cuda.synchronize()
+    y_ref, _, S_ref, _ = oracle.verify_case(case)
+    tol = 2e-5 if case.state == "f32" else 1e-2
+    e_y = rel_err(y.cpu().numpy(), y_ref)
+    e_s = rel_err(dev.read_states(pools[0]), S_ref)
+    assert e_y <= 2e-5 and e_s <= tol, f"verify/recompute parity failed: {e_y} {e_s}"
+    pools[0] = dev.make_state(case, spare_slots=0, fill_nan=False)
+
+    _, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
+    _, c_launch, _, c_spread = timed_loop(torch, commit, K, W, layers * 2)
+    act_b = 2 if case.act == "bf16" else 4
+    st_b = 2 if case.state == "bf16" else 4
+    per_tok_in = (C + dk + 1 + dv) * act_b
+    v_bytes = B * H * (dk * dv * st_b + n * per_tok_in + 3 * C * act_b + n * dv * 4) + \
+        per_call_bytes(H, dk, dv, B)
+    m = case.accepted
+    c_bytes = int((m > 0).sum()) * H * (2 * dk * dv * st_b + 3 * C * act_b) + \
+        int(m.sum()) * H * per_tok_in + int(np.minimum(m, 4).sum()) * H * C * act_b + \
+        per_call_bytes(H, dk, dv, B)
+    return dict(
+        workload=case.name, rows=B, heads=H, n_draft=n, state=case.state,
+        verify_kernel_us=v_launch * 1e6, th_per_s=B * H * n / v_launch,
+        verify_bytes=v_bytes, verify_hbm_gbs=v_bytes / v_launch / 1e9,
+        commit_kernel_us=c_launch * 1e6, commit_bytes=c_bytes,
+        commit_hbm_gbs=c_bytes / c_launch / 1e9,
+        verify_plus_commit_us=(v_launch + c_launch) * 1e6,
+        verify_spread=v_spread, commit_spread=c_spread,
+        parity_rel_err={"y": e_y, "committed_state": e_s})
+
+
 # ------------------------------------------------------------ prefill
 
 def run_prefill_mode(torch, case, K, W):
@@ -455,6 +513,12 @@ def main():
         print(f"# verify {case2.name}", file=sys.stderr, flush=True)
         modes["spec_verify_commit"] = run_verify_mode(torch, case2, args.steps,
                                                       args.warmup, 8)
+        modes["spec_verify_commit"]["verify_plus_commit_us"] = (
+            modes["spec_verify_commit"]["verify_kernel_us"] +
+            modes["spec_verify_commit"]["commit_kernel_us"])
+        print(f"# verify without records, commit by recompute", file=sys.stderr, flush=True)
+        modes["spec_verify_recompute"] = run_verify_recompute_mode(
+            torch, case2, args.steps, args.warmup, 8)
         for st, layers in (("f32", 32), ("bf16", 64)):
             casec = wl.compact_heads(st)
             print(f"# decode {casec.name}", file=sys.stderr, flush=True)

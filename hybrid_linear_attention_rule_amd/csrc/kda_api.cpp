@@ -216,7 +216,7 @@ int kda_decode(const kda_shape* s, const kda_params* p, int32_t batch,
                                   beta, g, y, status, 1);
     a.pool = pool;
     a.ring = ring;
-    return kda::launch_token(*s, a, batch, false, stream);
+    return kda::launch_token(*s, a, batch, kda::TokenMode::Decode, stream);
 }
 
 int kda_verify(const kda_shape* s, const kda_params* p, int32_t batch,
@@ -233,7 +233,7 @@ int kda_verify(const kda_shape* s, const kda_params* p, int32_t batch,
     if (batch == 0) return KDA_OK;
     if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
     if (!slot_ids || !positions || !q || !k || !v || !alpha || !beta || !g || !pool ||
-        !ring || !draft_states || !draft_conv || !y)
+        !ring || !y)
         return KDA_ERR_NULL;
     kda::TokenArgs a = token_args(s, p, num_slots, slot_ids, positions, q, k, v, alpha,
                                   beta, g, y, status, n_draft);
@@ -241,7 +241,31 @@ int kda_verify(const kda_shape* s, const kda_params* p, int32_t batch,
     a.ring = const_cast<void*>(ring);
     a.records = draft_states;
     a.draft_conv = draft_conv;
-    return kda::launch_token(*s, a, batch, true, stream);
+    return kda::launch_token(*s, a, batch, kda::TokenMode::Verify, stream);
+}
+
+int kda_commit_recompute(const kda_shape* s, const kda_params* p, int32_t batch,
+                         int32_t n_draft, int64_t num_slots, const int32_t* slot_ids,
+                         const int32_t* positions, const int32_t* accepted, const void* q,
+                         const void* k, const void* v, const void* alpha, const void* beta,
+                         const void* g, void* pool, void* ring, int32_t* status,
+                         hipStream_t stream) {
+    int rc = check_shape(s);
+    if (rc != KDA_OK) return rc;
+    if ((rc = check_params(p)) != KDA_OK) return rc;
+    if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
+        return KDA_ERR_SHAPE;
+    if (batch == 0) return KDA_OK;
+    if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!slot_ids || !positions || !accepted || !q || !k || !v || !alpha || !beta || !g ||
+        !pool || !ring)
+        return KDA_ERR_NULL;
+    kda::TokenArgs a = token_args(s, p, num_slots, slot_ids, positions, q, k, v, alpha,
+                                  beta, g, nullptr, status, n_draft);
+    a.pool = pool;
+    a.ring = ring;
+    a.accepted = accepted;
+    return kda::launch_token(*s, a, batch, kda::TokenMode::Recompute, stream);
 }
 
 int kda_commit_accepted(const kda_shape* s, int32_t batch, int32_t n_draft,

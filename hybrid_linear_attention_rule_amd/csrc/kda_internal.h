@@ -10,8 +10,10 @@
 
 namespace kda {
 
-// Decode (n == 1, stores state and ring) and verify (n draft tokens,
-// writes records and raw drafts) share one per-token kernel.
+// Decode (n == 1, stores state and ring), verify (n draft tokens, writes
+// records and raw drafts when given) and recompute (the first accepted[row]
+// of n draft tokens from the stored state; stores state and ring) share one
+// per-token kernel.
 struct TokenArgs {
     const int32_t* slot_ids;
     const int32_t* positions;
@@ -27,13 +29,14 @@ struct TokenArgs {
     const float* norm_w;
     void* pool;          // decode: read + written; verify: read only
     void* ring;          // decode: read + written; verify: read only
-    float* records;      // verify only
-    void* draft_conv;    // verify only
+    float* records;      // verify only; NULL: no records
+    void* draft_conv;    // verify only; NULL: raw drafts not kept
+    const int32_t* accepted;  // recompute only: tokens to run per row
     float* y;
     int32_t* status;
     int64_t num_slots;
     int32_t H;
-    int32_t n;           // tokens per row (1 for decode)
+    int32_t n;           // input rows per batch row (1 for decode)
     float q_scale;
     float l2_eps;
     float norm_eps;
@@ -99,9 +102,11 @@ struct PrefillArgs {
     int32_t gate_logits;  // alpha, beta hold logits a, b
 };
 
+enum class TokenMode { Decode, Verify, Recompute };
+
 // Each returns KDA_OK, KDA_ERR_UNSUPPORTED (no instantiation) or KDA_ERR_HIP.
-int launch_token(const kda_shape& s, const TokenArgs& a, int32_t batch,
-                 bool verify, hipStream_t stream);
+int launch_token(const kda_shape& s, const TokenArgs& a, int32_t batch, TokenMode mode,
+                 hipStream_t stream);
 int launch_commit(const kda_shape& s, const CommitArgs& a, int32_t batch,
                   hipStream_t stream);
 int launch_state_io(const kda_shape& s, const StateIoArgs& a,

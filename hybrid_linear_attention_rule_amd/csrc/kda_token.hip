@@ -37,6 +37,15 @@
 
 namespace kda {
 
+// What one launch does per row.
+//   kModeDecode:    one token; state and ring stored.
+//   kModeVerify:    n draft tokens, state in registers; optional FP32 record
+//                   per token and raw drafts; pool and ring read only.
+//   kModeRecompute: the first m = accepted[row] of n draft tokens again from
+//                   the stored state (commit without records); state stored
+//                   once, ring entries of the m tokens written, no output.
+constexpr int kModeDecode = 0, kModeVerify = 1, kModeRecompute = 2;
+
 template <int DK, int DV, int VEC>
 struct TileMap {
     static constexpr int NT = DK * DV / 32;    // threads per workgroup: 32 state
@@ -160,9 +169,9 @@ __device__ __forceinline__ float act_from_bits(uint32_t bits) {
 // issued before any loaded value is used, so no wait for one tap stalls the
 // others or the state stream; taps before position 0 are zeroed afterwards.
 // The raw token is copied to the ring (decode: entry pos mod 4) or to
-// draft_conv (verify).  Also loads alpha, beta and g, writes the conv of v to
+// draft_conv (verify; skipped when draft_conv is NULL).  Also loads alpha, beta and g, writes the conv of v to
 // LDS and the per-wave partial sums of |c_q|^2, |c_k|^2 and c_q . c_k.
-template <int DK, int DV, int ACT, bool VERIFY, class Issue>
+template <int DK, int DV, int ACT, int MODE, class Issue>
 __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
                                         int slot, int pos, float4 w4a, float4 w4b,
                                         float* vt_s, float (*red_s)[4], float& ca,
@@ -244,13 +253,16 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
             cb = fmaf(w4b.z, xb[2], cb);
             cb = fmaf(w4b.w, xb[3], cb);
         }
-        // keep the raw token: decode -> ring entry pos mod 4, verify -> draft_conv
-        char* dst = VERIFY
-            ? static_cast<char*>(a.draft_conv) + (size_t)(tok * H + h) * C * ESZ
-            : static_cast<char*>(a.ring) +
-                  ((size_t)(ring_slot + (pos & (kConvW - 1))) * H + h) * C * ESZ;
-        st_act_bits<ACT>(dst + (qk ? 0 : 2 * DK) * ESZ, lc, bA[kConvW - 1]);
-        if (qk) st_act_bits<ACT>(dst + DK * ESZ, lc, bB[kConvW - 1]);
+        // keep the raw token: decode and recompute -> ring entry (pos + t)
+        // mod 4, verify -> draft_conv (when kept)
+        if (MODE != kModeVerify || a.draft_conv) {
+            char* dst = MODE == kModeVerify
+                ? static_cast<char*>(a.draft_conv) + (size_t)(tok * H + h) * C * ESZ
+                : static_cast<char*>(a.ring) +
+                      ((size_t)(ring_slot + ((pos + t) & (kConvW - 1))) * H + h) * C * ESZ;
+            st_act_bits<ACT>(dst + (qk ? 0 : 2 * DK) * ESZ, lc, bA[kConvW - 1]);
+            if (qk) st_act_bits<ACT>(dst + DK * ESZ, lc, bB[kConvW - 1]);
+        }
     }
     if (isv) vt_s[lc] = ca;
     const float cq = qk ? ca : 0.f, ck = cb;
@@ -263,7 +275,7 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
     }
 }
 
-template <int DK, int DV, int ACT, int ST, bool VERIFY>
+template <int DK, int DV, int ACT, int ST, int MODE>
 __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     constexpr int VEC = (ST == kF32) ? 4 : 8;
     using M = TileMap<DK, DV, VEC>;
@@ -285,7 +297,10 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     const int wave = tid / kWave;
     const int c = tid % LJ;                      // dv chunk: j = c*VEC + e
     const int r = tid / LJ;                      // row group: i = r*RPT + p
-    const int n = VERIFY ? a.n : 1;             // decode: exactly one token
+    constexpr bool VERIFY = MODE == kModeVerify;
+    constexpr bool RECOMP = MODE == kModeRecompute;
+    const int stride = MODE == kModeDecode ? 1 : a.n;   // input rows per batch row
+    int n = VERIFY ? a.n : 1;                   // tokens to run (decode: one)
     const bool qk_lane = tid < DK;
     const bool v_lane = tid >= DK && tid < DK + DV;
 
@@ -310,6 +325,15 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
             atomicOr(a.status, slot >= a.num_slots ? KDA_STATUS_BAD_SLOT : KDA_STATUS_BAD_POSITION);
         return;
     }
+    if constexpr (RECOMP) {
+        const int m = a.accepted[b];
+        if (m < 0 || m > a.n) {
+            if (tid == 0 && a.status) atomicOr(a.status, KDA_STATUS_BAD_ACCEPTED);
+            return;
+        }
+        if (m == 0) return;
+        n = m;
+    }
 
     // ---- state in: issued as soon as the slot is known (a fresh sequence,
     // position 0, discards what it loaded), consumed after the conv --------
@@ -321,15 +345,15 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     // phase B overlap the state loads, and the unpack waits for them
     uint4 raw[RPT];
     float ca, cb, al, beta, gv;
-    phase_a<DK, DV, ACT, VERIFY>(a, b, h, 0, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
+    phase_a<DK, DV, ACT, MODE>(a, b, h, 0, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
                                  beta, gv,
                                  [&] { load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw); });
     // A decode call with BF16 storage keeps the state packed as loaded and
     // widens one row at a time where it is used: the FP32 values are exact
     // and the update rounds once on the way out, as with a widened copy,
-    // but 16 fewer registers stay live.  Verify and FP32 storage hold the
-    // FP32 state.
-    constexpr bool PACKED = !VERIFY && ST == kBF16;
+    // but 16 fewer registers stay live.  Verify, recompute (several tokens,
+    // rounded once at the end) and FP32 storage hold the FP32 state.
+    constexpr bool PACKED = MODE == kModeDecode && ST == kBF16;
     float s[PACKED ? 1 : RPT][VEC];
     if constexpr (PACKED) {
         if (pos == 0) {
@@ -361,10 +385,10 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
 
 #pragma unroll 1
     for (int t = 0; t < n; ++t) {
-        const int64_t tok = (int64_t)b * n + t;     // row of the inputs
+        const int64_t tok = (int64_t)b * stride + t;   // row of the inputs
         // ---------------- A. conv, raw copy, norm partial sums -----------
         if (t > 0)
-            phase_a<DK, DV, ACT, VERIFY>(a, b, h, t, n, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
+            phase_a<DK, DV, ACT, MODE>(a, b, h, t, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
                                          al, beta, gv, [] {});
         __syncthreads();
 
@@ -470,9 +494,10 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
             }
         }
         if constexpr (VERIFY) {
-            store_record<DV, RPT, VEC>(a.records + ((size_t)tok * H + h) * head_elems, r, c, s);
+            if (a.records)
+                store_record<DV, RPT, VEC>(a.records + ((size_t)tok * H + h) * head_elems, r, c, s);
         }
-        if (tid < DV) {
+        if (!RECOMP && tid < DV) {
             float ms = 0.f;
 #pragma unroll
             for (int w = 0; w < DV / kWave; ++w) ms += red_s[w][3];
@@ -547,34 +572,38 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
 }
 
 template <int DK, int DV, int ACT, int ST>
-static int launch_token_t(const TokenArgs& a, int32_t batch, bool verify,
-                          hipStream_t stream) {
+static int launch_token_t(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
     const dim3 grid((unsigned)batch * (unsigned)a.H), block(DK * DV / 32);
-    if (verify)
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, true>), grid, block, 0, stream, a);
+    if (mode == kModeVerify)
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeVerify>), grid, block, 0, stream, a);
+    else if (mode == kModeRecompute)
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeRecompute>), grid, block, 0,
+                           stream, a);
     else
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeDecode>), grid, block, 0, stream, a);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 template <int DK, int DV>
-static int dispatch_token(const kda_shape& s, const TokenArgs& a, int32_t batch,
-                          bool verify, hipStream_t stream) {
+static int dispatch_token(const kda_shape& s, const TokenArgs& a, int32_t batch, int mode,
+                          hipStream_t stream) {
     if (s.act_dtype == kF32 && s.state_dtype == kF32)
-        return launch_token_t<DK, DV, kF32, kF32>(a, batch, verify, stream);
+        return launch_token_t<DK, DV, kF32, kF32>(a, batch, mode, stream);
     if (s.act_dtype == kF32 && s.state_dtype == kBF16)
-        return launch_token_t<DK, DV, kF32, kBF16>(a, batch, verify, stream);
+        return launch_token_t<DK, DV, kF32, kBF16>(a, batch, mode, stream);
     if (s.act_dtype == kBF16 && s.state_dtype == kF32)
-        return launch_token_t<DK, DV, kBF16, kF32>(a, batch, verify, stream);
-    return launch_token_t<DK, DV, kBF16, kBF16>(a, batch, verify, stream);
+        return launch_token_t<DK, DV, kBF16, kF32>(a, batch, mode, stream);
+    return launch_token_t<DK, DV, kBF16, kBF16>(a, batch, mode, stream);
 }
 
-int launch_token(const kda_shape& s, const TokenArgs& a, int32_t batch,
-                 bool verify, hipStream_t stream) {
+int launch_token(const kda_shape& s, const TokenArgs& a, int32_t batch, TokenMode mode,
+                 hipStream_t stream) {
+    const int m = mode == TokenMode::Verify ? kModeVerify
+                : mode == TokenMode::Recompute ? kModeRecompute : kModeDecode;
     if (s.head_k == 128 && s.head_v == 128)
-        return dispatch_token<128, 128>(s, a, batch, verify, stream);
+        return dispatch_token<128, 128>(s, a, batch, m, stream);
     if (s.head_k == 64 && s.head_v == 64)
-        return dispatch_token<64, 64>(s, a, batch, verify, stream);
+        return dispatch_token<64, 64>(s, a, batch, m, stream);
     return KDA_ERR_UNSUPPORTED;
 }
 

@@ -71,6 +71,8 @@ SIGNATURES = {
                    [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_commit_accepted": (ctypes.c_int, [_SP, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp]),
+    "kda_commit_recompute": (ctypes.c_int, [_SP, _PP, _i32, _i32, _i64, _vp, _vp, _vp] +
+                             [_vp] * 6 + [_vp, _vp, _vp, _vp]),
     "kda_prefill": (ctypes.c_int, [_SP, _PP, _i32, _vp, _i64, _i32, _i64, _vp, _vp] +
                     [_vp] * 6 + [_vp, _vp, _vp, _vp, _sz, _vp, _vp]),
 }
@@ -301,8 +303,11 @@ def verify(shape, params, slot_ids, positions, q, k, v, alpha, beta, g, pool, ri
     _expect(positions, B, torch.int32, "positions")
     _check_tokens(shape, B * n, q, k, v, alpha, beta, g)
     _check_pool_ring(shape, pool, ring)
-    _expect(draft_states, B * n * H * dv * dk, torch.float32, "draft_states")
-    _expect(draft_conv, B * n * H * shape.channels, shape.act_dtype, "draft_conv")
+    # draft_states / draft_conv may be None: no records / raw drafts kept
+    if draft_states is not None:
+        _expect(draft_states, B * n * H * dv * dk, torch.float32, "draft_states")
+    if draft_conv is not None:
+        _expect(draft_conv, B * n * H * shape.channels, shape.act_dtype, "draft_conv")
     _expect(y, B * n * H * dv, torch.float32, "y")
     _check(load().kda_verify(ctypes.byref(shape.c()), ctypes.byref(params.c()),
                              slot_ids.numel(), n, pool.shape[0], _ptr(slot_ids),
@@ -328,6 +333,26 @@ def commit_accepted(shape, slot_ids, positions, accepted, draft_states, draft_co
                                       _ptr(accepted), _ptr(draft_states),
                                       _ptr(draft_conv), _ptr(pool), _ptr(ring),
                                       _ptr(status), _stream(stream)))
+
+
+def commit_recompute(shape, params, slot_ids, positions, accepted, q, k, v, alpha, beta, g,
+                     pool, ring, status=None, stream=None):
+    """Commit accepted[b] of the verify's n draft tokens by running them
+    again from the stored state (q, k, v, alpha, beta, g: the verify's inputs,
+    [B, n, H, .])."""
+    B = slot_ids.numel()
+    n = q.shape[1]
+    _check_params(shape, params)
+    _expect(slot_ids, B, torch.int32, "slot_ids")
+    _expect(positions, B, torch.int32, "positions")
+    _expect(accepted, B, torch.int32, "accepted")
+    _check_tokens(shape, B * n, q, k, v, alpha, beta, g)
+    _check_pool_ring(shape, pool, ring)
+    _check(load().kda_commit_recompute(ctypes.byref(shape.c()), ctypes.byref(params.c()),
+                                       B, n, pool.shape[0], _ptr(slot_ids), _ptr(positions),
+                                       _ptr(accepted), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(alpha), _ptr(beta), _ptr(g), _ptr(pool),
+                                       _ptr(ring), _ptr(status), _stream(stream)))
 
 
 def prefill(shape, params, cu_seqlens, max_seqlen, slot_ids, positions, q, k, v,

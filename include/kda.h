@@ -206,9 +206,11 @@ int kda_decode(const kda_shape *shape, const kda_params *params,
  *   q, k, alpha [batch, n_draft, H, dk]; v, g [batch, n_draft, H, dv];
  *   beta [batch, n_draft, H]: act.  1 <= n_draft <= 16.
  *   draft_states [batch, n_draft, H, dk, dv] FP32: the state after each
- *            draft token (never rounded, whatever the storage dtype).
+ *            draft token (never rounded, whatever the storage dtype).  May
+ *            be NULL: no records are written, and the accepted prefix is
+ *            then committed with kda_commit_recompute.
  *   draft_conv [batch, n_draft, H, C] act: the raw draft tokens, kept for
- *            the commit.
+ *            kda_commit_accepted.  May be NULL (not kept).
  *   y [batch, n_draft, H, dv] FP32.
  * Inactive rows (negative slot) write nothing. */
 int kda_verify(const kda_shape *shape, const kda_params *params,
@@ -235,6 +237,32 @@ int kda_commit_accepted(const kda_shape *shape, int32_t batch,
                         const int32_t *accepted, const float *draft_states,
                         const void *draft_conv, void *pool, void *ring,
                         int32_t *status, hipStream_t stream);
+
+/* ----- commit the accepted prefix by recomputing it --------------------- */
+/* The alternative to per-token records: verify writes none (draft_states
+ * NULL), and the commit runs the accepted tokens again from the stored state
+ * and history.  Same result as kda_commit_accepted up to FP32 rounding order
+ * (the same per-token arithmetic, FP32 across the m tokens, rounded once on
+ * store for BF16 storage).  It trades the records' HBM traffic (n_draft
+ * FP32 states per head) for reading the state once more.  Source: the
+ * accepted-prefix commit of the speculative path ("Kimi K3 on modeling_v2
+ * ...", section 5); the pages keep records ("Extend ... isolated NVFP4 Kimi
+ * K3 targets", Description), which kda_commit_accepted follows.
+ *   accepted [batch] int32 (device): m in [0, n_draft]; m >= 1 runs draft
+ *            tokens 1..m of row b (the rows kda_verify was given, same
+ *            layout) from the stored state, stores the state once and writes
+ *            ring entries for positions p..p+m-1.  m = 0 writes nothing.
+ *            Out-of-range m sets KDA_STATUS_BAD_ACCEPTED.
+ *   q, k, alpha, v, g, beta: the verify's inputs, [batch, n_draft, H, .].
+ *   positions: the same values passed to kda_verify; the caller advances
+ *            them by m afterwards.  No output is written (verify gave y). */
+int kda_commit_recompute(const kda_shape *shape, const kda_params *params,
+                         int32_t batch, int32_t n_draft, int64_t num_slots,
+                         const int32_t *slot_ids, const int32_t *positions,
+                         const int32_t *accepted, const void *q, const void *k,
+                         const void *v, const void *alpha, const void *beta,
+                         const void *g, void *pool, void *ring,
+                         int32_t *status, hipStream_t stream);
 
 /* ----- chunked prefill over variable-length sequences ------------------- */
 /* Source: the KDA prefill kernel and its varlen index glue ("Kimi K3 NVFP4
