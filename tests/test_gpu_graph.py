@@ -139,3 +139,64 @@ def test_verify_commit_graph_replay_matches_eager():
         pos += c.accepted
     assert torch.equal(_bits(ds_g.pool), _bits(ds_e.pool))
     assert torch.equal(_bits(ds_g.ring), _bits(ds_e.ring))
+
+
+def test_records_free_verify_and_recompute_graph_replay_matches_eager():
+    """verify without records + kda_commit_recompute captured once and
+    replayed for three rounds with drafts, positions and accepted lengths
+    rewritten in place: every replay matches the eager records path."""
+    torch = need_gpu()
+    n = 4
+    cases = [wl.make_verify(71 + i, B=6, H=4, dk=128, dv=128, n_draft=n, act="bf16",
+                            state="bf16", init="random", name=f"graph_recompute_{i}")
+             for i in range(3)]
+    base = cases[0]
+    B, H, dk, dv = base.batch, base.H, base.dk, base.dv
+    C = 2 * dk + dv
+
+    ds_e = dev.make_state(base)
+    pos = base.pos0.astype(np.int64).copy()
+    ys_e = []
+    for c in cases:
+        tok = dev.tokens_to_device(c.tokens, c.act)
+        rec = torch.empty((B, n, H, dk, dv), device="cuda")
+        dconv = torch.empty((B, n, H, C), device="cuda", dtype=torch.bfloat16)
+        y = torch.empty((B, n, H, dv), device="cuda")
+        p_t = torch.from_numpy(pos.astype(np.int32)).cuda()
+        kda.verify(ds_e.shape, ds_e.params, ds_e.slot_ids, p_t,
+                   *[tok[x] for x in NAMES], ds_e.pool, ds_e.ring, rec, dconv, y)
+        kda.commit_accepted(ds_e.shape, ds_e.slot_ids, p_t,
+                            torch.from_numpy(c.accepted).cuda(), rec, dconv,
+                            ds_e.pool, ds_e.ring)
+        ys_e.append(y)
+        pos += c.accepted
+    torch.cuda.synchronize()
+
+    ds_g = dev.make_state(base)
+    pos = base.pos0.astype(np.int64).copy()
+    pos_buf = torch.empty(B, dtype=torch.int32, device="cuda")
+    acc_buf = torch.empty(B, dtype=torch.int32, device="cuda")
+    tok0 = dev.tokens_to_device(base.tokens, base.act)
+    in_buf = {x: torch.empty_like(tok0[x]) for x in NAMES}
+    y = torch.empty((B, n, H, dv), device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        kda.verify(ds_g.shape, ds_g.params, ds_g.slot_ids, pos_buf,
+                   *[in_buf[x] for x in NAMES], ds_g.pool, ds_g.ring, None, None, y)
+        kda.commit_recompute(ds_g.shape, ds_g.params, ds_g.slot_ids, pos_buf, acc_buf,
+                             *[in_buf[x] for x in NAMES], ds_g.pool, ds_g.ring)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        tok = dev.tokens_to_device(c.tokens, c.act)
+        for x in NAMES:
+            in_buf[x].copy_(tok[x])
+        pos_buf.copy_(torch.from_numpy(pos.astype(np.int32)))
+        acc_buf.copy_(torch.from_numpy(c.accepted))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y), _bits(ys_e[i])), f"replay {i}: y differs"
+        pos += c.accepted
+    assert torch.equal(_bits(ds_g.pool), _bits(ds_e.pool))
+    assert torch.equal(_bits(ds_g.ring), _bits(ds_e.ring))

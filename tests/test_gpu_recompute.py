@@ -101,3 +101,29 @@ def test_recompute_zero_inactive_and_bad_accepted_write_nothing():
     assert st == kda.STATUS_BAD_ACCEPTED
     assert torch.equal(ds.pool.view(torch.uint8), pool0.view(torch.uint8))
     assert torch.equal(ds.ring.view(torch.uint8), ring0.view(torch.uint8))
+
+
+def test_longest_draft_block_records_and_recompute_agree():
+    """n_draft = 16, the longest block the library takes: accepted lengths
+    past the ring's four entries overwrite ring entries several times, and
+    both commits keep the last three raw tokens."""
+    torch = need_gpu()
+    n = 16
+    case = wl.make_verify(56, B=6, H=2, dk=128, dv=128, n_draft=n, act="bf16", state="f32",
+                          init="random", name="recompute_n16")
+    case.accepted = np.array([16, 15, 5, 4, 3, 0], dtype=np.int32)
+    ds_r = dev.make_state(case)
+    rec, dconv, y_r, slot_t, pos_t, st = run_verify_gpu(case, ds_r)
+    assert int(st.item()) == 0
+    assert commit_gpu(case, ds_r, rec, dconv, slot_t, pos_t, case.accepted) == 0
+    ds = dev.make_state(case)
+    tok, slot_t, pos_t, y, _ = verify_no_records(case, ds)
+    assert recompute(ds, tok, slot_t, pos_t, case.accepted) == 0
+    y_ref, rec_ref, S_ref, h_ref = oracle.verify_case(case)
+    assert_parity(y_r.cpu().numpy(), y_ref, 2e-5, "verify y")
+    assert_parity(rec.cpu().numpy(), rec_ref, 2e-5, "records")
+    assert_parity(dev.read_states(ds), S_ref, 2e-5, "recomputed states")
+    np.testing.assert_array_equal(dev.read_window(ds, case.pos0 + case.accepted), h_ref)
+    assert torch.equal(y, y_r)
+    assert torch.equal(ds.pool.view(torch.uint8), ds_r.pool.view(torch.uint8))
+    assert torch.equal(ds.ring.view(torch.uint8), ds_r.ring.view(torch.uint8))
