@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--no-modes", action="store_true",
                     help="time only the headline decode workload")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="comma list of the extra modes to run (bf16, verify, recompute, "
+                         "compact, prefill); all when empty")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (a known byte count "
                          "for scaling the HBM byte counters)")
@@ -507,11 +510,14 @@ def main():
           file=sys.stderr, flush=True)
 
     modes = {}
-    if not args.no_modes:
+    only = set(x for x in args.only.split(",") if x)
+    want = (lambda m: not args.no_modes and (not only or m in only))
+    if want("bf16"):
         case3 = wl.config(3)
         print(f"# decode {case3.name}", file=sys.stderr, flush=True)
         modes["large_batch_decode_bf16_state"] = run_decode_mode(
             torch, case3, args.steps, args.warmup, 4)
+    if want("verify"):
         case2 = wl.config(2)
         print(f"# verify {case2.name}", file=sys.stderr, flush=True)
         modes["spec_verify_commit"] = run_verify_mode(torch, case2, args.steps,
@@ -519,14 +525,17 @@ def main():
         modes["spec_verify_commit"]["verify_plus_commit_us"] = (
             modes["spec_verify_commit"]["verify_kernel_us"] +
             modes["spec_verify_commit"]["commit_kernel_us"])
+    if want("recompute"):
         print(f"# verify without records, commit by recompute", file=sys.stderr, flush=True)
         modes["spec_verify_recompute"] = run_verify_recompute_mode(
-            torch, case2, args.steps, args.warmup, 8)
+            torch, wl.config(2), args.steps, args.warmup, 8)
+    if want("compact"):
         for st, layers in (("f32", 32), ("bf16", 48)):
             casec = wl.compact_heads(st)
             print(f"# decode {casec.name}", file=sys.stderr, flush=True)
             modes[f"compact_heads_decode_{st}_state"] = run_decode_mode(
                 torch, casec, args.steps, args.warmup, layers)
+    if want("prefill"):
         case4 = wl.config(4)
         print(f"# prefill {case4.name}", file=sys.stderr, flush=True)
         modes["chunked_prefill"] = run_prefill_mode(torch, case4, args.steps, args.warmup)
