@@ -5,6 +5,7 @@
 // entries, ...", section 1).  Nothing here allocates, synchronises the host
 // or reads the environment.
 #include <hip/hip_runtime_api.h>
+#include <math.h>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -16,13 +17,16 @@ constexpr int kMaxDraft = 16;
 
 bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 
-size_t act_size(const kda_shape* s) { return s->act_dtype == KDA_BF16 ? 2 : 4; }
+size_t act_size(const kda_shape* s) {
+    return s->act_dtype == KDA_F32 ? 4 : (s->act_dtype == KDA_BF16 ? 2 : 1);
+}
 size_t state_size(const kda_shape* s) { return s->state_dtype == KDA_BF16 ? 2 : 4; }
 
 // Shape check shared by every entry point.  Returns KDA_OK or an error.
 int check_shape(const kda_shape* s) {
     if (!s) return KDA_ERR_NULL;
-    if (!dtype_ok(s->act_dtype) || !dtype_ok(s->state_dtype)) return KDA_ERR_DTYPE;
+    if (!(dtype_ok(s->act_dtype) || s->act_dtype == KDA_FP8_E4M3) || !dtype_ok(s->state_dtype))
+        return KDA_ERR_DTYPE;
     if (s->gate != KDA_GATE_SIGMOID && s->gate != KDA_GATE_SILU) return KDA_ERR_DTYPE;
     if (s->gate_inputs != KDA_GATES_VALUES && s->gate_inputs != KDA_GATES_LOGITS)
         return KDA_ERR_DTYPE;
@@ -34,9 +38,21 @@ int check_shape(const kda_shape* s) {
     return KDA_OK;
 }
 
-int check_params(const kda_params* p) {
+// Checks the parameters a call with shape s uses (s already checked).
+int check_params(const kda_params* p, const kda_shape* s) {
     if (!p || !p->conv_w_q || !p->conv_w_k || !p->conv_w_v) return KDA_ERR_NULL;
+    if (s->act_dtype == KDA_FP8_E4M3)
+        for (int i = 0; i < 3; ++i)
+            if (!(p->qkv_scale[i] > 0.0f) || !(p->qkv_scale[i] < INFINITY)) return KDA_ERR_SHAPE;
     return KDA_OK;
+}
+
+// Dequantisation scales of q, k and v (1 unless the activations are FP8).
+void set_scales(const kda_params* p, const kda_shape* s, float& sq, float& sk, float& sv) {
+    const bool fp8 = s->act_dtype == KDA_FP8_E4M3;
+    sq = fp8 ? p->qkv_scale[0] : 1.0f;
+    sk = fp8 ? p->qkv_scale[1] : 1.0f;
+    sv = fp8 ? p->qkv_scale[2] : 1.0f;
 }
 
 }  // namespace
@@ -195,6 +211,7 @@ static kda::TokenArgs token_args(const kda_shape* s, const kda_params* p,
     a.norm_eps = s->norm_eps;
     a.gate = s->gate;
     a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
+    set_scales(p, s, a.scale_q, a.scale_k, a.scale_v);
     return a;
 }
 
@@ -205,7 +222,7 @@ int kda_decode(const kda_shape* s, const kda_params* p, int32_t batch,
                int32_t* status, hipStream_t stream) {
     int rc = check_shape(s);
     if (rc != KDA_OK) return rc;
-    if ((rc = check_params(p)) != KDA_OK) return rc;
+    if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (batch < 0 || num_slots < 0) return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
     if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
@@ -227,7 +244,7 @@ int kda_verify(const kda_shape* s, const kda_params* p, int32_t batch,
                int32_t* status, hipStream_t stream) {
     int rc = check_shape(s);
     if (rc != KDA_OK) return rc;
-    if ((rc = check_params(p)) != KDA_OK) return rc;
+    if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
         return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
@@ -252,7 +269,7 @@ int kda_commit_recompute(const kda_shape* s, const kda_params* p, int32_t batch,
                          hipStream_t stream) {
     int rc = check_shape(s);
     if (rc != KDA_OK) return rc;
-    if ((rc = check_params(p)) != KDA_OK) return rc;
+    if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
         return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
@@ -306,7 +323,7 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
                 hipStream_t stream) {
     int rc = check_shape(s);
     if (rc != KDA_OK) return rc;
-    if ((rc = check_params(p)) != KDA_OK) return rc;
+    if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || num_slots < 0)
         return KDA_ERR_SHAPE;
     if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return KDA_OK;
@@ -345,6 +362,7 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
     a.norm_eps = s->norm_eps;
     a.gate = s->gate;
     a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
+    set_scales(p, s, a.scale_q, a.scale_k, a.scale_v);
     return kda::launch_prefill(*s, a, stream);
 }
 

@@ -12,7 +12,15 @@
 
 namespace kda {
 
-enum : int { kF32 = 0, kBF16 = 1 };
+enum : int { kF32 = 0, kBF16 = 1, kFP8 = 2 };
+
+// FP8 activations carry q, k, v (and the raw tokens kept in the ring and
+// the draft buffer) as OCP E4M3 bytes times a per-tensor scale; alpha, beta
+// and g then stay BF16.  kGateAct is the dtype of alpha, beta and g.
+template <int ACT>
+constexpr int kGateAct = ACT == kFP8 ? kBF16 : ACT;
+template <int ACT>
+constexpr size_t kActSize = ACT == kF32 ? 4 : (ACT == kBF16 ? 2 : 1);
 enum : int { kGateSigmoid = 0, kGateSilu = 1 };
 
 constexpr int kWave = 64;
@@ -20,6 +28,18 @@ constexpr int kConvW = 4;  // conv taps; the ring holds kConvW entries
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
+}
+
+// OCP FP8 E4M3 (bias 7, three mantissa bits, no infinities) to FP32,
+// exactly: exponent field e > 0 gives 2^(e-7) * (1 + m/8), placed straight
+// into the FP32 fields; e = 0 gives the subnormal m * 2^-9.  The NaN code
+// (all exponent and mantissa bits set) is not a valid input.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+    const uint32_t em = byte & 0x7fu;
+    const uint32_t sign = (byte & 0x80u) << 24;
+    const float mag = em >= 8u ? __uint_as_float(((em >> 3) + 120u) << 23 | (em & 7u) << 20)
+                               : (float)em * 0.001953125f;   // m * 2^-9
+    return __uint_as_float(__float_as_uint(mag) | sign);
 }
 
 // Round to nearest even; NaN stays a quiet NaN.
@@ -30,24 +50,23 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Activation bits to FP32 (exact; an FP8 value before its tensor scale).
+template <int ACT>
+__device__ __forceinline__ float act_from_bits(uint32_t bits) {
+    if constexpr (ACT == kF32) return __uint_as_float(bits);
+    else if constexpr (ACT == kBF16) return bf16_to_f32(bits);
+    else return e4m3_to_f32(bits);
+}
+
 // Scalar activation load, widened to FP32.
 template <int ACT>
 __device__ __forceinline__ float ld_act(const void* base, int64_t idx) {
     if constexpr (ACT == kF32) {
         return static_cast<const float*>(base)[idx];
-    } else {
+    } else if constexpr (ACT == kBF16) {
         return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
-    }
-}
-
-// Raw copy of one activation element (bit exact).
-template <int ACT>
-__device__ __forceinline__ void cp_act(void* dst, int64_t di, const void* src,
-                                       int64_t si) {
-    if constexpr (ACT == kF32) {
-        static_cast<float*>(dst)[di] = static_cast<const float*>(src)[si];
     } else {
-        static_cast<uint16_t*>(dst)[di] = static_cast<const uint16_t*>(src)[si];
+        return e4m3_to_f32(static_cast<const uint8_t*>(base)[idx]);
     }
 }
 
@@ -55,8 +74,10 @@ template <int ACT>
 __device__ __forceinline__ void st_act_bits(void* dst, int64_t di, uint32_t bits) {
     if constexpr (ACT == kF32) {
         static_cast<uint32_t*>(dst)[di] = bits;
-    } else {
+    } else if constexpr (ACT == kBF16) {
         static_cast<uint16_t*>(dst)[di] = static_cast<uint16_t>(bits);
+    } else {
+        static_cast<uint8_t*>(dst)[di] = static_cast<uint8_t>(bits);
     }
 }
 
@@ -64,8 +85,10 @@ template <int ACT>
 __device__ __forceinline__ uint32_t ld_act_bits(const void* src, int64_t si) {
     if constexpr (ACT == kF32) {
         return static_cast<const uint32_t*>(src)[si];
-    } else {
+    } else if constexpr (ACT == kBF16) {
         return static_cast<const uint16_t*>(src)[si];
+    } else {
+        return static_cast<const uint8_t*>(src)[si];
     }
 }
 

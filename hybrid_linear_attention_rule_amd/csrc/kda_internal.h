@@ -42,6 +42,7 @@ struct TokenArgs {
     float norm_eps;
     int32_t gate;
     int32_t gate_logits;  // alpha, beta hold logits a, b
+    float scale_q, scale_k, scale_v;  // FP8 activations: dequantisation scales
 };
 
 struct CommitArgs {
@@ -100,6 +101,7 @@ struct PrefillArgs {
     float norm_eps;
     int32_t gate;
     int32_t gate_logits;  // alpha, beta hold logits a, b
+    float scale_q, scale_k, scale_v;  // FP8 activations: dequantisation scales
 };
 
 enum class TokenMode { Decode, Verify, Recompute };

@@ -154,6 +154,10 @@ template <>
 struct Raw8<kBF16> {
     uint4 u;
 };
+template <>
+struct Raw8<kFP8> {
+    uint2 u;                          // eight E4M3 bytes (8-byte aligned)
+};
 
 template <int ACT>
 __device__ __forceinline__ Raw8<ACT> ld_raw8(const void* base, int64_t idx) {
@@ -162,8 +166,10 @@ __device__ __forceinline__ Raw8<ACT> ld_raw8(const void* base, int64_t idx) {
         const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
         r.a = p[0];
         r.b = p[1];
-    } else {
+    } else if constexpr (ACT == kBF16) {
         r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    } else {
+        r.u = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + idx);
     }
     return r;
 }
@@ -176,8 +182,10 @@ __device__ __forceinline__ Raw8<ACT> ld_raw8_at(const char* base, uint32_t off) 
         const float4* p = reinterpret_cast<const float4*>(base + off);
         r.a = p[0];
         r.b = p[1];
-    } else {
+    } else if constexpr (ACT == kBF16) {
         r.u = *reinterpret_cast<const uint4*>(base + off);
+    } else {
+        r.u = *reinterpret_cast<const uint2*>(base + off);
     }
     return r;
 }
@@ -188,11 +196,17 @@ __device__ __forceinline__ void unpack8(const Raw8<ACT>& r, bool ok, float (&x)[
     if constexpr (ACT == kF32) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
         x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
-    } else {
+    } else if constexpr (ACT == kBF16) {
         x[0] = __uint_as_float(r.u.x << 16); x[1] = __uint_as_float(r.u.x & 0xffff0000u);
         x[2] = __uint_as_float(r.u.y << 16); x[3] = __uint_as_float(r.u.y & 0xffff0000u);
         x[4] = __uint_as_float(r.u.z << 16); x[5] = __uint_as_float(r.u.z & 0xffff0000u);
         x[6] = __uint_as_float(r.u.w << 16); x[7] = __uint_as_float(r.u.w & 0xffff0000u);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            x[q] = e4m3_to_f32((r.u.x >> (8 * q)) & 0xffu);
+            x[4 + q] = e4m3_to_f32((r.u.y >> (8 * q)) & 0xffu);
+        }
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
@@ -221,10 +235,11 @@ __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v
 
 // Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
 // [c0, c0 + 8), from the seven raw tokens tb-3..tb+3 and the channels' four
-// taps; zero for tokens at or past L.
+// taps; zero for tokens at or past L.  FP8 activations: times the tensor's
+// dequantisation scale `sc`, taken out of the sum.
 template <int ACT>
 __device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[7],
-                                        const float4 (&wt)[8], int tb, int L,
+                                        const float4 (&wt)[8], int tb, int L, float sc,
                                         float (&c)[4][8]) {
     float x[7][8];
 #pragma unroll
@@ -238,6 +253,7 @@ __device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok
             acc = fmaf(w4.y, x[e + 1][q], acc);
             acc = fmaf(w4.z, x[e + 2][q], acc);
             acc = fmaf(w4.w, x[e + 3][q], acc);
+            if constexpr (ACT == kFP8) acc *= sc;
             c[e][q] = tb + e < L ? acc : 0.f;
         }
     }
@@ -339,10 +355,11 @@ __device__ __forceinline__ ChunkItem next_item(const PrefillArgs& a, int n_slots
 }
 
 // A lane's raw inputs for one item: q, k, v for its seven conv tokens, alpha
-// and beta for its four tokens.
+// and beta (in the gate dtype) for its four tokens.
 template <int ACT>
 struct ChunkIn {
-    Raw8<ACT> rq[7], rk[7], rv[7], ra[4];
+    Raw8<ACT> rq[7], rk[7], rv[7];
+    Raw8<kGateAct<ACT>> ra[4];
     uint32_t rb[4];                  // bits, widened where used (no wait here)
     bool okm[7];
 };
@@ -355,14 +372,17 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
         // Interior chunk: every conv token lies inside the sequence.  Each
         // load is a uniform row base plus one per-lane byte offset (lane's
         // first token, head and channels), so the addressing is scalar.
-        constexpr size_t ESZ = ACT == kF32 ? 4 : 2;
-        const size_t row_b = (size_t)a.H * PD * ESZ;             // bytes per token row
+        constexpr int GACT = kGateAct<ACT>;
+        constexpr size_t ESZ = kActSize<ACT>, GESZ = kActSize<GACT>;
+        const size_t row_b = (size_t)a.H * PD * ESZ;             // bytes per q|k|v token row
+        const size_t rowa_b = (size_t)a.H * PD * GESZ;           // bytes per alpha token row
         const int64_t row0 = (int64_t)it.v.lo + t0 - 3;          // token of conv tap 0, lane 0
         const uint32_t off = (uint32_t)((size_t)tb * row_b + ((size_t)h * PD + c0) * ESZ);
+        const uint32_t offa = (uint32_t)((size_t)tb * rowa_b + ((size_t)h * PD + c0) * GESZ);
         const char* qb = static_cast<const char*>(a.q) + row0 * row_b;
         const char* kb = static_cast<const char*>(a.k) + row0 * row_b;
         const char* vb = static_cast<const char*>(a.v) + row0 * row_b;
-        const char* ab = static_cast<const char*>(a.alpha) + (row0 + 3) * row_b;
+        const char* ab = static_cast<const char*>(a.alpha) + (row0 + 3) * rowa_b;
 #pragma unroll
         for (int m = 0; m < 7; ++m) {
             in.rq[m] = ld_raw8_at<ACT>(qb + m * row_b, off);
@@ -370,13 +390,14 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
             in.rv[m] = ld_raw8_at<ACT>(vb + m * row_b, off);
             in.okm[m] = true;
         }
-        const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * ESZ;
-        const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * ESZ);
+        const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * GESZ;
+        const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * GESZ);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            in.ra[e] = ld_raw8_at<ACT>(ab + e * row_b, off);
-            in.rb[e] = ACT == kF32 ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * ESZ + offb)
-                                   : *reinterpret_cast<const uint16_t*>(bb + e * a.H * ESZ + offb);
+            in.ra[e] = ld_raw8_at<GACT>(ab + e * rowa_b, offa);
+            in.rb[e] = GACT == kF32
+                ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * GESZ + offb)
+                : *reinterpret_cast<const uint16_t*>(bb + e * a.H * GESZ + offb);
         }
         return;
     }
@@ -390,8 +411,8 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
     for (int e = 0; e < 4; ++e) {
         // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
         const int64_t row = (int64_t)(it.v.lo + t0 + min(tb + e, L - 1)) * a.H + h;
-        in.ra[e] = ld_raw8<ACT>(a.alpha, row * PD + c0);
-        in.rb[e] = ld_act_bits<ACT>(a.beta, row);
+        in.ra[e] = ld_raw8<kGateAct<ACT>>(a.alpha, row * PD + c0);
+        in.rb[e] = ld_act_bits<kGateAct<ACT>>(a.beta, row);
     }
 }
 
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     // Persistent: the workgroup takes items blockIdx.x, + gridDim.x, ...
     // The next item's inputs are requested as soon as the current item's
     // convolutions have consumed theirs, so they arrive during steps 2-5.
-    constexpr bool kEarlyTaps = ACT == kBF16;
+    constexpr bool kEarlyTaps = ACT != kF32;
     ChunkItem it;
     ChunkIn<ACT> in;
     float4 wtq[8], wtk[8], wtv[8];             // conv taps of the lane's channels
@@ -482,7 +503,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     {
         if constexpr (!kEarlyTaps) load_taps(a, h, c0, wtq, wtk, wtv);
         float qh[4][8], kh[4][8], al[4][8];
-        conv4x8<ACT>(in.rq, in.okm, wtq, tb, L, qh);
+        conv4x8<ACT>(in.rq, in.okm, wtq, tb, L, a.scale_q, qh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sq = 0.f;
@@ -492,7 +513,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
-        conv4x8<ACT>(in.rk, in.okm, wtk, tb, L, kh);
+        conv4x8<ACT>(in.rk, in.okm, wtk, tb, L, a.scale_k, kh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sk = 0.f;
@@ -505,8 +526,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool live = tb + e < L;
-            unpack8<ACT>(in.ra[e], true, al[e]);
-            float bv = ACT == kF32 ? __uint_as_float(in.rb[e]) : bf16_to_f32(in.rb[e]);
+            unpack8<kGateAct<ACT>>(in.ra[e], true, al[e]);
+            float bv = act_from_bits<kGateAct<ACT>>(in.rb[e]);
             if (a.gate_logits) {
 #pragma unroll
                 for (int q = 0; q < 8; ++q) al[e][q] = decay_from_logit(al[e][q]);
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             for (int q = 0; q < 8; ++q) al[e][q] = live ? al[e][q] : 1.f;
             bt[e] = live ? bv : 0.f;
         }
-        conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, cv);
+        conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, a.scale_v, cv);
 
         // every input of this item is consumed: find the next item (its
         // inputs are requested at the start of step 2b)
@@ -1561,7 +1582,7 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
     float* y = a.y + row * PD + 4 * l32;
     const float4 o = *reinterpret_cast<const float4*>(y);
     float gv[4];
-    if constexpr (ACT == kF32) {
+    if constexpr (kGateAct<ACT> == kF32) {
         const float4 g4 =
             *reinterpret_cast<const float4*>(static_cast<const float*>(a.g) + row * PD + 4 * l32);
         gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
@@ -1645,7 +1666,10 @@ int launch_prefill(const kda_shape& s, const PrefillArgs& a, hipStream_t stream)
     if (s.act_dtype == kF32 && s.state_dtype == kF32) return launch_prefill_t<kF32, kF32>(a, stream);
     if (s.act_dtype == kF32 && s.state_dtype == kBF16) return launch_prefill_t<kF32, kBF16>(a, stream);
     if (s.act_dtype == kBF16 && s.state_dtype == kF32) return launch_prefill_t<kBF16, kF32>(a, stream);
-    return launch_prefill_t<kBF16, kBF16>(a, stream);
+    if (s.act_dtype == kBF16 && s.state_dtype == kBF16) return launch_prefill_t<kBF16, kBF16>(a, stream);
+    if (s.act_dtype == kFP8 && s.state_dtype == kF32) return launch_prefill_t<kFP8, kF32>(a, stream);
+    if (s.act_dtype == kFP8 && s.state_dtype == kBF16) return launch_prefill_t<kFP8, kBF16>(a, stream);
+    return KDA_ERR_UNSUPPORTED;
 }
 
 }  // namespace kda

@@ -93,6 +93,8 @@ int launch_conv_io(const kda_shape& s, const StateIoArgs& a, hipStream_t stream)
     const dim3 grid((unsigned)a.n * (kConvW - 1) * (unsigned)a.H), block(256);
     if (s.act_dtype == kF32)
         hipLaunchKernelGGL(conv_io_kernel<kF32>, grid, block, 0, stream, a, C);
+    else if (s.act_dtype == kFP8)
+        hipLaunchKernelGGL(conv_io_kernel<kFP8>, grid, block, 0, stream, a, C);
     else
         hipLaunchKernelGGL(conv_io_kernel<kBF16>, grid, block, 0, stream, a, C);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;

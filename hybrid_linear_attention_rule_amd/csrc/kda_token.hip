@@ -153,11 +153,6 @@ __device__ __forceinline__ void store_record(float* rec, int r, int c,
                                  __float_as_uint(s[p][e + 2]), __float_as_uint(s[p][e + 3])));
 }
 
-template <int ACT>
-__device__ __forceinline__ float act_from_bits(uint32_t bits) {
-    if constexpr (ACT == kF32) return __uint_as_float(bits);
-    else return bf16_to_f32(bits);
-}
 
 // Phase A of a token.  Conv roles, one per wave (dk and dv are multiples of
 // the wave size): waves covering threads t < DK convolve q channel t (A) and
@@ -178,7 +173,9 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
                                         float& cb, float& al, float& beta, float& gv,
                                         Issue&& issue_more) {
     constexpr int C = 2 * DK + DV;
-    constexpr size_t ESZ = (ACT == kF32) ? 4 : 2;
+    constexpr size_t ESZ = kActSize<ACT>;                  // q, k, v, ring, drafts
+    constexpr int GACT = kGateAct<ACT>;
+    constexpr size_t GESZ = kActSize<GACT>;                // alpha, beta, g
     const int tid = threadIdx.x;
     const int H = a.H;
     const int64_t tok = (int64_t)b * n + t;
@@ -194,11 +191,11 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
 
     // unconditional loads from valid lane offsets; lanes that do not own a
     // channel discard the value
-    const float al_ld = ld_act<ACT>(static_cast<const char*>(a.alpha) +
-                                        (size_t)(tok * H + h) * DK * ESZ, qk ? tid : 0);
-    const float g_ld = ld_act<ACT>(static_cast<const char*>(a.g) +
-                                       (size_t)(tok * H + h) * DV * ESZ, tid < DV ? tid : 0);
-    beta = ld_act<ACT>(a.beta, tok * H + h);
+    const float al_ld = ld_act<GACT>(static_cast<const char*>(a.alpha) +
+                                         (size_t)(tok * H + h) * DK * GESZ, qk ? tid : 0);
+    const float g_ld = ld_act<GACT>(static_cast<const char*>(a.g) +
+                                        (size_t)(tok * H + h) * DV * GESZ, tid < DV ? tid : 0);
+    beta = ld_act<GACT>(a.beta, tok * H + h);
     al = qk ? al_ld : 0.f;
     if (a.gate_logits) {
         beta = write_from_logit(beta);
@@ -252,6 +249,11 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
             cb = fmaf(w4b.y, xb[1], cb);
             cb = fmaf(w4b.z, xb[2], cb);
             cb = fmaf(w4b.w, xb[3], cb);
+        }
+        if constexpr (ACT == kFP8) {
+            // per-tensor dequantisation, taken out of the conv sum
+            ca *= qk ? a.scale_q : a.scale_v;
+            cb *= a.scale_k;
         }
         // keep the raw token: decode and recompute -> ring entry (pos + t)
         // mod 4, verify -> draft_conv (when kept)
@@ -593,6 +595,10 @@ static int dispatch_token(const kda_shape& s, const TokenArgs& a, int32_t batch,
         return launch_token_t<DK, DV, kF32, kBF16>(a, batch, mode, stream);
     if (s.act_dtype == kBF16 && s.state_dtype == kF32)
         return launch_token_t<DK, DV, kBF16, kF32>(a, batch, mode, stream);
+    if (s.act_dtype == kFP8 && s.state_dtype == kF32)
+        return launch_token_t<DK, DV, kFP8, kF32>(a, batch, mode, stream);
+    if (s.act_dtype == kFP8)
+        return launch_token_t<DK, DV, kFP8, kBF16>(a, batch, mode, stream);
     return launch_token_t<DK, DV, kBF16, kBF16>(a, batch, mode, stream);
 }
 
@@ -623,6 +629,10 @@ static int dispatch_commit(const kda_shape& s, const CommitArgs& a, int32_t batc
         return launch_commit_t<DK, DV, kF32, kBF16>(a, batch, stream);
     if (s.act_dtype == kBF16 && s.state_dtype == kF32)
         return launch_commit_t<DK, DV, kBF16, kF32>(a, batch, stream);
+    if (s.act_dtype == kFP8 && s.state_dtype == kF32)
+        return launch_commit_t<DK, DV, kFP8, kF32>(a, batch, stream);
+    if (s.act_dtype == kFP8)
+        return launch_commit_t<DK, DV, kFP8, kBF16>(a, batch, stream);
     return launch_commit_t<DK, DV, kBF16, kBF16>(a, batch, stream);
 }
 

@@ -15,14 +15,26 @@ import numpy as np
 import torch
 
 from . import kda
-from .workloads import Case
+from .workloads import FP8_SCALE, Case, gate_dtype
 
 RING = 4
 
 
 def _act(x: np.ndarray, act: str, device) -> torch.Tensor:
-    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    """Values exact in `act` -> device tensor of that dtype (FP8: the E4M3
+    values x / FP8_SCALE, exact because the scale is a power of two)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if act == "fp8":
+        t = torch.from_numpy(x / np.float32(FP8_SCALE))
+        return t.to(torch.float8_e4m3fn).to(device)
+    t = torch.from_numpy(x)
     return t.to(device=device, dtype=torch.bfloat16 if act == "bf16" else torch.float32)
+
+
+def _from_act(t: torch.Tensor, act: str) -> np.ndarray:
+    """Device activations -> their float64 values."""
+    x = t.float().cpu().numpy().astype(np.float64)
+    return x * FP8_SCALE if act == "fp8" else x
 
 
 def shape_of(case: Case, gate: str = "sigmoid", q_scale=1.0) -> kda.KdaShape:
@@ -33,13 +45,17 @@ def shape_of(case: Case, gate: str = "sigmoid", q_scale=1.0) -> kda.KdaShape:
                                      "logits": kda.GATES_LOGITS}[case.gates])
 
 
+def qkv_scale_of(case: Case) -> tuple:
+    return (FP8_SCALE,) * 3 if case.act == "fp8" else (1.0, 1.0, 1.0)
+
+
 def params_of(case: Case, device="cuda") -> kda.KdaParams:
     w = case.weights
     f = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
     return kda.KdaParams(f(w.conv_q.reshape(-1, w.conv_q.shape[-1])),
                          f(w.conv_k.reshape(-1, w.conv_k.shape[-1])),
                          f(w.conv_v.reshape(-1, w.conv_v.shape[-1])),
-                         f(w.norm_w))
+                         f(w.norm_w), qkv_scale_of(case))
 
 
 @dataclass
@@ -89,7 +105,7 @@ def read_states(ds: DeviceState, slots=None) -> np.ndarray:
 def read_window(ds: DeviceState, positions: np.ndarray, slots=None) -> np.ndarray:
     """Logical float64 history [B, 3, H, C] (oldest first) at `positions`."""
     slots = ds.slots if slots is None else slots
-    ring = ds.ring.float().cpu().numpy()
+    ring = _from_act(ds.ring, ds.shape.act)
     B = len(slots)
     out = np.zeros((B, RING - 1) + ring.shape[2:])
     for b in range(B):
@@ -101,6 +117,15 @@ def read_window(ds: DeviceState, positions: np.ndarray, slots=None) -> np.ndarra
 
 
 def tokens_to_device(toks, act: str, device="cuda"):
-    """TokenInputs arrays -> dict of device tensors in the activation dtype."""
-    return {name: _act(getattr(toks, name), act, device)
-            for name in ("q", "k", "v", "alpha", "beta", "g")}
+    """TokenInputs arrays -> dict of device tensors: q, k, v in the
+    activation dtype, alpha, beta and g in the gate dtype."""
+    out = {name: _act(getattr(toks, name), act, device) for name in ("q", "k", "v")}
+    out.update({name: _act(getattr(toks, name), gate_dtype(act), device)
+                for name in ("alpha", "beta", "g")})
+    return out
+
+
+def acts_to_numpy(t: torch.Tensor, act: str) -> np.ndarray:
+    """Raw activations read back from the device (ring, draft tokens) as
+    their float64 values."""
+    return _from_act(t, act)

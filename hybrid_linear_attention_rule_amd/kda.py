@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
 
-F32, BF16 = 0, 1
+F32, BF16, FP8_E4M3 = 0, 1, 2
 GATE_SIGMOID, GATE_SILU = 0, 1
 GATES_VALUES, GATES_LOGITS = 0, 1
 STATUS_BAD_SLOT = 1
@@ -25,8 +25,8 @@ STATUS_BAD_POSITION = 2
 STATUS_BAD_ACCEPTED = 4
 STATUS_BAD_SEQLENS = 8
 
-_DT = {"f32": F32, "bf16": BF16}
-_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+_DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.float8_e4m3fn}
 
 
 class KdaError(RuntimeError):
@@ -46,7 +46,8 @@ class _Shape(ctypes.Structure):
 
 class _Params(ctypes.Structure):
     _fields_ = [("conv_w_q", ctypes.c_void_p), ("conv_w_k", ctypes.c_void_p),
-                ("conv_w_v", ctypes.c_void_p), ("norm_w", ctypes.c_void_p)]
+                ("conv_w_v", ctypes.c_void_p), ("norm_w", ctypes.c_void_p),
+                ("qkv_scale", ctypes.c_float * 3)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -121,12 +122,13 @@ def _expect(t, numel, dtype, name):
 
 def _check_tokens(shape, lead, q, k, v, alpha, beta, g):
     H, dk, dv, a = shape.num_heads, shape.head_k, shape.head_v, shape.act_dtype
+    ga = shape.gate_dtype
     _expect(q, lead * H * dk, a, "q")
     _expect(k, lead * H * dk, a, "k")
     _expect(v, lead * H * dv, a, "v")
-    _expect(alpha, lead * H * dk, a, "alpha")
-    _expect(beta, lead * H, a, "beta")
-    _expect(g, lead * H * dv, a, "g")
+    _expect(alpha, lead * H * dk, ga, "alpha")
+    _expect(beta, lead * H, ga, "beta")
+    _expect(g, lead * H * dv, ga, "g")
 
 
 def _check_pool_ring(shape, pool, ring):
@@ -175,7 +177,13 @@ class KdaShape:
 
     @property
     def act_dtype(self) -> torch.dtype:
+        """dtype of q, k, v, the ring and the raw drafts"""
         return _TORCH_DT[_DT[self.act]]
+
+    @property
+    def gate_dtype(self) -> torch.dtype:
+        """dtype of alpha, beta and g (BF16 when the activations are FP8)"""
+        return torch.bfloat16 if self.act == "fp8" else self.act_dtype
 
     @property
     def state_dtype(self) -> torch.dtype:
@@ -188,11 +196,13 @@ class KdaParams:
     conv_w_k: torch.Tensor  # [H*dk, 4] fp32
     conv_w_v: torch.Tensor  # [H*dv, 4] fp32
     norm_w: torch.Tensor | None = None  # [dv] fp32
+    qkv_scale: tuple = (1.0, 1.0, 1.0)  # FP8 activations: dequantisation scales
 
     def c(self) -> _Params:
         return _Params(self.conv_w_q.data_ptr(), self.conv_w_k.data_ptr(),
                        self.conv_w_v.data_ptr(),
-                       None if self.norm_w is None else self.norm_w.data_ptr())
+                       None if self.norm_w is None else self.norm_w.data_ptr(),
+                       (ctypes.c_float * 3)(*self.qkv_scale))
 
 
 # ------------------------------------------------------------------ sizes

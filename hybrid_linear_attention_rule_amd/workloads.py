@@ -18,8 +18,9 @@ themselves (rounded to the activation dtype) in place of alpha and beta;
 the mixer then forms alpha and beta.
 
 Draws are fp64 from numpy's PCG64 and are then rounded to the activation
-dtype: float32 (round to nearest even), or bfloat16 (round to float32, then
-to nearest even on the upper 16 bits).  Conv and norm weights stay float32.
+dtype: float32 (round to nearest even), bfloat16 (round to float32, then
+to nearest even on the upper 16 bits), or for "fp8" q, k, v and the history
+to E4M3 values times FP8_SCALE with alpha, beta and g in bfloat16.  Conv and norm weights stay float32.
 Every array here holds values that are exact in its dtype, stored as float32
 (bfloat16 values are float32 values with 16 zero low bits); ``bf16_bits``
 gives the 16-bit patterns the device buffers hold.
@@ -30,7 +31,12 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-ACT_DTYPES = ("f32", "bf16")
+ACT_DTYPES = ("f32", "bf16", "fp8")
+
+# FP8 workloads store q, k, v (and the raw history) as E4M3 values times this
+# per-tensor dequantisation scale; N(0, 1) draws then sit far inside E4M3's
+# range (|x| / scale <= 448 for |x| <= 14).
+FP8_SCALE = 2.0 ** -5
 STATE_DTYPES = ("f32", "bf16")
 
 
@@ -45,11 +51,32 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return (u.astype(np.uint32) << 16).view(np.float32)
 
 
+def round_e4m3(x: np.ndarray) -> np.ndarray:
+    """Nearest OCP FP8 E4M3 value (bias 7, three mantissa bits, no
+    infinities, largest finite 448), ties to even, saturating at +-448, as
+    float32.  A binade [2^e, 2^(e+1)) holds steps of 2^(e-3); below 2^-6 the
+    subnormals keep the step 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = 2.0 ** (np.clip(e, -6, 8) - 3)
+    r = np.minimum(np.round(a / step) * step, 448.0)     # np.round: ties to even
+    return (np.sign(x) * r).astype(np.float32)
+
+
+def gate_dtype(act: str) -> str:
+    """dtype of alpha, beta and g: FP8 activations keep the gates in BF16."""
+    return "bf16" if act == "fp8" else act
+
+
 def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return round_f32(x)
     if dtype == "bf16":
         return round_bf16(x)
+    if dtype == "fp8":
+        return (round_e4m3(np.asarray(x, dtype=np.float64) / FP8_SCALE) *
+                np.float32(FP8_SCALE)).astype(np.float32)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
@@ -132,14 +159,15 @@ def _tokens(rng, lead, H, dk, dv, act, gates="values") -> TokenInputs:
     v = round_to(rng.standard_normal(lead + (H, dv)), act)
     a = rng.standard_normal(lead + (H, dk))
     b = rng.standard_normal(lead + (H,))
+    ga = gate_dtype(act)
     if gates == "logits":
-        alpha, beta = round_to(a, act), round_to(b, act)
+        alpha, beta = round_to(a, ga), round_to(b, ga)
     elif gates == "values":
-        alpha = round_to(np.exp(-_softplus(a)), act)
-        beta = round_to(_sigmoid(b), act)
+        alpha = round_to(np.exp(-_softplus(a)), ga)
+        beta = round_to(_sigmoid(b), ga)
     else:
         raise ValueError(f"unknown gate inputs {gates!r}")
-    g = round_to(rng.standard_normal(lead + (H, dv)), act)
+    g = round_to(rng.standard_normal(lead + (H, dv)), ga)
     return TokenInputs(q, k, v, alpha, beta, g)
 
 

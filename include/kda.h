@@ -93,7 +93,12 @@ enum {
     KDA_STATUS_BAD_SEQLENS = 8    /* cu_seqlens not monotone, or past end */
 };
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+/* KDA_FP8_E4M3 is an activation dtype only: q, k, v, the conv ring and the
+ * raw draft tokens are OCP FP8 E4M3 bytes (bias 7, no infinities, max 448)
+ * times per-tensor scales (kda_params.qkv_scale), and alpha, beta and g are
+ * BF16.  It follows the FP8 activations the model keeps ("Extend
+ * NVIDIA/TensorRT-LLM#19991 ...", Description). */
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_FP8_E4M3 = 2 } kda_dtype;
 typedef enum { KDA_GATE_SIGMOID = 0, KDA_GATE_SILU = 1 } kda_gate;
 /* What the alpha and beta buffers hold.  LOGITS: the decay logit a per key
  * channel and the write logit b per head, as the f_b projection the mixer
@@ -110,7 +115,8 @@ typedef struct {
     int32_t head_k;      /* dk */
     int32_t head_v;      /* dv */
     int32_t conv_width;  /* 4 */
-    int32_t act_dtype;   /* kda_dtype of q, k, v, alpha, beta, g and the ring */
+    int32_t act_dtype;   /* kda_dtype of q, k, v, alpha, beta, g and the ring
+                          * (FP8: q, k, v and the ring; alpha, beta, g BF16) */
     int32_t state_dtype; /* kda_dtype of the state pool */
     int32_t gate;        /* kda_gate of the output gate */
     float q_scale;       /* multiplies the normalised q (1 in the usual form) */
@@ -119,12 +125,16 @@ typedef struct {
     int32_t gate_inputs; /* kda_gate_inputs of the alpha and beta buffers */
 } kda_shape;
 
-/* Host struct of device pointers to the layer's parameters. */
+/* Host struct of the layer's parameters: device pointers to the weights,
+ * and host values of the FP8 dequantisation scales. */
 typedef struct {
     const float *conv_w_q; /* [H*dk, 4] */
     const float *conv_w_k; /* [H*dk, 4] */
     const float *conv_w_v; /* [H*dv, 4] */
     const float *norm_w;   /* [dv] or NULL for ones */
+    float qkv_scale[3];    /* FP8 activations: q, k, v = E4M3 value * scale
+                            * (each finite and > 0, else KDA_ERR_SHAPE);
+                            * ignored for other activation dtypes */
 } kda_params;
 
 /* Text of a return code (host, static storage). */

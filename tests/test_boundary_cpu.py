@@ -54,6 +54,8 @@ def test_sizes(lib):
     assert kda.state_bytes(shape(state="bf16"), 256) == 256 * 32 * 128 * 128 * 2
     assert kda.conv_bytes(s, 64) == 64 * 4 * 32 * 384 * 2
     assert kda.conv_bytes(shape(act="f32"), 3) == 3 * 4 * 32 * 384 * 4
+    assert kda.conv_bytes(shape(act="fp8"), 3) == 3 * 4 * 32 * 384
+    assert kda.draft_conv_bytes(shape(act="fp8"), 16, 4) == 16 * 4 * 32 * 384
     assert kda.draft_state_bytes(s, 16, 4) == 16 * 4 * 32 * 128 * 128 * 4
     assert kda.draft_state_bytes(shape(state="bf16"), 16, 4) == 16 * 4 * 32 * 128 * 128 * 4
     assert kda.draft_conv_bytes(s, 16, 4) == 16 * 4 * 32 * 384 * 2
@@ -91,6 +93,16 @@ def test_decode_host_errors(lib):
     c.gate = 5
     assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
                           *([BOGUS] * 11), None, None) == E_DTYPE
+    c = shape(act="fp8").c()             # FP8 is an activation dtype only
+    c.state_dtype = 2
+    assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                          *([BOGUS] * 11), None, None) == E_DTYPE
+    for bad_scale in (0.0, -1.0, float("inf"), float("nan")):
+        p = _params()
+        p.qkv_scale[0] = p.qkv_scale[1] = p.qkv_scale[2] = 1.0
+        p.qkv_scale[1] = bad_scale
+        assert lib.kda_decode(ctypes.byref(shape(act="fp8").c()), ctypes.byref(p), 4, 8,
+                              *([BOGUS] * 11), None, None) == E_SHAPE, bad_scale
     for bad_inputs in (2, -1):          # neither values nor logits
         c = shape().c()
         c.gate_inputs = bad_inputs

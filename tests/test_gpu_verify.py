@@ -62,7 +62,7 @@ def check_verify_commit(case):
     assert_parity(rec_l, rec_ref, 2e-5, "verify records")
     # raw drafts are kept bit for bit
     raw = np.concatenate([case.tokens.q, case.tokens.k, case.tokens.v], axis=-1)
-    np.testing.assert_array_equal(dconv.float().cpu().numpy(), raw)
+    np.testing.assert_array_equal(dev.acts_to_numpy(dconv, case.act), raw)
     assert commit_gpu(case, ds, rec, dconv, slot_t, pos_t, case.accepted) == 0
     assert_parity(dev.read_states(ds), S_ref, tol_for(case.state), "committed states")
     win = dev.read_window(ds, case.pos0 + case.accepted)

@@ -100,6 +100,25 @@ def test_bf16_rounding_hand_values():
     assert ref.bf16(3.0) == 3.0
 
 
+def test_fp8_e4m3_rounding_matches_torch():
+    """The generator's E4M3 rounding (ties to even, subnormals below 2^-6,
+    saturation at 448) against torch's float8_e4m3fn cast, on float32
+    inputs across the whole finite range, exact ties included."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(50000) * np.exp2(rng.uniform(-12, 9, 50000))
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    vals = np.sort(vals[np.isfinite(vals) & (vals >= 0)])
+    ties = (vals[:-1] + vals[1:]) / 2.0                  # halfway between neighbours
+    x = wl.round_f32(np.concatenate([x, ties, -ties, vals, -vals]))
+    x = x[np.abs(x) <= 448.0]
+    got = wl.round_e4m3(x)
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(got, want)
+    assert wl.round_e4m3(np.array([1000.0, -460.0]))[0] == 448.0
+
+
 def test_bf16_rounding_matches_torch():
     torch = pytest.importorskip("torch")
     rng = np.random.default_rng(7)
