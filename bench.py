@@ -51,7 +51,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma list of the extra modes to run (bf16, verify, recompute, "
-                         "compact, prefill); all when empty")
+                         "compact, fp8, prefill); all when empty")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (a known byte count "
                          "for scaling the HBM byte counters)")
@@ -61,12 +61,20 @@ def parse():
 # ------------------------------------------------------------ byte models
 # Algorithmic bytes: every tensor the step must touch, counted once.
 
-def decode_bytes_per_th(dk, dv, act_b, state_b):
+def act_bytes(act):
+    """Bytes per element of q, k, v (and the ring, raw drafts) and of alpha,
+    beta, g: FP8 activations keep the gates in BF16."""
+    a = {"f32": 4, "bf16": 2, "fp8": 1}[act]
+    return a, (2 if act == "fp8" else a)
+
+
+def decode_bytes_per_th(dk, dv, act_b, state_b, gate_b=None):
     C = 2 * dk + dv
+    gate_b = act_b if gate_b is None else gate_b
     return (2 * dk * dv * state_b          # state read + write
             + C * act_b                    # raw q, k, v
-            + dk * act_b + act_b           # alpha, beta
-            + dv * act_b                   # g
+            + dk * gate_b + gate_b         # alpha, beta
+            + dv * gate_b                  # g
             + 3 * C * act_b                # conv history read (3 ring entries)
             + C * act_b                    # new ring entry
             + dv * 4)                      # y (FP32)
@@ -76,11 +84,12 @@ def per_call_bytes(H, dk, dv, rows):
     return H * (2 * dk + dv) * 4 * 4 + dv * 4 + rows * 8   # conv taps, norm_w, ids
 
 
-def verify_bytes_per_head(n, dk, dv, act_b, state_b):
+def verify_bytes_per_head(n, dk, dv, act_b, state_b, gate_b=None):
     C = 2 * dk + dv
+    gate_b = act_b if gate_b is None else gate_b
     return (dk * dv * state_b              # state read
             + n * dk * dv * 4              # FP32 records
-            + n * (C + dk + 1 + dv) * act_b  # q, k, v, alpha, beta, g
+            + n * (C * act_b + (dk + 1 + dv) * gate_b)  # q, k, v, alpha, beta, g
             + 3 * C * act_b                # conv history
             + n * C * act_b                # raw drafts kept
             + n * dv * 4)                  # y
@@ -106,14 +115,15 @@ PREFILL_MFMA_32_PER_CHUNK = 336 + 96 + 2 * 4 * 162
 PREFILL_MFMA_16_PER_CHUNK = 288
 
 
-def prefill_bytes(lens, H, dk, dv, act_b, st_b):
+def prefill_bytes(lens, H, dk, dv, act_b, st_b, gate_b=None):
     """Algorithmic HBM bytes of one prefill call from position 0: q, k, v,
     alpha, g and beta read once, y (FP32) written once, the final state and
     the ring's last three raw tokens written once per (sequence, head),
     conv taps and norm weight once."""
     T = int(np.sum(lens))
     C = 2 * dk + dv
-    per_th = (C + dk + dv) * act_b + act_b + dv * 4
+    gate_b = act_b if gate_b is None else gate_b
+    per_th = C * act_b + (dk + dv + 1) * gate_b + dv * 4
     per_sh = dk * dv * st_b + 3 * C * act_b
     return T * H * per_th + len(lens) * H * per_sh + H * C * 4 * 4 + dv * 4
 
@@ -254,11 +264,11 @@ def run_decode_mode(torch, case, K, W, layers):
     # many small pools rotate, so the replays still split into five groups
     per_graph = layers * 4 if layers <= 8 else layers
     total, per_launch, n_timed, spread = timed_loop(torch, launch, K, W, per_graph)
-    act_b = 2 if case.act == "bf16" else 4
+    act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     n_active = int(case.active.sum(axis=1).mean())
     th_per_step = n_active * H
-    bytes_launch = th_per_step * decode_bytes_per_th(dk, dv, act_b, st_b) + \
+    bytes_launch = th_per_step * decode_bytes_per_th(dk, dv, act_b, st_b, gate_b) + \
         per_call_bytes(H, dk, dv, B)
     return dict(
         workload=case.name, rows=B, active_rows=n_active, heads=H, dk=dk, dv=dv,
@@ -301,9 +311,9 @@ def run_verify_mode(torch, case, K, W, layers):
     e_r = rel_err(recs[0].cpu().numpy(), rec_ref)
     assert e_y <= 2e-5 and e_r <= 2e-5, f"verify parity failed: {e_y} {e_r}"
     total, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
-    act_b = 2 if case.act == "bf16" else 4
+    act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
-    per_head = verify_bytes_per_head(n, dk, dv, act_b, st_b)
+    per_head = verify_bytes_per_head(n, dk, dv, act_b, st_b, gate_b)
     bytes_launch = B * H * per_head + per_call_bytes(H, dk, dv, B)
 
     # commit: copies record m-1 of rows with m >= 1 (m = accepted)
@@ -364,9 +374,9 @@ def run_verify_recompute_mode(torch, case, K, W, layers):
 
     _, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
     _, c_launch, _, c_spread = timed_loop(torch, commit, K, W, layers * 2)
-    act_b = 2 if case.act == "bf16" else 4
+    act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
-    per_tok_in = (C + dk + 1 + dv) * act_b
+    per_tok_in = C * act_b + (dk + 1 + dv) * gate_b
     v_bytes = B * H * (dk * dv * st_b + n * per_tok_in + 3 * C * act_b + n * dv * 4) + \
         per_call_bytes(H, dk, dv, B)
     m = case.accepted
@@ -416,7 +426,7 @@ def run_prefill_mode(torch, case, K, W):
     assert e_y <= 2e-5 and e_s <= tol, f"prefill parity failed: {e_y} {e_s}"
     n_timed_req = max(10, K // 16)
     total, per_launch, n_timed, spread = timed_loop(torch, launch, n_timed_req, max(2, W // 8), 2)
-    act_b = 2 if case.act == "bf16" else 4
+    act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     lens = np.asarray(case.lens)
     flops = sum(H * (prefill_flops_per_chunk(64, dk) * (int(L) // 64) +
@@ -425,7 +435,7 @@ def run_prefill_mode(torch, case, K, W):
     chunks = int(sum((int(L) + 63) // 64 for L in lens)) * H
     issued = chunks * (PREFILL_MFMA_32_PER_CHUNK * 16 * 16 * 32 * 2 +
                        PREFILL_MFMA_16_PER_CHUNK * 16 * 16 * 16 * 2)
-    nbytes = prefill_bytes(lens, H, dk, dv, act_b, st_b)
+    nbytes = prefill_bytes(lens, H, dk, dv, act_b, st_b, gate_b)
     floor_s = max(flops / (MFMA_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9))
     return dict(
         workload=case.name, seq_lens=[int(x) for x in lens], heads=H, dk=dk, dv=dv,
@@ -535,6 +545,15 @@ def main():
             print(f"# decode {casec.name}", file=sys.stderr, flush=True)
             modes[f"compact_heads_decode_{st}_state"] = run_decode_mode(
                 torch, casec, args.steps, args.warmup, layers)
+    if want("fp8"):
+        casef = wl.fp8_decode()
+        print(f"# decode {casef.name}", file=sys.stderr, flush=True)
+        modes["batched_decode_fp8_act"] = run_decode_mode(torch, casef, args.steps,
+                                                          args.warmup, args.layers)
+        casefp = wl.fp8_prefill()
+        print(f"# prefill {casefp.name}", file=sys.stderr, flush=True)
+        modes["chunked_prefill_fp8_act"] = run_prefill_mode(torch, casefp, args.steps,
+                                                            args.warmup)
     if want("prefill"):
         case4 = wl.config(4)
         print(f"# prefill {case4.name}", file=sys.stderr, flush=True)

@@ -30,16 +30,22 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// OCP FP8 E4M3 (bias 7, three mantissa bits, no infinities) to FP32,
-// exactly: exponent field e > 0 gives 2^(e-7) * (1 + m/8), placed straight
-// into the FP32 fields; e = 0 gives the subnormal m * 2^-9.  The NaN code
-// (all exponent and mantissa bits set) is not a valid input.
+// OCP FP8 E4M3 (bias 7, three mantissa bits, no infinities, largest finite
+// 448) to FP32, exactly, by the matrix-core generation's conversion
+// instruction (v_cvt_f32_fp8 on byte 0).  On gfx950 it reads the OCP
+// encoding: for every finite code it gives 2^(e-7) * (1 + m/8) for an
+// exponent field e > 0 and m * 2^-9 for e = 0, and NaN for the NaN codes.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
-    const uint32_t em = byte & 0x7fu;
-    const uint32_t sign = (byte & 0x80u) << 24;
-    const float mag = em >= 8u ? __uint_as_float(((em >> 3) + 120u) << 23 | (em & 7u) << 20)
-                               : (float)em * 0.001953125f;   // m * 2^-9
-    return __uint_as_float(__float_as_uint(mag) | sign);
+    return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Four E4M3 bytes of a word to FP32 (bytes 0..3 in order), two per
+// v_cvt_pk_f32_fp8.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t word, float (&x)[4]) {
+    typedef float f2v __attribute__((ext_vector_type(2)));
+    const f2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+    const f2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+    x[0] = lo.x; x[1] = lo.y; x[2] = hi.x; x[3] = hi.y;
 }
 
 // Round to nearest even; NaN stays a quiet NaN.

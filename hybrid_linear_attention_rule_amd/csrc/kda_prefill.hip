@@ -202,10 +202,13 @@ __device__ __forceinline__ void unpack8(const Raw8<ACT>& r, bool ok, float (&x)[
         x[4] = __uint_as_float(r.u.z << 16); x[5] = __uint_as_float(r.u.z & 0xffff0000u);
         x[6] = __uint_as_float(r.u.w << 16); x[7] = __uint_as_float(r.u.w & 0xffff0000u);
     } else {
+        float lo[4], hi[4];
+        e4m3x4_to_f32(r.u.x, lo);
+        e4m3x4_to_f32(r.u.y, hi);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            x[q] = e4m3_to_f32((r.u.x >> (8 * q)) & 0xffu);
-            x[4 + q] = e4m3_to_f32((r.u.y >> (8 * q)) & 0xffu);
+            x[q] = lo[q];
+            x[4 + q] = hi[q];
         }
     }
 #pragma unroll

@@ -285,3 +285,16 @@ def compact_heads(state: str = "f32") -> Case:
     return make_decode(5, B=256, H=2, dk=128, dv=128, steps=16, act="bf16", state=state,
                        init="random", name=COMPACT_HEADS_NAME.format(state))
 
+
+def fp8_decode() -> Case:
+    """The batched-decode workload (64 rows, 32 heads, 32 steps, FP32 state)
+    with FP8 E4M3 q, k, v and BF16 gates."""
+    return make_decode(1, B=64, H=32, dk=128, dv=128, steps=32, act="fp8", state="f32",
+                       init="random", name="batched_decode_B64_H32_d128_fp8act_f32state")
+
+
+def fp8_prefill() -> Case:
+    """The chunked-prefill workload with FP8 E4M3 q, k, v and BF16 gates."""
+    return make_prefill(4, lens=[8192, 4096, 2048, 1024], H=32, dk=128, dv=128, act="fp8",
+                        state="f32", name="chunked_prefill_lens8192_4096_2048_1024_H32_d128_C64_fp8act")
+

@@ -75,3 +75,21 @@ def test_conv_history_roundtrip_fp8():
     kda.conv_read(ds.shape, ring2, ds.slot_ids, pos, win2)
     torch.cuda.synchronize()
     assert torch.equal(win.view(torch.uint8), win2.view(torch.uint8))
+
+
+def test_every_finite_e4m3_code_decodes_exactly():
+    """q, k and v built from all 254 finite E4M3 codes (subnormals, 448 and
+    both signs included), shuffled over a decode workload: the kernels'
+    conversion of every code matches the oracle run on the codes' values."""
+    torch = need_gpu()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    vals = codes.float().numpy().astype(np.float64)
+    vals = vals[np.isfinite(vals)] * wl.FP8_SCALE
+    assert len(vals) == 254
+    case = wl.make_decode(96, B=4, H=2, dk=128, dv=128, steps=3, act="fp8", state="f32",
+                          init="random", name="decode_fp8_all_codes")
+    rng = np.random.default_rng(96)
+    for name in ("q", "k", "v"):
+        arr = getattr(case.tokens, name)
+        arr[...] = rng.permutation(np.resize(vals, arr.size)).reshape(arr.shape)
+    check_decode(case)
