@@ -495,7 +495,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     const int n = lane & 15, g = lane >> 4;
     const int tb = 16 * wave + 4 * g;          // this lane's sub-block (step 1)
     const int c0 = 8 * n;                      // and channels
-    const int h = it.h, t0 = it.t0, L = it.L;
+    const int h = it.h, L = it.L;
     const SeqView v = it.v;
     char* ws = static_cast<char*>(a.workspace) + ((size_t)chunk_slot(v.lo, it.s, it.cc) * H + h) * WS_B;
     ChunkItem nx;
