@@ -51,6 +51,12 @@
  *     so every call can be captured in a HIP graph and replayed with those
  *     buffers rewritten in place.
  *
+ * Dtypes: the state is FP32 or BF16; q, k, v, the ring and the raw draft
+ * tokens are in the activation dtype (FP32, BF16, or FP8 E4M3 with
+ * per-tensor scales); alpha, beta and g are in the activation dtype, BF16
+ * when it is FP8; y, the draft records and the conv and norm weights are
+ * FP32.
+ *
  * Layouts (row-major, contiguous):
  *   C = 2*dk + dv, the raw channels of one head in the order q | k | v.
  *   state pool   [num_slots, H, dk, dv]   state dtype, S[i][j] with i the key
@@ -197,7 +203,8 @@ int kda_conv_read(const kda_shape *shape, const void *ring, int64_t num_slots,
  *   positions [batch] int32: tokens row b has consumed.  0 means a fresh
  *            sequence: zero state and empty history, pool and ring not read.
  *            The library never writes positions; the caller advances them.
- *   q, k, alpha [batch, H, dk]; v, g [batch, H, dv]; beta [batch, H]: act.
+ *   q, k, alpha [batch, H, dk]; v, g [batch, H, dv]; beta [batch, H]: act
+ *            (with FP8 activations alpha, beta and g are BF16).
  *   pool, ring: read and written for active rows (state after the token;
  *            ring entry positions[b] mod 4 <- the raw q | k | v).
  *   y [batch, H, dv] FP32: the gated-norm output of active rows. */
@@ -214,7 +221,8 @@ int kda_decode(const kda_shape *shape, const kda_params *params,
  * records with either storage dtype ("Extend ... isolated NVFP4 Kimi K3
  * targets", Description).
  *   q, k, alpha [batch, n_draft, H, dk]; v, g [batch, n_draft, H, dv];
- *   beta [batch, n_draft, H]: act.  1 <= n_draft <= 16.
+ *   beta [batch, n_draft, H]: act (alpha, beta, g BF16 with FP8
+ *            activations).  1 <= n_draft <= 16.
  *   draft_states [batch, n_draft, H, dk, dv] FP32: the state after each
  *            draft token (never rounded, whatever the storage dtype).  May
  *            be NULL: no records are written, and the accepted prefix is
@@ -287,7 +295,7 @@ int kda_commit_recompute(const kda_shape *shape, const kda_params *params,
  *   slot_ids, positions [num_seqs]: as in kda_decode; positions > 0
  *            continue a sequence from its stored state and history.
  *   q, k, alpha [total_tokens, H, dk]; v, g [total_tokens, H, dv];
- *   beta [total_tokens, H]: act.
+ *   beta [total_tokens, H]: act (alpha, beta, g BF16 with FP8 activations).
  *   pool, ring: the final state (stored once) and the last 3 raw tokens.
  *   y [total_tokens, H, dv] FP32.
  *   workspace: device scratch of kda_prefill_workspace_bytes() bytes. */
