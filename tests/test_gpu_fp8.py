@@ -93,3 +93,16 @@ def test_every_finite_e4m3_code_decodes_exactly():
         arr = getattr(case.tokens, name)
         arr[...] = rng.permutation(np.resize(vals, arr.size)).reshape(arr.shape)
     check_decode(case)
+
+
+def test_fp8_activations_with_gate_logits():
+    """FP8 q, k, v together with BF16 gate logits, in decode and in a
+    continued prefill."""
+    need_gpu()
+    case = wl.make_decode(97, B=4, H=2, dk=128, dv=128, steps=4, act="fp8", state="bf16",
+                          init="random", gates="logits", name="decode_fp8_logits")
+    check_decode(case)
+    case = wl.make_prefill(98, lens=[90, 3, 140], H=2, dk=128, dv=128, act="fp8", state="f32",
+                           init="random", gates="logits", slice_len=32,
+                           name="prefill_fp8_logits")
+    check_prefill(case)

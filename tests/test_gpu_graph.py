@@ -1,4 +1,4 @@
-"""HIP-graph capture and replay of decode, verify and commit.
+"""HIP-graph capture and replay of decode, verify, commit and prefill.
 
 The calls read slots, positions, accepted lengths and token inputs on the
 device, so one captured call replays correctly after those buffers are
@@ -200,3 +200,63 @@ def test_records_free_verify_and_recompute_graph_replay_matches_eager():
         pos += c.accepted
     assert torch.equal(_bits(ds_g.pool), _bits(ds_e.pool))
     assert torch.equal(_bits(ds_g.ring), _bits(ds_e.ring))
+
+
+def test_prefill_graph_replay_with_new_lengths_matches_eager():
+    """kda_prefill captured once (host sizes: 3 sequences, 180 tokens,
+    lengths at most 128) and replayed with cu_seqlens, tokens and start
+    states rewritten in place: the sequence lengths change between replays
+    and every replay equals the eager call bit for bit."""
+    torch = need_gpu()
+    splits = [[100, 50, 30], [60, 90, 30], [1, 128, 51]]
+    cases = [wl.make_prefill(81 + i, lens=l, H=2, dk=128, dv=128, act="bf16", state="f32",
+                             init="random", slice_len=16, name=f"graph_prefill_{i}")
+             for i, l in enumerate(splits)]
+    for c in cases[1:]:
+        c.weights = cases[0].weights      # one layer: the captured call's weights
+    T, B, H, dv, mx = 180, 3, 2, 128, 128
+    nbytes = kda.prefill_workspace_bytes(dev.shape_of(cases[0]), B, T)
+
+    def eager(c):
+        ds = dev.make_state(c)
+        tok = dev.tokens_to_device(c.tokens, c.act)
+        y = torch.full((T, H, dv), float("nan"), device="cuda")
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        kda.prefill(ds.shape, ds.params, torch.from_numpy(c.cu_seqlens).cuda(), mx,
+                    ds.slot_ids, torch.from_numpy(c.pos0.astype(np.int32)).cuda(),
+                    *[tok[x] for x in NAMES], ds.pool, ds.ring, y, ws)
+        torch.cuda.synchronize()
+        return ds, y
+
+    outs = [eager(c) for c in cases]
+
+    ds_g = dev.make_state(cases[0])
+    tok0 = dev.tokens_to_device(cases[0].tokens, cases[0].act)
+    in_buf = {x: torch.empty_like(tok0[x]) for x in NAMES}
+    cu_buf = torch.empty(B + 1, dtype=torch.int32, device="cuda")
+    pos_buf = torch.empty(B, dtype=torch.int32, device="cuda")
+    y = torch.empty((T, H, dv), device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        kda.prefill(ds_g.shape, ds_g.params, cu_buf, mx, ds_g.slot_ids, pos_buf,
+                    *[in_buf[x] for x in NAMES], ds_g.pool, ds_g.ring, y, ws)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        start = dev.make_state(c)                     # this case's start state
+        ds_g.pool.copy_(start.pool)
+        ds_g.ring.copy_(start.ring)
+        tok = dev.tokens_to_device(c.tokens, c.act)
+        for x in NAMES:
+            in_buf[x].copy_(tok[x])
+        cu_buf.copy_(torch.from_numpy(c.cu_seqlens))
+        pos_buf.copy_(torch.from_numpy(c.pos0.astype(np.int32)))
+        y.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        ds_e, y_e = outs[i]
+        assert torch.equal(_bits(y), _bits(y_e)), f"replay {i}: y differs"
+        assert torch.equal(_bits(ds_g.pool), _bits(ds_e.pool)), f"replay {i}: states differ"
+        assert torch.equal(_bits(ds_g.ring), _bits(ds_e.ring)), f"replay {i}: ring differs"
