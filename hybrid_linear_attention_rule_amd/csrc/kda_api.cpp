@@ -35,6 +35,9 @@ int check_shape(const kda_shape* s) {
     if (!(s->l2_eps >= 0.0f) || !(s->norm_eps >= 0.0f)) return KDA_ERR_SHAPE;
     if (!((s->head_k == 64 && s->head_v == 64) || (s->head_k == 128 && s->head_v == 128)))
         return KDA_ERR_UNSUPPORTED;
+    const int64_t w = (int64_t)s->num_heads * s->head_k;      // == H * head_v
+    for (int32_t rs : {s->qkv_row_stride, s->g_row_stride})
+        if (rs != 0 && (rs < w || rs % 8 != 0)) return KDA_ERR_SHAPE;
     return KDA_OK;
 }
 
@@ -45,6 +48,13 @@ int check_params(const kda_params* p, const kda_shape* s) {
         for (int i = 0; i < 3; ++i)
             if (!(p->qkv_scale[i] > 0.0f) || !(p->qkv_scale[i] < INFINITY)) return KDA_ERR_SHAPE;
     return KDA_OK;
+}
+
+// Elements between token rows of q, k, v and of g.
+void set_row_strides(const kda_shape* s, int64_t& qkv, int64_t& g) {
+    const int64_t w = (int64_t)s->num_heads * s->head_k;
+    qkv = s->qkv_row_stride ? s->qkv_row_stride : w;
+    g = s->g_row_stride ? s->g_row_stride : w;
 }
 
 // Dequantisation scales of q, k and v (1 unless the activations are FP8).
@@ -212,6 +222,7 @@ static kda::TokenArgs token_args(const kda_shape* s, const kda_params* p,
     a.gate = s->gate;
     a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
     set_scales(p, s, a.scale_q, a.scale_k, a.scale_v);
+    set_row_strides(s, a.qkv_rs, a.g_rs);
     return a;
 }
 
@@ -363,6 +374,7 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
     a.gate = s->gate;
     a.gate_logits = s->gate_inputs == KDA_GATES_LOGITS;
     set_scales(p, s, a.scale_q, a.scale_k, a.scale_v);
+    set_row_strides(s, a.qkv_rs, a.g_rs);
     return kda::launch_prefill(*s, a, stream);
 }
 

@@ -43,6 +43,7 @@ struct TokenArgs {
     int32_t gate;
     int32_t gate_logits;  // alpha, beta hold logits a, b
     float scale_q, scale_k, scale_v;  // FP8 activations: dequantisation scales
+    int64_t qkv_rs, g_rs;             // elements between token rows of q|k|v and of g
 };
 
 struct CommitArgs {
@@ -102,6 +103,7 @@ struct PrefillArgs {
     int32_t gate;
     int32_t gate_logits;  // alpha, beta hold logits a, b
     float scale_q, scale_k, scale_v;  // FP8 activations: dequantisation scales
+    int64_t qkv_rs, g_rs;             // elements between token rows of q|k|v and of g
 };
 
 enum class TokenMode { Decode, Verify, Recompute };

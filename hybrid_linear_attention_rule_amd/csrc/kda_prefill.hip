@@ -230,7 +230,7 @@ __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v
     const bool in_seq = gt >= 0;
     ok = lt < L && (in_seq || p >= 0);
     const bool use_ring = ok && !in_seq;
-    const int64_t idx_in = ((int64_t)(v.lo + (ok && in_seq ? gt : t0)) * a.H + h) * PD + ch0;
+    const int64_t idx_in = (int64_t)(v.lo + (ok && in_seq ? gt : t0)) * a.qkv_rs + h * PD + ch0;
     const int64_t idx_ring =
         (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * a.H + h) * (3 * PD) + ring_ch0;
     return ld_raw8<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in);
@@ -377,7 +377,7 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
         // first token, head and channels), so the addressing is scalar.
         constexpr int GACT = kGateAct<ACT>;
         constexpr size_t ESZ = kActSize<ACT>, GESZ = kActSize<GACT>;
-        const size_t row_b = (size_t)a.H * PD * ESZ;             // bytes per q|k|v token row
+        const size_t row_b = (size_t)a.qkv_rs * ESZ;             // bytes per q|k|v token row
         const size_t rowa_b = (size_t)a.H * PD * GESZ;           // bytes per alpha token row
         const int64_t row0 = (int64_t)it.v.lo + t0 - 3;          // token of conv tap 0, lane 0
         const uint32_t off = (uint32_t)((size_t)tb * row_b + ((size_t)h * PD + c0) * ESZ);
@@ -1561,7 +1561,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             for (int ch = tid; ch < C; ch += kStateThreads) {
                 const void* src = ch < PD ? a.q : (ch < 2 * PD ? a.k : a.v);
                 st_act_bits<ACT>(a.ring, dst + ch,
-                                 ld_act_bits<ACT>(src, (row * H + h) * PD + (ch % PD)));
+                                 ld_act_bits<ACT>(src, row * a.qkv_rs + h * PD + (ch % PD)));
             }
         }
     }
@@ -1582,16 +1582,17 @@ __global__ __launch_bounds__(256) void prefill_finish_kernel(PrefillArgs a) {
     const bool in = h_raw < a.H;
     const int h = in ? h_raw : a.H - 1;
     const int64_t row = token * a.H + h;
+    const int64_t grow = token * a.g_rs + (int64_t)h * PD;      // g of (token, head)
     float* y = a.y + row * PD + 4 * l32;
     const float4 o = *reinterpret_cast<const float4*>(y);
     float gv[4];
     if constexpr (kGateAct<ACT> == kF32) {
         const float4 g4 =
-            *reinterpret_cast<const float4*>(static_cast<const float*>(a.g) + row * PD + 4 * l32);
+            *reinterpret_cast<const float4*>(static_cast<const float*>(a.g) + grow + 4 * l32);
         gv[0] = g4.x; gv[1] = g4.y; gv[2] = g4.z; gv[3] = g4.w;
     } else {
         const uint2 g2 =
-            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.g) + row * PD + 4 * l32);
+            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.g) + grow + 4 * l32);
         gv[0] = __uint_as_float(g2.x << 16); gv[1] = __uint_as_float(g2.x & 0xffff0000u);
         gv[2] = __uint_as_float(g2.y << 16); gv[3] = __uint_as_float(g2.y & 0xffff0000u);
     }

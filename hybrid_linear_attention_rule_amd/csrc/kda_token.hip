@@ -166,7 +166,7 @@ __device__ __forceinline__ void store_record(float* rec, int r, int c,
 // The raw token is copied to the ring (decode: entry pos mod 4) or to
 // draft_conv (verify; skipped when draft_conv is NULL).  Also loads alpha, beta and g, writes the conv of v to
 // LDS and the per-wave partial sums of |c_q|^2, |c_k|^2 and c_q . c_k.
-template <int DK, int DV, int ACT, int MODE, class Issue>
+template <int DK, int DV, int ACT, int MODE, bool STRIDED, class Issue>
 __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
                                         int slot, int pos, float4 w4a, float4 w4b,
                                         float* vt_s, float (*red_s)[4], float& ca,
@@ -193,8 +193,11 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
     // channel discard the value
     const float al_ld = ld_act<GACT>(static_cast<const char*>(a.alpha) +
                                          (size_t)(tok * H + h) * DK * GESZ, qk ? tid : 0);
-    const float g_ld = ld_act<GACT>(static_cast<const char*>(a.g) +
-                                        (size_t)(tok * H + h) * DV * GESZ, tid < DV ? tid : 0);
+    // token rows of q, k, v and g: contiguous [rows, H, d], or (STRIDED)
+    // a.qkv_rs / a.g_rs elements apart
+    const size_t g_off = STRIDED ? (size_t)(tok * a.g_rs + h * DV) : (size_t)(tok * H + h) * DV;
+    const float g_ld = ld_act<GACT>(static_cast<const char*>(a.g) + g_off * GESZ,
+                                    tid < DV ? tid : 0);
     beta = ld_act<GACT>(a.beta, tok * H + h);
     al = qk ? al_ld : 0.f;
     if (a.gate_logits) {
@@ -215,9 +218,15 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
             const char* pb;
             if (rel >= 0) {
                 const int64_t row = (int64_t)b * n + rel;
-                pa = qk ? qb + (size_t)(row * H + h) * DK * ESZ
-                        : vb + (size_t)(row * H + h) * DV * ESZ;
-                pb = kb + (size_t)(row * H + h) * DK * ESZ;
+                if constexpr (STRIDED) {
+                    pa = qk ? qb + (size_t)(row * a.qkv_rs + h * DK) * ESZ
+                            : vb + (size_t)(row * a.qkv_rs + h * DV) * ESZ;
+                    pb = kb + (size_t)(row * a.qkv_rs + h * DK) * ESZ;
+                } else {
+                    pa = qk ? qb + (size_t)(row * H + h) * DK * ESZ
+                            : vb + (size_t)(row * H + h) * DV * ESZ;
+                    pb = kb + (size_t)(row * H + h) * DK * ESZ;
+                }
             } else {
                 const char* e = ringb +
                     ((size_t)(ring_slot + ((pos + rel) & (kConvW - 1))) * H + h) * C * ESZ;
@@ -277,7 +286,7 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
     }
 }
 
-template <int DK, int DV, int ACT, int ST, int MODE>
+template <int DK, int DV, int ACT, int ST, int MODE, bool STRIDED>
 __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     constexpr int VEC = (ST == kF32) ? 4 : 8;
     using M = TileMap<DK, DV, VEC>;
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
     // phase B overlap the state loads, and the unpack waits for them
     uint4 raw[RPT];
     float ca, cb, al, beta, gv;
-    phase_a<DK, DV, ACT, MODE>(a, b, h, 0, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
+    phase_a<DK, DV, ACT, MODE, STRIDED>(a, b, h, 0, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb, al,
                                  beta, gv,
                                  [&] { load_state_raw<ST, DV, RPT, VEC>(pool_head, r, c, raw); });
     // A decode call with BF16 storage keeps the state packed as loaded and
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
         const int64_t tok = (int64_t)b * stride + t;   // row of the inputs
         // ---------------- A. conv, raw copy, norm partial sums -----------
         if (t > 0)
-            phase_a<DK, DV, ACT, MODE>(a, b, h, t, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
+            phase_a<DK, DV, ACT, MODE, STRIDED>(a, b, h, t, stride, slot, pos, w4a, w4b, vt_s, red_s, ca, cb,
                                          al, beta, gv, [] {});
         __syncthreads();
 
@@ -573,16 +582,30 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     }
 }
 
-template <int DK, int DV, int ACT, int ST>
-static int launch_token_t(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
+template <int DK, int DV, int ACT, int ST, bool STRIDED>
+static void launch_token_s(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
     const dim3 grid((unsigned)batch * (unsigned)a.H), block(DK * DV / 32);
     if (mode == kModeVerify)
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeVerify>), grid, block, 0, stream, a);
-    else if (mode == kModeRecompute)
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeRecompute>), grid, block, 0,
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeVerify, STRIDED>), grid, block, 0,
                            stream, a);
+    else if (mode == kModeRecompute)
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeRecompute, STRIDED>), grid, block,
+                           0, stream, a);
     else
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeDecode>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeDecode, STRIDED>), grid, block, 0,
+                           stream, a);
+}
+
+// Contiguous inputs take the instantiation whose addressing has no row
+// strides; inputs with a row stride other than the contiguous one take the
+// strided one.
+template <int DK, int DV, int ACT, int ST>
+static int launch_token_t(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
+    const int64_t w = (int64_t)a.H * DK;
+    if (a.qkv_rs == w && a.g_rs == w)
+        launch_token_s<DK, DV, ACT, ST, false>(a, batch, mode, stream);
+    else
+        launch_token_s<DK, DV, ACT, ST, true>(a, batch, mode, stream);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -41,7 +41,8 @@ class _Shape(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
                 ("gate", ctypes.c_int32), ("q_scale", ctypes.c_float),
                 ("l2_eps", ctypes.c_float), ("norm_eps", ctypes.c_float),
-                ("gate_inputs", ctypes.c_int32)]
+                ("gate_inputs", ctypes.c_int32), ("qkv_row_stride", ctypes.c_int32),
+                ("g_row_stride", ctypes.c_int32)]
 
 
 class _Params(ctypes.Structure):
@@ -120,15 +121,34 @@ def _expect(t, numel, dtype, name):
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
 
 
+def _expect_rows(t, lead, H, d, dtype, rs, name):
+    """A [.., H, d] device tensor whose `lead` token rows start rs elements
+    apart (rs = 0: contiguous, H*d), as the kernels index it."""
+    if rs == 0:
+        return _expect(t, lead * H * d, dtype, name)
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.dtype != dtype or t.dim() < 3 or tuple(t.shape[-2:]) != (H, d):
+        raise ValueError(f"{name}: expected a {dtype} device tensor [.., {H}, {d}]")
+    want, step = [], rs
+    for n in reversed(t.shape[:-2]):
+        want.append(step)
+        step *= n
+    if (t.stride(-1), t.stride(-2)) != (1, d) or tuple(t.stride()[:-2]) != tuple(reversed(want)) \
+            or t.numel() != lead * H * d:
+        raise ValueError(f"{name}: token rows must be {rs} elements apart, heads {d}, "
+                         f"channels contiguous (strides {tuple(t.stride())})")
+
+
 def _check_tokens(shape, lead, q, k, v, alpha, beta, g):
     H, dk, dv, a = shape.num_heads, shape.head_k, shape.head_v, shape.act_dtype
     ga = shape.gate_dtype
-    _expect(q, lead * H * dk, a, "q")
-    _expect(k, lead * H * dk, a, "k")
-    _expect(v, lead * H * dv, a, "v")
+    _expect_rows(q, lead, H, dk, a, shape.qkv_row_stride, "q")
+    _expect_rows(k, lead, H, dk, a, shape.qkv_row_stride, "k")
+    _expect_rows(v, lead, H, dv, a, shape.qkv_row_stride, "v")
     _expect(alpha, lead * H * dk, ga, "alpha")
     _expect(beta, lead * H, ga, "beta")
-    _expect(g, lead * H * dv, ga, "g")
+    _expect_rows(g, lead, H, dv, ga, shape.g_row_stride, "g")
 
 
 def _check_pool_ring(shape, pool, ring):
@@ -165,11 +185,14 @@ class KdaShape:
     norm_eps: float = 1e-6
     conv_width: int = 4
     gate_inputs: int = GATES_VALUES
+    qkv_row_stride: int = 0   # elements between token rows of q, k, v; 0 = contiguous
+    g_row_stride: int = 0     # the same for g
 
     def c(self) -> _Shape:
         return _Shape(self.num_heads, self.head_k, self.head_v, self.conv_width,
                       _DT[self.act], _DT[self.state], self.gate, self.q_scale,
-                      self.l2_eps, self.norm_eps, self.gate_inputs)
+                      self.l2_eps, self.norm_eps, self.gate_inputs, self.qkv_row_stride,
+                      self.g_row_stride)
 
     @property
     def channels(self) -> int:

@@ -57,7 +57,8 @@
  * when it is FP8; y, the draft records and the conv and norm weights are
  * FP32.
  *
- * Layouts (row-major, contiguous):
+ * Layouts (row-major; q, k, v and g may have a token-row stride, see
+ * kda_shape; everything else is contiguous):
  *   C = 2*dk + dv, the raw channels of one head in the order q | k | v.
  *   state pool   [num_slots, H, dk, dv]   state dtype, S[i][j] with i the key
  *                                          channel (dv contiguous)
@@ -129,6 +130,12 @@ typedef struct {
     float l2_eps;        /* epsilon of the q/k L2 norms */
     float norm_eps;      /* epsilon of the gated RMSNorm */
     int32_t gate_inputs; /* kda_gate_inputs of the alpha and beta buffers */
+    int32_t qkv_row_stride; /* elements from one token row of q (k, v) to the
+                             * next; 0 = contiguous (H*dk).  Lets q, k and v be
+                             * column ranges of one packed projection output,
+                             * e.g. [tokens, H*(2dk+dv)].  Else >= H*dk and a
+                             * multiple of 8 (KDA_ERR_SHAPE). */
+    int32_t g_row_stride;   /* the same for g (0 = contiguous, H*dv) */
 } kda_shape;
 
 /* Host struct of the layer's parameters: device pointers to the weights,

@@ -103,6 +103,12 @@ def test_decode_host_errors(lib):
         p.qkv_scale[1] = bad_scale
         assert lib.kda_decode(ctypes.byref(shape(act="fp8").c()), ctypes.byref(p), 4, 8,
                               *([BOGUS] * 11), None, None) == E_SHAPE, bad_scale
+    for field, bad in (("qkv_row_stride", 4096 - 8), ("qkv_row_stride", 4096 + 4),
+                       ("g_row_stride", 100), ("g_row_stride", -8)):
+        c = shape().c()                  # H*dk = 4096: below it, or not a multiple of 8
+        setattr(c, field, bad)
+        assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                              *([BOGUS] * 11), None, None) == E_SHAPE, (field, bad)
     for bad_inputs in (2, -1):          # neither values nor logits
         c = shape().c()
         c.gate_inputs = bad_inputs
