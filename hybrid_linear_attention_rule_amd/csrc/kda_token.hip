@@ -153,7 +153,6 @@ __device__ __forceinline__ void store_record(float* rec, int r, int c,
                                  __float_as_uint(s[p][e + 2]), __float_as_uint(s[p][e + 3])));
 }
 
-
 // Phase A of a token.  Conv roles, one per wave (dk and dv are multiples of
 // the wave size): waves covering threads t < DK convolve q channel t (A) and
 // k channel t (B); waves covering DK <= t < DK + DV convolve v channel t - DK
@@ -163,9 +162,12 @@ __device__ __forceinline__ void store_record(float* rec, int r, int c,
 // wave-uniform (a scalar base plus a 32-bit lane offset), and every load is
 // issued before any loaded value is used, so no wait for one tap stalls the
 // others or the state stream; taps before position 0 are zeroed afterwards.
-// The raw token is copied to the ring (decode: entry pos mod 4) or to
-// draft_conv (verify; skipped when draft_conv is NULL).  Also loads alpha, beta and g, writes the conv of v to
-// LDS and the per-wave partial sums of |c_q|^2, |c_k|^2 and c_q . c_k.
+// The raw token is copied to the ring (decode and recompute: entry
+// (pos + t) mod 4) or to draft_conv (verify; skipped when draft_conv is
+// NULL).  Also loads alpha, beta and g (forming them from their logits when
+// asked), writes the conv of v to LDS and the per-wave partial sums of
+// |c_q|^2, |c_k|^2 and c_q . c_k.  `n` is the number of input rows per batch
+// row (1 for decode, the draft count otherwise).
 template <int DK, int DV, int ACT, int MODE, bool STRIDED, class Issue>
 __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t, int n,
                                         int slot, int pos, float4 w4a, float4 w4b,
