@@ -558,21 +558,38 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     const size_t head_elems = (size_t)DV * DK;
     const float* rec = a.records + (((size_t)b * a.n + (m - 1)) * H + h) * head_elems;
     const size_t head_off = ((size_t)slot * H + h) * head_elems;
+    // every 16-byte word of the thread's share of the record is requested
+    // before any is stored (the record and the pool are distinct buffers),
+    // so the copy streams instead of waiting once per word
+    constexpr int kThreads = 256;
     if constexpr (ST == kF32) {
-        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(a.pool) + head_off);
-        const float4* src = reinterpret_cast<const float4*>(rec);
-        for (int i = tid; i < (int)(head_elems / 4); i += blockDim.x) dst[i] = src[i];
+        constexpr int kWords = DK * DV / 4 / kThreads;
+        char* dst = static_cast<char*>(a.pool) + head_off * 4;
+        const char* src = reinterpret_cast<const char*>(rec);
+        uint4 w[kWords];
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) w[q] = ld_stream(src + (size_t)(tid + q * kThreads) * 16);
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) st_stream(dst + (size_t)(tid + q * kThreads) * 16, w[q]);
     } else {
-        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.pool) + head_off);
-        const float4* src = reinterpret_cast<const float4*>(rec);
-        for (int i = tid; i < (int)(head_elems / 8); i += blockDim.x) {
-            const float4 x0 = src[2 * i], x1 = src[2 * i + 1];
+        constexpr int kWords = DK * DV / 8 / kThreads;     // bf16 words out, two FP32 words in
+        char* dst = static_cast<char*>(a.pool) + head_off * 2;
+        const char* src = reinterpret_cast<const char*>(rec);
+        uint4 x[2 * kWords];
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) {
+            x[2 * q] = ld_stream(src + (size_t)(tid + q * kThreads) * 32);
+            x[2 * q + 1] = ld_stream(src + (size_t)(tid + q * kThreads) * 32 + 16);
+        }
+#pragma unroll
+        for (int q = 0; q < kWords; ++q) {
+            const uint4 x0 = x[2 * q], x1 = x[2 * q + 1];
             uint4 o;
-            o.x = f32_to_bf16_rne(x0.x) | (f32_to_bf16_rne(x0.y) << 16);
-            o.y = f32_to_bf16_rne(x0.z) | (f32_to_bf16_rne(x0.w) << 16);
-            o.z = f32_to_bf16_rne(x1.x) | (f32_to_bf16_rne(x1.y) << 16);
-            o.w = f32_to_bf16_rne(x1.z) | (f32_to_bf16_rne(x1.w) << 16);
-            dst[i] = o;
+            o.x = pack_bf16x2(__uint_as_float(x0.x), __uint_as_float(x0.y));
+            o.y = pack_bf16x2(__uint_as_float(x0.z), __uint_as_float(x0.w));
+            o.z = pack_bf16x2(__uint_as_float(x1.x), __uint_as_float(x1.y));
+            o.w = pack_bf16x2(__uint_as_float(x1.z), __uint_as_float(x1.w));
+            st_stream(dst + (size_t)(tid + q * kThreads) * 16, o);
         }
     }
     const int first = m > kConvW ? m - kConvW : 0;
