@@ -190,9 +190,24 @@ __device__ __forceinline__ Raw8<ACT> ld_raw8_at(const char* base, uint32_t off) 
     return r;
 }
 
-// Widens to FP32; zero where !ok.
+// Zero unless ok, selected on the raw words.
 template <int ACT>
-__device__ __forceinline__ void unpack8(const Raw8<ACT>& r, bool ok, float (&x)[8]) {
+__device__ __forceinline__ Raw8<ACT> keep_if(const Raw8<ACT>& r, bool ok) {
+    Raw8<ACT> o;
+    if constexpr (ACT == kF32) {
+        o.a = make_float4(ok ? r.a.x : 0.f, ok ? r.a.y : 0.f, ok ? r.a.z : 0.f, ok ? r.a.w : 0.f);
+        o.b = make_float4(ok ? r.b.x : 0.f, ok ? r.b.y : 0.f, ok ? r.b.z : 0.f, ok ? r.b.w : 0.f);
+    } else if constexpr (ACT == kBF16) {
+        o.u = make_uint4(ok ? r.u.x : 0u, ok ? r.u.y : 0u, ok ? r.u.z : 0u, ok ? r.u.w : 0u);
+    } else {
+        o.u = make_uint2(ok ? r.u.x : 0u, ok ? r.u.y : 0u);
+    }
+    return o;
+}
+
+// Widens to FP32.
+template <int ACT>
+__device__ __forceinline__ void unpack8(const Raw8<ACT>& r, float (&x)[8]) {
     if constexpr (ACT == kF32) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
         x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
@@ -211,16 +226,14 @@ __device__ __forceinline__ void unpack8(const Raw8<ACT>& r, bool ok, float (&x)[
             x[4 + q] = hi[q];
         }
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) x[q] = ok ? x[q] : 0.f;
 }
 
 // Raw channels [ch0, ch0 + 8) of one of q|k|v for local chunk token lt
 // (-3 <= lt < 64): the packed input inside the sequence, the ring for
-// earlier positions >= 0, zero before position 0 and past the chunk's end
-// (`ok` false).  Branch-free: the load always goes to a valid address (the
-// chunk's first token when the value is zero), so all of a lane's loads are
-// in flight together.
+// earlier positions >= 0; `ok` is false before position 0 and past the
+// chunk's end, where the value must count as zero.  Branch-free: the load
+// always goes to a valid address (the chunk's first token where `ok` is
+// false), so all of a lane's loads are in flight together.
 template <int ACT>
 __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v, int h, int t0,
                                           int L, int lt, const void* src, int ch0, int ring_ch0,
@@ -239,14 +252,17 @@ __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v
 // Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
 // [c0, c0 + 8), from the seven raw tokens tb-3..tb+3 and the channels' four
 // taps; zero for tokens at or past L.  FP8 activations: times the tensor's
-// dequantisation scale `sc`, taken out of the sum.
+// dequantisation scale `sc`, taken out of the sum.  Only the three raw
+// tokens before tb can lie before position 0 and must read as zero (`ok`);
+// a later raw token past the chunk's end feeds only outputs at or past L,
+// which are zeroed here whatever it holds.
 template <int ACT>
-__device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[7],
+__device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[3],
                                         const float4 (&wt)[8], int tb, int L, float sc,
                                         float (&c)[4][8]) {
     float x[7][8];
 #pragma unroll
-    for (int m = 0; m < 7; ++m) unpack8<ACT>(r[m], ok[m], x[m]);
+    for (int m = 0; m < 7; ++m) unpack8<ACT>(m < 3 ? keep_if<ACT>(r[m], ok[m]) : r[m], x[m]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const float4 w4 = wt[q];
@@ -364,7 +380,7 @@ struct ChunkIn {
     Raw8<ACT> rq[7], rk[7], rv[7];
     Raw8<kGateAct<ACT>> ra[4];
     uint32_t rb[4];                  // bits, widened where used (no wait here)
-    bool okm[7];
+    bool okm[3];                     // raw tokens tb-3..tb-1 lie at position >= 0
 };
 
 template <int ACT>
@@ -391,7 +407,7 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
             in.rq[m] = ld_raw8_at<ACT>(qb + m * row_b, off);
             in.rk[m] = ld_raw8_at<ACT>(kb + m * row_b, off);
             in.rv[m] = ld_raw8_at<ACT>(vb + m * row_b, off);
-            in.okm[m] = true;
+            if (m < 3) in.okm[m] = true;
         }
         const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * GESZ;
         const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * GESZ);
@@ -406,9 +422,11 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
     }
 #pragma unroll
     for (int m = 0; m < 7; ++m) {
-        in.rq[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.q, c0, c0, in.okm[m]);
-        in.rk[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, in.okm[m]);
-        in.rv[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, in.okm[m]);
+        bool ok;
+        in.rq[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.q, c0, c0, ok);
+        in.rk[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, ok);
+        in.rv[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, ok);
+        if (m < 3) in.okm[m] = ok;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -439,6 +457,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     //   RC  kh * E4 [PC][LR]                    -> beta V transposed (step X)
     //   RD  A [PC][LS], T_bb on its diagonal blocks after step 3b
     //   RE  P [PC][LS]
+    //   (RA, RB, RC and RE hold their values times 2^12, the matrix-core
+    //   operand scale, which step 1 puts into the norm factors of q and k)
     //   RF  alpha product over each sub-block [NSB][PD]
     //   RG  step 2: per-wave suffix tables; from step 3a: prefix | suffix
     //       products over whole sub-blocks [2 NSB][PD]
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             float sq = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
-            const float r = a.q_scale / sqrtf(row16_sum(sq) + a.l2_eps);
+            const float r = (a.q_scale * kSc) / sqrtf(row16_sum(sq) + a.l2_eps);
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
@@ -522,14 +542,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             float sk = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) sk = fmaf(kh[e][q], kh[e][q], sk);
-            const float r = 1.0f / sqrtf(row16_sum(sk) + a.l2_eps);
+            const float r = kSc / sqrtf(row16_sum(sk) + a.l2_eps);
 #pragma unroll
             for (int q = 0; q < 8; ++q) kh[e][q] *= r;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool live = tb + e < L;
-            unpack8<kGateAct<ACT>>(in.ra[e], true, al[e]);
+            unpack8<kGateAct<ACT>>(in.ra[e], al[e]);
             float bv = act_from_bits<kGateAct<ACT>>(in.rb[e]);
             if (a.gate_logits) {
 #pragma unroll
@@ -588,8 +608,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             for (int ei = 0; ei < 4; ++ei)
 #pragma unroll
                 for (int et = ei; et < 4; ++et) {
-                    P4[et][ei] = pp[ip++];
-                    if (et > ei) A4[et][ei] = bt[et] * pa[ia++];
+                    P4[et][ei] = pp[ip++] * kInvSc;
+                    if (et > ei) A4[et][ei] = bt[et] * (pa[ia++] * kInvSc2);
                 }
 #pragma unroll
             for (int et = 0; et < 4; ++et) {
@@ -692,9 +712,6 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             float rk2[8], rq2[8], ck2[8];
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
-                rk[q] *= kSc;
-                rq[q] *= kSc;
-                ck[q] *= kSc;
                 const float fr = n >= 12 ? f3[q] : 1.f;
                 const float fc = n < 4 ? f1[q] : 1.f;
                 rk2[q] = rk[q] * fr;
@@ -714,7 +731,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 const bool adj = jtl - jil == 1;
                 Am[16 * wave + tl][16 * wave + n] =
                     bet[16 * wave + tl] * ((adj ? aA1[r] : aA2[r]) * kInvSc2);
-                Pm[16 * wave + tl][16 * wave + n] = (adj ? aP1[r] : aP2[r]) * kInvSc2;
+                Pm[16 * wave + tl][16 * wave + n] = (adj ? aP1[r] : aP2[r]) * kInvSc;
             } else if (jil > jtl) {
                 Am[16 * wave + tl][16 * wave + n] = 0.f;
                 Pm[16 * wave + tl][16 * wave + n] = 0.f;
@@ -753,8 +770,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                     float f = jtl >= 1 ? t0f[q] : 1.f;
                     f *= jtl >= 2 ? t1f[q] : 1.f;
                     f *= jtl >= 3 ? t2f[q] : 1.f;
-                    rk[q] *= f * kSc;
-                    rq[q] *= f * kSc;
+                    rk[q] *= f;
+                    rq[q] *= f;
                 }
                 xk[kb] = split_op(rk);
                 xq[kb] = split_op(rq);
@@ -770,7 +787,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                     ld4x2(&KE[ic][cb], &KE[ic][cb + 4], ck);
                     ld4x2(&AUX[aux_rb + ji][cb], &AUX[aux_rb + ji][cb + 4], sf);
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) ck[q] *= sf[q] * kSc;
+                    for (int q = 0; q < 8; ++q) ck[q] *= sf[q];
                     const SplitOp sck = split_op(ck);
                     A = mma3(xk[kb], sck, A);
                     P = mma3(xq[kb], sck, P);
@@ -779,7 +796,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 for (int r = 0; r < 4; ++r) {
                     const int tr = 16 * rb + 4 * g + r;
                     Am[tr][ic] = bet[tr] * (A[r] * kInvSc2);
-                    Pm[tr][ic] = P[r] * kInvSc2;
+                    Pm[tr][ic] = P[r] * kInvSc;
                 }
             }
         }
@@ -837,8 +854,6 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
             float xp[8];
             ld4x2(&Pm[t][cb], &Pm[t][cb + 16], xp);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) xp[q] *= kSc;
             st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(xp));
         }
     } else {
@@ -857,7 +872,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
             ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q] * kSc;
+            for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q];
             st_frag(ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B, lane, split_op(x));
         }
 #pragma unroll
@@ -869,7 +884,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int ts = 32 * kb + kslot(g, q);
-                x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c] * kSc;
+                x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c];
             }
             st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
         }
@@ -901,10 +916,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 make_float4(bq[t4][0] * kd[t4][0] * pre[t4], bq[t4][1] * kd[t4][1] * pre[t4],
                             bq[t4][2] * kd[t4][2] * pre[t4], bq[t4][3] * kd[t4][3] * pre[t4]);
         }
+        float bs[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bs[e] = bt[e] * kSc;
 #pragma unroll
         for (int q = 0; q < 8; ++q)
             *reinterpret_cast<float4*>(&VT[swz(c0 + q, tb)]) =
-                make_float4(bt[0] * cv[0][q], bt[1] * cv[1][q], bt[2] * cv[2][q], bt[3] * cv[3][q]);
+                make_float4(bs[0] * cv[0][q], bs[1] * cv[1][q], bs[2] * cv[2][q], bs[3] * cv[3][q]);
     }
     lds_sync();
 
@@ -925,7 +943,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = 16 * ((4 * wave + u) & 7) + n;
-                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]) * kSc;
+                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]);
             }
             if (b == 1) {
                 const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 + n][4 * g]);
