@@ -383,10 +383,16 @@ struct ChunkIn {
     bool okm[3];                     // raw tokens tb-3..tb-1 lie at position >= 0
 };
 
-template <int ACT>
-__device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkItem& it, int tb,
-                                              int c0, ChunkIn<ACT>& in) {
+// Part PART of a lane's raw inputs: 0 q, 1 k, 2 v with alpha and beta.  The
+// three parts are issued at three points of a step, so that the loads of
+// the workgroup's four waves pass the address units in turn instead of all
+// at once; `okm` is set by part 0.
+template <int ACT, int PART>
+__device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const ChunkItem& it, int tb,
+                                                int c0, ChunkIn<ACT>& in) {
     const int h = it.h, t0 = it.t0, L = it.L;
+    Raw8<ACT>* dst = PART == 0 ? in.rq : (PART == 1 ? in.rk : in.rv);
+    const void* src = PART == 0 ? a.q : (PART == 1 ? a.k : a.v);
     if (it.cc >= 1 && L == PC) {
         // Interior chunk: every conv token lies inside the sequence.  Each
         // load is a uniform row base plus one per-lane byte offset (lane's
@@ -394,47 +400,54 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
         constexpr int GACT = kGateAct<ACT>;
         constexpr size_t ESZ = kActSize<ACT>, GESZ = kActSize<GACT>;
         const size_t row_b = (size_t)a.qkv_rs * ESZ;             // bytes per q|k|v token row
-        const size_t rowa_b = (size_t)a.H * PD * GESZ;           // bytes per alpha token row
         const int64_t row0 = (int64_t)it.v.lo + t0 - 3;          // token of conv tap 0, lane 0
         const uint32_t off = (uint32_t)((size_t)tb * row_b + ((size_t)h * PD + c0) * ESZ);
-        const uint32_t offa = (uint32_t)((size_t)tb * rowa_b + ((size_t)h * PD + c0) * GESZ);
-        const char* qb = static_cast<const char*>(a.q) + row0 * row_b;
-        const char* kb = static_cast<const char*>(a.k) + row0 * row_b;
-        const char* vb = static_cast<const char*>(a.v) + row0 * row_b;
-        const char* ab = static_cast<const char*>(a.alpha) + (row0 + 3) * rowa_b;
+        const char* xb = static_cast<const char*>(src) + row0 * row_b;
 #pragma unroll
-        for (int m = 0; m < 7; ++m) {
-            in.rq[m] = ld_raw8_at<ACT>(qb + m * row_b, off);
-            in.rk[m] = ld_raw8_at<ACT>(kb + m * row_b, off);
-            in.rv[m] = ld_raw8_at<ACT>(vb + m * row_b, off);
-            if (m < 3) in.okm[m] = true;
+        for (int m = 0; m < 7; ++m) dst[m] = ld_raw8_at<ACT>(xb + m * row_b, off);
+        if constexpr (PART == 0) {
+#pragma unroll
+            for (int m = 0; m < 3; ++m) in.okm[m] = true;
         }
-        const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * GESZ;
-        const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * GESZ);
+        if constexpr (PART == 2) {
+            const size_t rowa_b = (size_t)a.H * PD * GESZ;       // bytes per alpha token row
+            const uint32_t offa = (uint32_t)((size_t)tb * rowa_b + ((size_t)h * PD + c0) * GESZ);
+            const char* ab = static_cast<const char*>(a.alpha) + (row0 + 3) * rowa_b;
+            const char* bb = static_cast<const char*>(a.beta) + (row0 + 3) * (int64_t)a.H * GESZ;
+            const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * GESZ);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            in.ra[e] = ld_raw8_at<GACT>(ab + e * rowa_b, offa);
-            in.rb[e] = GACT == kF32
-                ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * GESZ + offb)
-                : *reinterpret_cast<const uint16_t*>(bb + e * a.H * GESZ + offb);
+            for (int e = 0; e < 4; ++e) {
+                in.ra[e] = ld_raw8_at<GACT>(ab + e * rowa_b, offa);
+                in.rb[e] = GACT == kF32
+                    ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * GESZ + offb)
+                    : *reinterpret_cast<const uint16_t*>(bb + e * a.H * GESZ + offb);
+            }
         }
         return;
     }
 #pragma unroll
     for (int m = 0; m < 7; ++m) {
         bool ok;
-        in.rq[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.q, c0, c0, ok);
-        in.rk[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.k, c0, PD + c0, ok);
-        in.rv[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, a.v, c0, 2 * PD + c0, ok);
-        if (m < 3) in.okm[m] = ok;
+        dst[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, src, c0, PART * PD + c0, ok);
+        if (PART == 0 && m < 3) in.okm[m] = ok;
     }
+    if constexpr (PART == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
-        const int64_t row = (int64_t)(it.v.lo + t0 + min(tb + e, L - 1)) * a.H + h;
-        in.ra[e] = ld_raw8<kGateAct<ACT>>(a.alpha, row * PD + c0);
-        in.rb[e] = ld_act_bits<kGateAct<ACT>>(a.beta, row);
+        for (int e = 0; e < 4; ++e) {
+            // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
+            const int64_t row = (int64_t)(it.v.lo + t0 + min(tb + e, L - 1)) * a.H + h;
+            in.ra[e] = ld_raw8<kGateAct<ACT>>(a.alpha, row * PD + c0);
+            in.rb[e] = ld_act_bits<kGateAct<ACT>>(a.beta, row);
+        }
     }
+}
+
+template <int ACT>
+__device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkItem& it, int tb,
+                                              int c0, ChunkIn<ACT>& in) {
+    load_chunk_part<ACT, 0>(a, it, tb, c0, in);
+    load_chunk_part<ACT, 1>(a, it, tb, c0, in);
+    load_chunk_part<ACT, 2>(a, it, tb, c0, in);
 }
 
 // The conv taps of channels [c0, c0 + 8) of head h, for q, k and v.
@@ -685,10 +698,11 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     }
     lds_sync();
 
-    // The next item's inputs.  Requested here rather than right after the
-    // convolutions: by now the previous item's workspace stores have
-    // drained, and the loads still have steps 2b-5 to arrive.
-    if (nx.idx >= 0) load_chunk_in<ACT>(a, nx, tb, c0, in);
+    // The next item's inputs, in three parts over step 2b.  Requested here
+    // rather than right after the convolutions: by now the previous item's
+    // workspace stores have drained, and the loads still have steps 2b-5 to
+    // arrive.
+    if (nx.idx >= 0) load_chunk_part<ACT, 0>(a, nx, tb, c0, in);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2b. cross-sub-block entries of A and P on the matrix cores; wave w
@@ -724,6 +738,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             aA2 = mma3(split_op(rk2), sck2, aA2);
             aP2 = mma3(split_op(rq2), sck2, aP2);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tl = 4 * g + r, jtl = g, jil = n >> 2;
@@ -776,6 +793,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 xk[kb] = split_op(rk);
                 xq[kb] = split_op(rq);
             }
+            __builtin_amdgcn_sched_barrier(0);
+            if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
+            __builtin_amdgcn_sched_barrier(0);
             for (int bi = bi0; bi < bi1; ++bi) {
                 const int ic = 16 * bi + n;
                 const int ji = ic >> 2;
