@@ -80,6 +80,25 @@ def test_prefill_continues_from_stored_state_and_history():
     check_prefill(case)
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16", "fp8"])
+def test_prefill_from_positions_zero_one_two(act):
+    """Start positions 0, 1 and 2: the conv taps before position 0 count as
+    zero (the ring holds NaN there) and the later ones come from the ring;
+    lengths 1-3 also leave raw taps past the chunk's end in the same lanes."""
+    need_gpu()
+    case = wl.make_prefill(87, lens=[1, 2, 3, 70, 65, 5, 2], H=2, dk=128, dv=128, act=act,
+                           state="f32", init="random", slice_len=32,
+                           name=f"prefill_short_history_{act}")
+    case.pos0[:] = [1, 2, 1, 2, 0, 1, 0]
+    for b, p in enumerate(case.pos0):
+        if p == 0:
+            case.S0[b] = 0.0               # position 0 starts from the zero state
+        for j in range(case.width - 1):
+            if p - (case.width - 1) + j < 0:
+                case.hist0[b, j] = 0.0     # no token before position 0
+    check_prefill(case)
+
+
 def test_prefill_strong_decay_stays_finite():
     """Decays down to alpha ~ e^-12 per token: the factorised exponentials
     stay <= 1, nothing overflows."""
