@@ -845,8 +845,32 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     lds_sync();
 
     // ---- 3b. wave 0: T_bb = (I + A_bb)^-1 for the four diagonal blocks,
-    // in place (lane = block * 16 + column), then the P fragments.  Waves
-    // 1..3: scaled-Q and scaled-K fragments to the workspace.
+    // in place (lane = block * 16 + column), then the P fragments and the
+    // last scaled-Q and scaled-K fragments.  Waves 1..3: the other scaled-Q
+    // and scaled-K fragments to the workspace.
+    // (e(t,-1) * qh) rows, A operand
+    auto q_frag = [&](int f) {
+        const int tt = f >> 2, kb = f & 3;
+        const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
+        float qd[8], pr[8], x[8];
+        ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
+        ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q];
+        st_frag(ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B, lane, split_op(x));
+    };
+    // (e(last,t) * kh)^T, A operand
+    auto k_frag = [&](int f) {
+        const int ct = f & 7, kb = f >> 3;
+        const int c = 16 * ct + n;
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int ts = 32 * kb + kslot(g, q);
+            x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c];
+        }
+        st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
+    };
     if (wave == 0) {
         const int b = lane >> 4, ic = lane & 15;
         float x[16];
@@ -876,38 +900,17 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             ld4x2(&Pm[t][cb], &Pm[t][cb + 16], xp);
             st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(xp));
         }
+        q_frag(15);
+        k_frag(15);
     } else {
         // Static, unrolled loops (no branch between fragments) so that the
         // LDS reads of later fragments overlap the work of earlier ones.
-        // Wave 1 + w1 takes fragments w1, w1 + 3, ... of each kind; an index
-        // past the last fragment is clamped to it and rewrites the same
-        // bytes.
+        // Wave 1 + w1 takes fragments w1, w1 + 3, ..., w1 + 12 of each kind.
         const int w1 = wave - 1;
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {          // (e(t,-1) * qh) rows, A operand
-            const int f = min(w1 + 3 * i, 15);
-            const int tt = f >> 2, kb = f & 3;
-            const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
-            float qd[8], pr[8], x[8];
-            ld4x2(&QD[t][cb], &QD[t][cb + 16], qd);
-            ld4x2(&AUX[t >> 2][cb], &AUX[t >> 2][cb + 16], pr);
+        for (int i = 0; i < 5; ++i) q_frag(w1 + 3 * i);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) x[q] = qd[q] * pr[q];
-            st_frag(ws + (tt >> 1) * HALF_B + frag_q(tt & 1, kb) * FRAG_B, lane, split_op(x));
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {          // (e(last,t) * kh)^T, A operand
-            const int f = min(w1 + 3 * i, 15);
-            const int ct = f & 7, kb = f >> 3;
-            const int c = 16 * ct + n;
-            float x[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int ts = 32 * kb + kslot(g, q);
-                x[q] = KE[ts][c] * AUX[NSB + (ts >> 2)][c];
-            }
-            st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
-        }
+        for (int i = 0; i < 5; ++i) k_frag(w1 + 3 * i);
     }
     lds_sync();
 
