@@ -380,7 +380,7 @@ struct ChunkIn {
     Raw8<ACT> rq[7], rk[7], rv[7];
     Raw8<kGateAct<ACT>> ra[4];
     uint32_t rb[4];                  // bits, widened where used (no wait here)
-    bool okm[3];                     // raw tokens tb-3..tb-1 lie at position >= 0
+    bool okm[3];                     // raw tokens tb-3..tb-1: false where they count as zero
 };
 
 // Part PART of a lane's raw inputs: 0 q, 1 k, 2 v with alpha and beta.  The
@@ -496,8 +496,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     const int H = a.H;
 
     // Persistent: the workgroup takes items blockIdx.x, + gridDim.x, ...
-    // The next item's inputs are requested as soon as the current item's
-    // convolutions have consumed theirs, so they arrive during steps 2-5.
+    // The next item's inputs are requested in three parts during step 2b,
+    // after the current item's convolutions have consumed theirs, and arrive
+    // during steps 2b-5.
     constexpr bool kEarlyTaps = ACT != kF32;
     ChunkItem it;
     ChunkIn<ACT> in;
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, a.scale_v, cv);
 
         // every input of this item is consumed: find the next item (its
-        // inputs are requested at the start of step 2b)
+        // inputs are requested in three parts during step 2b)
         nx = next_item(a, n_slots, it.idx + gridDim.x, gridDim.x, it);
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
