@@ -24,6 +24,11 @@ MUTANTS = {
                            "hist[j * nch + ch];"),
     "norm_sum_not_mean": ("ms /= (double)dv;", "ms /= 1.0;"),
     "no_key_l2_norm": ("rk = 1.0 / sqrt(sk + cfg->l2_eps);", "rk = 1.0;"),
+    "q_scale_dropped": ("rq = cfg->q_scale / sqrt(sq + cfg->l2_eps);",
+                        "rq = 1.0 / sqrt(sq + cfg->l2_eps);"),
+    "q_scale_before_norm": ("rq = cfg->q_scale / sqrt(sq + cfg->l2_eps);",
+                            "rq = cfg->q_scale / sqrt(cfg->q_scale * "
+                            "cfg->q_scale * sq + cfg->l2_eps);"),
     "bf16_truncates": ("return ldexp(nearbyint(ldexp(f, 8)), e - 8);",
                        "return ldexp(trunc(ldexp(f, 8)), e - 8);"),
     "chunk_w_without_decay": ("exp(G[i * dk + c]) * KH[i * dk + c];",

@@ -73,6 +73,28 @@ def test_golden_hand_worked_three_tokens():
                                    atol=1e-15)
 
 
+def test_golden_query_scale():
+    gd = _read_golden("q_scale_two_tokens.txt")
+    cfg = OracleCfg(2, 2, 4, "sigmoid", float(gd["q_scale"][0]),
+                    float(gd["l2_eps"][0]), float(gd["norm_eps"][0]))
+    T = 2
+    stream = (gd["q"].reshape(T, 2), gd["k"].reshape(T, 2),
+              gd["v"].reshape(T, 2), gd["alpha"].reshape(T, 2), gd["beta"],
+              gd["g"].reshape(T, 2))
+    S, _, y, rec = _run(cfg, gd["S0"].reshape(2, 2), np.zeros((3, 6)), stream,
+                        _identity_taps(6), np.ones(2), want_records=True)
+    for t in range(T):
+        np.testing.assert_allclose(rec[t].ravel(), gd[f"S{t + 1}"],
+                                   rtol=0, atol=1e-15)
+        np.testing.assert_allclose(y[t], gd[f"y{t + 1}"], rtol=1e-14,
+                                   atol=1e-15)
+    # the chunkwise form applies the same scale
+    y_c = ref.run_one_chunked(cfg, 2, gd["S0"].reshape(2, 2).copy(),
+                              np.zeros((3, 6)), *stream,
+                              _identity_taps(6).astype(np.float64), np.ones(2))
+    np.testing.assert_allclose(y_c, y, rtol=1e-13, atol=1e-15)
+
+
 def test_golden_conv_taps():
     gd = _read_golden("conv_taps.txt")
     cfg = OracleCfg(1, 1, 4, "sigmoid", 1.0, 0.0, 0.0)
