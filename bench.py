@@ -1,22 +1,24 @@
 """Benchmark of the KDA mixer on one MI355X.
 
-The timed step is one batched decode call (conv, L2 norms, decay, delta-rule
-write, read-out, gated RMSNorm and the typed state store) over the
-batched-decode workload: 64 sequences x 32 heads, dk = dv = 128, bf16
-activations, FP32 state (64 KiB per head).  Eight independent state pools
-("layers") are rotated so the working set (1 GiB) is far larger than the
-256 MB Infinity Cache and every step streams its state from HBM.
+The timed step is one decode call (conv, L2 norms, decay, delta-rule write,
+read-out, gated RMSNorm and the typed state store) over the large-batch
+decode workload: 256 sequences x 32 heads, dk = dv = 128, bf16 activations,
+BF16 state storage (32 KiB per head), 192 of the 256 rows active per step.
+Four independent state pools ("layers", 256 MiB each) are rotated so the
+working set (1 GiB) is far larger than the 256 MB Infinity Cache and every
+step streams its state from HBM.
 
-Printed: one JSON line with the throughput (token-head state updates per
-second), the roofline of the decode kernel (algorithmic bytes per launch over
-its average launch time, HIP events on the launch stream), the CPU oracle's
-throughput on a bounded sample of the same workload, and the same figures for
-the other modes (large-batch BF16-state decode, speculative verify + commit,
-chunked prefill with its algorithmic and issued matrix-core rates).
+Printed: one JSON line with the throughput (active token-head state updates
+per second), the roofline of the decode kernel (algorithmic bytes per launch
+over its median launch time, HIP events on the launch stream), the CPU
+oracle's throughput on a bounded sample of the same workload, and the same
+figures for the other modes (batched decode with FP32 state, speculative
+verify + commit, chunked prefill with its algorithmic and issued matrix-core
+rates, two-head decode, FP8 inputs).
 
-The timed launches replay a captured HIP graph, so the host never sits
-between two kernels; the per-launch time is the replay time over the number
-of launches.
+Exactly --steps launches are timed, in five groups; each group is a captured
+HIP graph replayed once between HIP events, so the host never sits between
+two kernels.  The per-launch time is the median over the groups.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -41,16 +43,17 @@ MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, TFLOP/s
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--layers", type=int, default=8,
-                    help="state pools rotated to defeat the Infinity Cache")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="state pools of the headline workload rotated to defeat the "
+                         "Infinity Cache (4 x 256 MiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-modes", action="store_true",
                     help="time only the headline decode workload")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--only", default="",
-                    help="comma list of the extra modes to run (bf16, verify, recompute, "
+                    help="comma list of the extra modes to run (f32, verify, recompute, "
                          "compact, fp8, prefill); all when empty")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 1 GiB device copy (a known byte count "
@@ -130,24 +133,31 @@ def prefill_bytes(lens, H, dk, dv, act_b, st_b, gate_b=None):
 
 # ------------------------------------------------------------ measured traffic
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "token_kernel_batched_decode_hbm_traffic.md")
-TOKEN_KERNEL_SOURCES = ("kda_token.hip", "kda_device.h", "kda_internal.h")
+PROFILES = os.path.join(ROOT, "profiles")
+DECODE_BF16_TRAFFIC = ("token_kernel_large_batch_decode_bf16_state_hbm_traffic.md",
+                       ("kda_token.hip", "kda_device.h", "kda_internal.h"))
+DECODE_F32_TRAFFIC = ("token_kernel_batched_decode_hbm_traffic.md",
+                      ("kda_token.hip", "kda_device.h", "kda_internal.h"))
+PREFILL_TRAFFIC = ("prefill_kernels_chunked_prefill_hbm_traffic.md",
+                   ("kda_prefill.hip", "kda_mfma.h", "kda_device.h", "kda_internal.h"))
 
 
-def decode_traffic():
-    """HBM bytes per launch of the batched-decode kernel, from the rocprofv3
-    FETCH_SIZE / WRITE_SIZE runs recorded under profiles/ (scaled by the same
-    counters' reading for a 1 GiB copy).  None when the kernel's sources have
-    changed since the counters were taken."""
+def measured_traffic(which):
+    """HBM bytes per launch of a kernel (or, for the prefill, of one call's
+    kernels), from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded under
+    profiles/ (each scaled by the same counter's reading for a 1 GiB copy).
+    None when the file is missing or the kernels' sources have changed since
+    the counters were taken."""
     import hashlib
+    name, sources = which
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(os.path.join(PROFILES, name)).read()
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
                   if line.startswith(("traffic_bytes_per_launch:", "kernel_source_sha256:")))
     h = hashlib.sha256()
-    for f in TOKEN_KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "hybrid_linear_attention_rule_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     if fields.get("kernel_source_sha256", "").strip() != h.hexdigest():
@@ -157,43 +167,53 @@ def decode_traffic():
 
 # ------------------------------------------------------------ helpers
 
-def timed_loop(torch, launch, K, W, per_graph, repeats=5):
-    """Capture `per_graph` consecutive launches in one HIP graph and replay it
-    until K launches have run (after W warm-up launches outside the graph and
-    one untimed replay).  The replays are split over `repeats` timed groups,
-    each bracketed by HIP events on the launch stream with a device
-    synchronisation on both sides.  Returns (total seconds, median seconds
-    per launch over the groups, launches timed, spread)."""
+def timed_loop(torch, launch, K, W, groups=5):
+    """Time exactly K launches (at least `groups` of them, so K is raised to
+    `groups` when smaller), after W warm-up launches outside any graph.
+
+    The K launches are split into `groups` consecutive groups of K // groups
+    or K // groups + 1 launches.  Each group is captured as one HIP graph (the
+    launch index keeps counting across groups, so state pools and steps
+    rotate as in eager order) and replayed once untimed, then timed once:
+    device synchronisation, a short spin kernel that keeps the GPU busy while
+    the host queues the start event, the replay and the end event, then
+    synchronisation again.  The events sit on the launch stream.  Returns
+    (total seconds, median seconds per launch over the groups, launches
+    timed, spread)."""
+    K = max(K, groups)
     for i in range(W):
         launch(i)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(per_graph):
-            launch(W + i)
-    n_replays = max(1, (K + per_graph - 1) // per_graph)
-    repeats = min(repeats, n_replays)
-    groups = [n_replays // repeats + (1 if g < n_replays % repeats else 0)
-              for g in range(repeats)]
-    graph.replay()                       # one untimed replay
+    sizes = [K // groups + (1 if g < K % groups else 0) for g in range(groups)]
+    graphs, first = [], W
+    for n in sizes:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(first, first + n):
+                launch(i)
+        graphs.append((g, n))
+        first += n
+    for g, _ in graphs:                   # one untimed replay of each
+        g.replay()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     total, per = 0.0, []
-    for reps in groups:
+    for g, n in graphs:
         torch.cuda.synchronize()
+        torch.cuda._sleep(200000)
         t0.record()
-        for _ in range(reps):
-            graph.replay()
+        g.replay()
         t1.record()
         torch.cuda.synchronize()
         dt = t0.elapsed_time(t1) / 1e3
         total += dt
-        per.append(dt / (reps * per_graph))
+        per.append(dt / n)
     per.sort()
     med = per[len(per) // 2] if len(per) % 2 else 0.5 * (per[len(per) // 2 - 1] + per[len(per) // 2])
-    spread = {"repeats": len(per), "min_us": per[0] * 1e6, "max_us": per[-1] * 1e6}
-    return total, med, n_replays * per_graph, spread
+    spread = {"repeats": len(per), "min_us": per[0] * 1e6, "max_us": per[-1] * 1e6,
+              "launches_per_group": sizes}
+    return total, med, K, spread
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, reps=10):
@@ -260,10 +280,7 @@ def run_decode_mode(torch, case, K, W, layers):
     # restore layer 0 so that every layer starts from the same state
     pools[0] = dev.make_state(case, spare_slots=0, fill_nan=False)
 
-    # four steps per graph for the big workloads; one rotation per graph when
-    # many small pools rotate, so the replays still split into five groups
-    per_graph = layers * 4 if layers <= 8 else layers
-    total, per_launch, n_timed, spread = timed_loop(torch, launch, K, W, per_graph)
+    total, per_launch, n_timed, spread = timed_loop(torch, launch, K, W)
     act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     n_active = int(case.active.sum(axis=1).mean())
@@ -310,7 +327,7 @@ def run_verify_mode(torch, case, K, W, layers):
     e_y = rel_err(y.cpu().numpy(), y_ref)
     e_r = rel_err(recs[0].cpu().numpy(), rec_ref)
     assert e_y <= 2e-5 and e_r <= 2e-5, f"verify parity failed: {e_y} {e_r}"
-    total, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
+    total, v_launch, _, v_spread = timed_loop(torch, verify, K, W)
     act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     per_head = verify_bytes_per_head(n, dk, dv, act_b, st_b, gate_b)
@@ -321,7 +338,7 @@ def run_verify_mode(torch, case, K, W, layers):
         d = pools[i % layers]
         kda.commit_accepted(d.shape, slot_t, pos_t, acc_t, recs[0], dconv, d.pool,
                             d.ring)
-    c_total, c_launch, _, c_spread = timed_loop(torch, commit, K, W, layers * 2)
+    c_total, c_launch, _, c_spread = timed_loop(torch, commit, K, W)
     m = case.accepted
     commit_bytes = int((m > 0).sum()) * H * (dk * dv * 4 + dk * dv * st_b) + \
         int(np.minimum(m, 4).sum()) * H * 2 * C * act_b
@@ -372,8 +389,8 @@ def run_verify_recompute_mode(torch, case, K, W, layers):
     assert e_y <= 2e-5 and e_s <= tol, f"verify/recompute parity failed: {e_y} {e_s}"
     pools[0] = dev.make_state(case, spare_slots=0, fill_nan=False)
 
-    _, v_launch, _, v_spread = timed_loop(torch, verify, K, W, layers * 2)
-    _, c_launch, _, c_spread = timed_loop(torch, commit, K, W, layers * 2)
+    _, v_launch, _, v_spread = timed_loop(torch, verify, K, W)
+    _, c_launch, _, c_spread = timed_loop(torch, commit, K, W)
     act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     per_tok_in = C * act_b + (dk + 1 + dv) * gate_b
@@ -424,8 +441,7 @@ def run_prefill_mode(torch, case, K, W):
     tol = 2e-5 if case.state == "f32" else 1e-2
     e_s = rel_err(dev.read_states(ds), S_ref)
     assert e_y <= 2e-5 and e_s <= tol, f"prefill parity failed: {e_y} {e_s}"
-    n_timed_req = max(10, K // 16)
-    total, per_launch, n_timed, spread = timed_loop(torch, launch, n_timed_req, max(2, W // 8), 2)
+    total, per_launch, n_timed, spread = timed_loop(torch, launch, 10, 2)
     act_b, gate_b = act_bytes(case.act)
     st_b = 2 if case.state == "bf16" else 4
     lens = np.asarray(case.lens)
@@ -454,12 +470,31 @@ def run_prefill_mode(torch, case, K, W):
 
 # ------------------------------------------------------------ CPU oracle
 
-def cpu_baseline(case, seconds):
-    """The oracle as it stands, threaded over (sequence, head), on the same
-    workload: whole passes over its decode steps until `seconds` elapse; then
-    one pass on a single thread."""
+def cpu_info():
+    """The host's logical CPU count, the share this process may run on, and
+    the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        share = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        share = os.cpu_count() or 1
+    return os.cpu_count() or 1, share, model
+
+
+def cpu_baseline(case, seconds, max_threads=16):
+    """The oracle as it stands (fp64 C, threaded over (sequence, head)) on the
+    same workload: whole passes over its decode steps until `seconds`
+    elapse, on the host cores this process may use (at most `max_threads`,
+    one GPU's share of the host); then one pass on a single thread."""
     import oracle
-    from oracle.ref import default_threads
 
     def passes(th, secs):
         done, n = 0, 0
@@ -472,14 +507,17 @@ def cpu_baseline(case, seconds):
                 break
         return done / (time.perf_counter() - t0), n, time.perf_counter() - t0
 
-    th = default_threads()
+    nproc, share, model = cpu_info()
+    th = max(1, min(share, max_threads))
     rate, n, dt = passes(th, seconds)
     rate1, n1, dt1 = passes(1, 0.0)
     return {"value": rate, "unit": "token-head updates/s", "cores": th,
             "kind": "oracle",
             "sample": f"{n} full pass(es) of the {case.name} workload "
-                      f"({case.steps} decode steps x {case.batch} rows x {case.H} heads), "
-                      f"fp64 C oracle on {th} threads, {dt:.1f} s",
+                      f"({case.steps} decode steps, {int(case.active.sum(axis=1).mean())} "
+                      f"active of {case.batch} rows, {case.H} heads), fp64 C oracle on {th} "
+                      f"threads, {dt:.1f} s",
+            "host": {"nproc": nproc, "usable_cpus": share, "cpu_model": model},
             "single_thread": {"value": rate1, "sample": f"{n1} pass on 1 thread, {dt1:.1f} s"}}
 
 
@@ -512,21 +550,22 @@ def main():
     copy_gbs = copy_bandwidth(torch)
     print(f"# device copy of 1 GiB: {copy_gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
-    case1 = wl.config(1)
-    print(f"# decode {case1.name}: steps={args.steps} warmup={args.warmup} "
+    case3 = wl.config(3)
+    print(f"# decode {case3.name}: steps={args.steps} warmup={args.warmup} "
           f"layers={args.layers}", file=sys.stderr, flush=True)
-    head = run_decode_mode(torch, case1, args.steps, args.warmup, args.layers)
+    head = run_decode_mode(torch, case3, args.steps, args.warmup, args.layers)
     print(f"# decode kernel {head['kernel_us']:.2f} us, {head['hbm_gbs']:.0f} GB/s",
           file=sys.stderr, flush=True)
 
     modes = {}
     only = set(x for x in args.only.split(",") if x)
     want = (lambda m: not args.no_modes and (not only or m in only))
-    if want("bf16"):
-        case3 = wl.config(3)
-        print(f"# decode {case3.name}", file=sys.stderr, flush=True)
-        modes["large_batch_decode_bf16_state"] = run_decode_mode(
-            torch, case3, args.steps, args.warmup, 4)
+    if want("f32"):
+        case1 = wl.config(1)
+        print(f"# decode {case1.name}", file=sys.stderr, flush=True)
+        modes["batched_decode_f32_state"] = run_decode_mode(
+            torch, case1, args.steps, args.warmup, 8)
+        modes["batched_decode_f32_state"]["traffic"] = measured_traffic(DECODE_F32_TRAFFIC)
     if want("verify"):
         case2 = wl.config(2)
         print(f"# verify {case2.name}", file=sys.stderr, flush=True)
@@ -549,7 +588,7 @@ def main():
         casef = wl.fp8_decode()
         print(f"# decode {casef.name}", file=sys.stderr, flush=True)
         modes["batched_decode_fp8_act"] = run_decode_mode(torch, casef, args.steps,
-                                                          args.warmup, args.layers)
+                                                          args.warmup, 8)
         casefp = wl.fp8_prefill()
         print(f"# prefill {casefp.name}", file=sys.stderr, flush=True)
         modes["chunked_prefill_fp8_act"] = run_prefill_mode(torch, casefp, args.steps,
@@ -557,17 +596,19 @@ def main():
     if want("prefill"):
         case4 = wl.config(4)
         print(f"# prefill {case4.name}", file=sys.stderr, flush=True)
-        modes["chunked_prefill"] = run_prefill_mode(torch, case4, args.steps, args.warmup)
-        print(f"# prefill {modes['chunked_prefill']['prefill_us']:.1f} us",
-              file=sys.stderr, flush=True)
+        modes["chunked_prefill"] = pf = run_prefill_mode(torch, case4, args.steps, args.warmup)
+        t = measured_traffic(PREFILL_TRAFFIC)
+        pf["traffic"] = t
+        pf["traffic_over_algorithmic"] = None if t is None else t / pf["bytes_per_launch"]
+        print(f"# prefill {pf['prefill_us']:.1f} us", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
         print("# cpu oracle baseline", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(case1, args.cpu_seconds)
+        cpu = cpu_baseline(case3, args.cpu_seconds)
 
     line = {
-        "metric": "KDA decode token-head state updates/s (batched decode, 1 GPU)",
+        "metric": "KDA decode/verify token-head updates/s + achieved HBM GB/s (% peak), 1 GPU",
         "value": head["th_per_s"],
         "unit": "token-head updates/s",
         "n_gpus": 1,
@@ -578,15 +619,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
-        "data": "synthetic (seeded; distributions of the batched-decode workload)",
-        "config": {"workload": case1.name, "batch": case1.batch, "heads": case1.H,
-                   "head_k": case1.dk, "head_v": case1.dv, "act": case1.act,
-                   "state": case1.state, "state_pools_rotated": args.layers,
+        "data": "synthetic (seeded; distributions of the large-batch decode workload)",
+        "config": {"workload": case3.name, "batch": case3.batch,
+                   "active_rows_per_step": head["active_rows"], "heads": case3.H,
+                   "head_k": case3.dk, "head_v": case3.dv, "act": case3.act,
+                   "state": case3.state, "state_pools_rotated": args.layers,
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": head["hbm_gbs"],
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": head["hbm_frac"], "traffic": decode_traffic(),
-                     "kernel": "kda::token_kernel<128,128,bf16,f32,decode>",
+                     "frac": head["hbm_frac"], "traffic": measured_traffic(DECODE_BF16_TRAFFIC),
+                     "kernel": "kda::token_kernel<128,128,bf16,bf16,decode>",
                      "kernel_us": head["kernel_us"],
                      "kernel_us_spread": head["spread"],
                      "bytes_per_launch": head["bytes_per_launch"],

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include "kda.h"
 #include "kda_internal.h"
 
@@ -14,6 +16,14 @@ namespace {
 
 constexpr int kConvW = 4;
 constexpr int kMaxDraft = 16;
+
+// A launch may hold fewer than 2^32 work-items.  The per-token kernels run
+// batch * H workgroups of at most dk * dv / 32 threads, the commit kernel
+// batch * H workgroups of 256.
+bool token_grid_ok(const kda_shape* s, int32_t batch) {
+    const int64_t threads = std::max<int64_t>((int64_t)s->head_k * s->head_v / 32, 256);
+    return (int64_t)batch * s->num_heads * threads < (1LL << 32);
+}
 
 bool dtype_ok(int d) { return d == KDA_F32 || d == KDA_BF16; }
 
@@ -33,6 +43,7 @@ int check_shape(const kda_shape* s) {
     if (s->num_heads < 1 || s->head_k < 1 || s->head_v < 1) return KDA_ERR_SHAPE;
     if (s->conv_width != kConvW) return KDA_ERR_UNSUPPORTED;
     if (!(s->l2_eps >= 0.0f) || !(s->norm_eps >= 0.0f)) return KDA_ERR_SHAPE;
+    if (!(fabsf(s->q_scale) < INFINITY)) return KDA_ERR_SHAPE;   // NaN or infinite
     if (!((s->head_k == 64 && s->head_v == 64) || (s->head_k == 128 && s->head_v == 128)))
         return KDA_ERR_UNSUPPORTED;
     const int64_t w = (int64_t)s->num_heads * s->head_k;      // == H * head_v
@@ -78,7 +89,14 @@ const char* kda_status_str(int code) {
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_UNSUPPORTED: return "no kernel for these sizes";
         case KDA_ERR_HIP: return "HIP launch error";
-        default: return "unknown status code";
+        case KDA_STATUS_BAD_SLOT: return "device status: a slot id is >= num_slots";
+        case KDA_STATUS_BAD_POSITION: return "device status: a position is negative";
+        case KDA_STATUS_BAD_ACCEPTED: return "device status: an accepted length is outside [0, n_draft]";
+        case KDA_STATUS_BAD_SEQLENS: return "device status: cu_seqlens is not monotone or runs past the end";
+        case KDA_STATUS_STALLED:
+            return "device status: a prefill hand-off between waves timed out; the call's outputs are not valid";
+        default:
+            return code > 0 && code < 32 ? "device status: several bits set" : "unknown status code";
     }
 }
 
@@ -236,7 +254,7 @@ int kda_decode(const kda_shape* s, const kda_params* p, int32_t batch,
     if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (batch < 0 || num_slots < 0) return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
-    if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!token_grid_ok(s, batch)) return KDA_ERR_SHAPE;
     if (!slot_ids || !positions || !q || !k || !v || !alpha || !beta || !g || !pool ||
         !ring || !y)
         return KDA_ERR_NULL;
@@ -259,7 +277,7 @@ int kda_verify(const kda_shape* s, const kda_params* p, int32_t batch,
     if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
         return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
-    if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!token_grid_ok(s, batch)) return KDA_ERR_SHAPE;
     if (!slot_ids || !positions || !q || !k || !v || !alpha || !beta || !g || !pool ||
         !ring || !y)
         return KDA_ERR_NULL;
@@ -284,7 +302,7 @@ int kda_commit_recompute(const kda_shape* s, const kda_params* p, int32_t batch,
     if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
         return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
-    if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!token_grid_ok(s, batch)) return KDA_ERR_SHAPE;
     if (!slot_ids || !positions || !accepted || !q || !k || !v || !alpha || !beta || !g ||
         !pool || !ring)
         return KDA_ERR_NULL;
@@ -306,7 +324,7 @@ int kda_commit_accepted(const kda_shape* s, int32_t batch, int32_t n_draft,
     if (batch < 0 || num_slots < 0 || n_draft < 1 || n_draft > kMaxDraft)
         return KDA_ERR_SHAPE;
     if (batch == 0) return KDA_OK;
-    if ((int64_t)batch * s->num_heads > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    if (!token_grid_ok(s, batch)) return KDA_ERR_SHAPE;
     if (!slot_ids || !positions || !accepted || !draft_states || !draft_conv || !pool ||
         !ring)
         return KDA_ERR_NULL;
@@ -338,7 +356,8 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
     if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || num_slots < 0)
         return KDA_ERR_SHAPE;
     if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return KDA_OK;
-    if (total_tokens > 0x7fffffffLL) return KDA_ERR_SHAPE;
+    // the finish kernel runs one 256-thread workgroup per token (grid x)
+    if (total_tokens > 0x7fffffffLL || total_tokens * 256 >= (1LL << 32)) return KDA_ERR_SHAPE;
     if (!cu_seqlens || !slot_ids || !positions || !q || !k || !v || !alpha || !beta ||
         !g || !pool || !ring || !y)
         return KDA_ERR_NULL;

@@ -46,9 +46,9 @@ namespace kda {
 //                   once, ring entries of the m tokens written, no output.
 constexpr int kModeDecode = 0, kModeVerify = 1, kModeRecompute = 2;
 
-template <int DK, int DV, int VEC>
+template <int DK, int DV, int VEC, int EPT>
 struct TileMap {
-    static constexpr int NT = DK * DV / 32;    // threads per workgroup: 32 state
+    static constexpr int NT = DK * DV / EPT;   // threads per workgroup: EPT state
                                                // elements per thread
     static constexpr int LJ = DV / VEC;        // lanes along one dv row
     static constexpr int RG = NT / LJ;         // row groups
@@ -288,10 +288,10 @@ __device__ __forceinline__ void phase_a(const TokenArgs& a, int b, int h, int t,
     }
 }
 
-template <int DK, int DV, int ACT, int ST, int MODE, bool STRIDED>
-__global__ __launch_bounds__(DK * DV / 32) void token_kernel(TokenArgs a) {
+template <int DK, int DV, int ACT, int ST, int MODE, bool STRIDED, int EPT>
+__global__ __launch_bounds__(DK * DV / EPT) void token_kernel(TokenArgs a) {
     constexpr int VEC = (ST == kF32) ? 4 : 8;
-    using M = TileMap<DK, DV, VEC>;
+    using M = TileMap<DK, DV, VEC, EPT>;
     constexpr int LJ = M::LJ, RG = M::RG, RPT = M::RPT;
     constexpr int NW = M::NT / kWave;
     constexpr int PAD = 4;
@@ -601,18 +601,29 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
     }
 }
 
+// State elements per thread of a one-token decode: a 32 KiB BF16 head
+// (dk = dv = 128) is streamed by 256 threads with 128 bytes each, every other
+// case by DK * DV / 32 threads.
+#ifndef KDA_BF16_DECODE_EPT
+#define KDA_BF16_DECODE_EPT 32
+#endif
+template <int DK, int ST>
+constexpr int kDecodeEpt = (ST == kBF16 && DK == 128) ? KDA_BF16_DECODE_EPT : 32;
+
 template <int DK, int DV, int ACT, int ST, bool STRIDED>
 static void launch_token_s(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
     const dim3 grid((unsigned)batch * (unsigned)a.H), block(DK * DV / 32);
-    if (mode == kModeVerify)
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeVerify, STRIDED>), grid, block, 0,
-                           stream, a);
-    else if (mode == kModeRecompute)
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeRecompute, STRIDED>), grid, block,
+    if (mode == kModeVerify) {
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeVerify, STRIDED, 32>), grid, block,
                            0, stream, a);
-    else
-        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeDecode, STRIDED>), grid, block, 0,
-                           stream, a);
+    } else if (mode == kModeRecompute) {
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeRecompute, STRIDED, 32>), grid,
+                           block, 0, stream, a);
+    } else {
+        constexpr int EPT = kDecodeEpt<DK, ST>;
+        hipLaunchKernelGGL((token_kernel<DK, DV, ACT, ST, kModeDecode, STRIDED, EPT>), grid,
+                           dim3(DK * DV / EPT), 0, stream, a);
+    }
 }
 
 // Contiguous inputs take the instantiation whose addressing has no row

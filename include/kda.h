@@ -92,12 +92,17 @@ enum {
     KDA_ERR_HIP = -6          /* a HIP launch error */
 };
 
-/* Bits OR-ed into *status by the device. */
+/* Bits OR-ed into *status by the device.  kda_status_str() also names each
+ * single bit (a positive argument). */
 enum {
     KDA_STATUS_BAD_SLOT = 1,      /* slot id >= num_slots */
     KDA_STATUS_BAD_POSITION = 2,  /* negative position */
     KDA_STATUS_BAD_ACCEPTED = 4,  /* accepted length outside [0, n_draft] */
-    KDA_STATUS_BAD_SEQLENS = 8    /* cu_seqlens not monotone, or past end */
+    KDA_STATUS_BAD_SEQLENS = 8,   /* cu_seqlens not monotone, or past end */
+    KDA_STATUS_STALLED = 16       /* kda_prefill: a hand-off between the waves
+                                   * of a state workgroup did not arrive within
+                                   * its bounded wait; the outputs and final
+                                   * states of that call are not valid */
 };
 
 /* KDA_FP8_E4M3 is an activation dtype only: q, k, v, the conv ring and the
@@ -126,7 +131,8 @@ typedef struct {
                           * (FP8: q, k, v and the ring; alpha, beta, g BF16) */
     int32_t state_dtype; /* kda_dtype of the state pool */
     int32_t gate;        /* kda_gate of the output gate */
-    float q_scale;       /* multiplies the normalised q (1 in the usual form) */
+    float q_scale;       /* multiplies the normalised q (1 in the usual form);
+                          * any finite value, else KDA_ERR_SHAPE */
     float l2_eps;        /* epsilon of the q/k L2 norms */
     float norm_eps;      /* epsilon of the gated RMSNorm */
     int32_t gate_inputs; /* kda_gate_inputs of the alpha and beta buffers */
@@ -150,7 +156,9 @@ typedef struct {
                             * ignored for other activation dtypes */
 } kda_params;
 
-/* Text of a return code (host, static storage). */
+/* Text of a return code (zero or negative), or of one KDA_STATUS_* bit
+ * (positive; a value with several bits set gets a generic text).  Host,
+ * static storage. */
 const char *kda_status_str(int code);
 
 /* ----- sizes (host functions; 0 when the shape is invalid) ------------- */
@@ -166,7 +174,10 @@ size_t kda_draft_state_bytes(const kda_shape *shape, int32_t batch,
 size_t kda_draft_conv_bytes(const kda_shape *shape, int32_t batch,
                             int32_t n_draft);
 /* Bytes of workspace kda_prefill needs for `total_tokens` tokens in
- * `num_seqs` sequences. */
+ * `num_seqs` sequences: 147,456 bytes per (64-token chunk slot, head), with
+ * ceil(total_tokens / 64) + num_seqs chunk slots (2,304 bytes per token and
+ * head for long sequences; 1.14 GB for 15,360 tokens over 4 sequences at
+ * H = 32).  0 for head sizes the prefill does not support. */
 size_t kda_prefill_workspace_bytes(const kda_shape *shape, int32_t num_seqs,
                                    int64_t total_tokens);
 

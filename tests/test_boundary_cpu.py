@@ -67,6 +67,13 @@ def test_status_strings(lib):
     for code in (OK, E_NULL, E_SHAPE, E_DTYPE, E_WS, E_UNSUP, -6):
         assert lib.kda_status_str(code)
     assert lib.kda_status_str(123) == b"unknown status code"
+    # every device status bit has its own text; a mix gets a generic one
+    texts = {bit: lib.kda_status_str(bit) for bit in (1, 2, 4, 8, 16)}
+    assert len(set(texts.values())) == 5
+    assert b"slot" in texts[1] and b"position" in texts[2]
+    assert b"accepted" in texts[4] and b"cu_seqlens" in texts[8]
+    assert b"timed out" in texts[16] and b"not valid" in texts[16]
+    assert lib.kda_status_str(1 | 16) == b"device status: several bits set"
 
 
 def _decode(lib, sh, params, batch=4, num_slots=8, ptrs=None):
@@ -114,6 +121,14 @@ def test_decode_host_errors(lib):
         c.gate_inputs = bad_inputs
         assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
                               *([BOGUS] * 11), None, None) == E_DTYPE
+    for bad_q in (float("inf"), float("-inf"), float("nan")):
+        c = shape().c()
+        c.q_scale = bad_q
+        assert lib.kda_decode(ctypes.byref(c), ctypes.byref(_params()), 4, 8,
+                              *([BOGUS] * 11), None, None) == E_SHAPE, bad_q
+    # a launch holds fewer than 2^32 work-items: batch * H * 512 threads
+    assert _decode(lib, shape(num_heads=2048), _params(), batch=4096) == E_SHAPE
+    assert _decode(lib, shape(num_heads=1024), _params(), batch=8191, ptrs=[None] * 11) == E_NULL
     assert _decode(lib, shape(head_k=96, head_v=96), _params()) == E_UNSUP
     assert _decode(lib, shape(head_k=64, head_v=128), _params()) == E_UNSUP
     assert _decode(lib, shape(conv_width=3), _params()) == E_UNSUP
@@ -188,6 +203,8 @@ def test_prefill_host_errors(lib):
         assert prefill(ws=None, ws_bytes=0) == E_WS
         assert prefill(ws=BOGUS, ws_bytes=need - 1) == E_WS
     assert prefill(num_seqs=0, ptrs=[None] * 12) == OK
+    # one 256-thread workgroup per token: 2^24 tokens is over the launch limit
+    assert prefill(total=1 << 24, max_len=1 << 23) == E_SHAPE
 
 
 def test_state_io_host_errors(lib):
