@@ -56,15 +56,43 @@ constexpr int LR = PD + 4;         // padded LDS row of a [PC][PD] tile (floats)
 constexpr int LS = PC + 4;         // padded LDS row of a [PC][PC] tile
 constexpr int NSB = PC / 4;        // 4-token sub-blocks per chunk
 
-// Matrix-core operands bounded by 1 in magnitude (normalised keys and
-// queries times decay factors, A and P) are multiplied by 2^12 before the
-// fp16 split, T_bb and W (bounded by 256 in practice) by 2^8: the split of a
-// value below 2^-3 would otherwise lose its lo part to fp16 subnormals, about
-// 3e-8 absolute per element, which small rows of P turn into output error.
-// Products are scaled back by exact powers of two.  Values (V, Ut, U, S) are
-// split unscaled.
+// Operand scaling for the split-fp16 products.  The split of x into fp16
+// hi + lo keeps 2^-22 of |x| only while |x| < 65504 and |x| >= 2^-3; below
+// that lo falls into fp16 subnormals (about 3e-8 absolute per element).
+//   - Key-side operands bounded by 1 (normalised keys and queries times decay
+//     factors, A and P) are multiplied by 2^12 before the split, T_bb and W
+//     by 2^8.  |W| <= 1: row t of W is beta_t times the product of the
+//     earlier tokens' (I - beta k k^T) Diag(alpha) factors applied to k_t,
+//     each factor of norm at most 1.
+//   - Value-side operands (V, Ut, U and the state S) have no bound: v and
+//     the stored state may have any magnitude.  Every value column j carries
+//     a power-of-two scale 2^-e_j per chunk, with e_j the exponent of the
+//     column's largest magnitude (pow2_scale), so the split always sees values
+//     of order 1.  Every product on the value side is linear in each value
+//     column and never mixes columns, so a column's scale passes through it
+//     unchanged and is removed exactly afterwards.
+// Products are scaled back by exact powers of two.  The query scale is not
+// folded into any operand: O is linear in the normalised queries, so it
+// multiplies O once before the gated norm.
 constexpr float kSc = 4096.f, kInvSc = 1.f / 4096.f, kInvSc2 = 1.f / 16777216.f;
 constexpr float kScW = 256.f, kInvScW = 1.f / 256.f;
+
+// Power-of-two scale for a value column whose largest magnitude is m:
+// s = 2^-e with e the exponent of m, so m * s lies in [1, 2); is = 1 / s.
+// The exponent is clamped so that both stay normal FP32 numbers (m = 0 gives
+// s = 2^126, harmless on a zero column).
+__device__ __forceinline__ void pow2_scale(float m, float& s, float& is) {
+    const uint32_t ef = min(max((__float_as_uint(m) >> 23) & 0xffu, 1u), 253u);
+    s = __uint_as_float((254u - ef) << 23);
+    is = __uint_as_float(ef << 23);
+}
+
+// Largest magnitude over the 16 lanes n, n + 16, n + 32, n + 48 (one matrix
+// column); every one of them gets the result.
+__device__ __forceinline__ float col_max4(float m) {
+    m = fmaxf(m, __shfl_xor(m, 16));
+    return fmaxf(m, __shfl_xor(m, 32));
+}
 
 // Workspace per (chunk slot, head), in bytes.  A fragment is one 16x16x32
 // MFMA operand for a wave: 64 lanes x 8 fp16 hi values, then 64 x 8 lo.
@@ -72,11 +100,13 @@ constexpr float kScW = 256.f, kInvScW = 1.f / 256.f;
 // holds, in this order: -W tiles (2 x 4), scaled-Q tiles (2 x 4), scaled-K
 // tiles for that half of the tokens (8), and the P tiles of its rows (2 in
 // half 0, 4 in half 1); half 0's slot 26 holds the chunk's total decay
-// (FP32 [PD]).  Ut follows in FP32, in the state kernel's D-tile order.
+// (FP32 [PD]) and then the largest |Ut| of each value column over the
+// chunk (FP32 [PD]).  Ut follows in FP32, in the state kernel's D-tile order.
 constexpr int FRAG_B = 2048;
 constexpr int HALF_FRAGS = 28;
 constexpr int HALF_B = HALF_FRAGS * FRAG_B;
 constexpr int GAM_OFF = 26 * FRAG_B;           // in half 0
+constexpr int UTMAX_OFF = GAM_OFF + PD * 4;    // in half 0
 constexpr int UT_OFF = 2 * HALF_B;
 constexpr int WS_B = UT_OFF + PC * PD * 4;
 
@@ -546,7 +576,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             float sq = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
-            const float r = (a.q_scale * kSc) / sqrtf(row16_sum(sq) + a.l2_eps);
+            const float r = kSc / sqrtf(row16_sum(sq) + a.l2_eps);
 #pragma unroll
             for (int q = 0; q < 8; ++q) qh[e][q] *= r;
         }
@@ -959,6 +989,24 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     // column tiles 4w..4w+3 of the 256 columns (waves 0-1: W, 2-3: Ut).
     {
         const bool isW = wave < 2;
+        // Value columns: the solve runs on R scaled by the column's power-of-
+        // two scale (largest |beta v| over the chunk in [1, 2)); X comes out
+        // scaled by the same factor and is unscaled on its way out.
+        float sg[4] = {1.f, 1.f, 1.f, 1.f}, isg[4] = {1.f, 1.f, 1.f, 1.f};
+        if (!isW) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int c = 16 * ((4 * wave + u) & 7) + n;
+                float m = 0.f;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(&VT[swz(c, 16 * b + 4 * g)]);
+                    m = fmaxf(m, fmaxf(fmaxf(fabsf(r4[0]), fabsf(r4[1])),
+                                       fmaxf(fabsf(r4[2]), fabsf(r4[3]))));
+                }
+                pow2_scale(col_max4(m) * kInvSc, sg[u], isg[u]);
+            }
+        }
         f32x4_t X[4][4];
         SplitOp4 Xs[3][4];
 #pragma unroll
@@ -967,7 +1015,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int c = 16 * ((4 * wave + u) & 7) + n;
-                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]);
+                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]) *
+                         sg[u];
             }
             if (b == 1) {
                 const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 + n][4 * g]);
@@ -1016,14 +1065,21 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 }
         } else {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int u = 0; u < 4; ++u) {
+                const int j16 = 4 * (wave - 2) + u;
+                float m = 0.f;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int j16 = 4 * (wave - 2) + u;
+                for (int b = 0; b < 4; ++b) {
                     const int hh = b >> 1, uu = b & 1;
+                    const f32x4_t x = X[b][u] * isg[u];
                     *reinterpret_cast<f32x4_t*>(ws + UT_OFF +
-                                                ((((hh * 8 + j16) * 2 + uu) * 64 + lane) * 16)) = X[b][u];
+                                                ((((hh * 8 + j16) * 2 + uu) * 64 + lane) * 16)) = x;
+                    m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
                 }
+                // the column's largest |Ut| over the chunk, for the state pass's scale
+                m = col_max4(m);
+                if (g == 0) reinterpret_cast<float*>(ws + UTMAX_OFF)[16 * j16 + n] = m;
+            }
         }
     }
     lds_sync();
@@ -1203,7 +1259,8 @@ __device__ __forceinline__ void prod1x4(const SplitOp (&fa)[4], const SplitOp (&
 // the half's number (never 0) in the slice's flag; the O wave polls the flag
 // before reading U.  The U/S wave never waits for the O wave here (the
 // barriers at each half's start keep both in step), so the hand-off cannot
-// block.  The poll is bounded all the same.
+// block.  The poll is bounded all the same: await_half returns false when
+// the flag never arrived, and the kernel then reports KDA_STATUS_STALLED.
 // The flag is accessed through an LDS-typed pointer: through a generic one
 // the volatile access becomes a flat store, which also counts as a vector
 // memory operation and makes the compiler wait for every outstanding load.
@@ -1212,13 +1269,18 @@ __device__ __forceinline__ void publish_half(int* flag, int epoch) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     *(lds_vint_t*)flag = epoch;
 }
-__device__ __forceinline__ void await_half(int* flag, int epoch) {
+__device__ __forceinline__ bool await_half(int* flag, int epoch) {
+    bool ok = false;
     for (int spin = 0; spin < (1 << 22); ++spin) {
         const int f = __builtin_amdgcn_readfirstlane(*(lds_vint_t*)flag);
-        if (f == epoch) break;
+        if (f == epoch) {
+            ok = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
     asm volatile("" ::: "memory");
+    return ok;
 }
 
 // A fragment straight from the workspace (same layout as in LDS).
@@ -1328,11 +1390,20 @@ constexpr int kStateThreads = 384;
 //
 // O wave r computes row tile r of O = Qg S + P U for both column tiles and
 // stores it.  One barrier per half keeps the buffers in step.
+//
+// Value columns carry a power-of-two scale per chunk (pow2_scale of the
+// column's largest magnitude over the chunk's start state and its Ut): the
+// U/S waves trade their halves' column maxima through LDS before splitting
+// the state, and the O waves read the scale after the chunk's first barrier.
+// S is held unscaled between chunks.
 template <int ACT, int ST>
 __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char hbuf[2][SBUF_B];
     __shared__ StateX X;
     __shared__ int xflag[2];                      // per row tile: last half published
+    __shared__ int mflag[2];                      // per U/S wave: last chunk scale published
+    __shared__ float xmax[2][2][16];              // [U/S wave][column tile][column]
+    __shared__ float xisg[2][16];                 // 1 / scale of the chunk's columns
     __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1340,7 +1411,9 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
     const int n = lane & 15, g = lane >> 4;
     const int r = wave & 1;                       // row tile (U/S channel half; loader index)
     const int H = a.H;
-    if (tid < 2) xflag[tid] = 0;                  // visible after the first barrier
+    if (tid < 2) xflag[tid] = 0;
+    if (tid >= 2 && tid < 4) mflag[tid - 2] = 0;
+    lds_sync();                                   // the flags before any wave uses them
     // The half buffers are filled only by assembly loads; this store, which
     // never runs (num_seqs >= 1), keeps the compiler from treating them as
     // never written.
@@ -1421,18 +1494,53 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                                          : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[el]);
                     }
         }
+        bool stalled = false;
+        // the chunk's largest |Ut| in each of the lane's two value columns
+        auto ld_utmax = [&](int c, float (&m)[2]) {
+            const float* p = reinterpret_cast<const float*>(cws(c) + UTMAX_OFF);
+            m[0] = p[jc[0]];
+            m[1] = p[jc[1]];
+        };
+        float mut[2], mut_next[2];
+        ld_utmax(0, mut);
+        // the chunk's column scales: both U/S waves take the largest |S| over
+        // their channel halves, trade them through LDS, and combine them with
+        // the chunk's largest |Ut| into the same power of two
+        float sg[2], isg[2];
+        auto set_scale = [&](int cc) {
+            float m[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float x = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x = fmaxf(x, fabsf(S[j][i][e]));
+                m[j] = col_max4(x);
+                if (g == 0) xmax[r][j][n] = m[j];
+            }
+            publish_half(&mflag[r], cc + 1);
+            stalled |= !await_half(&mflag[1 - r], cc + 1);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                pow2_scale(fmaxf(fmaxf(m[j], xmax[1 - r][j][n]), mut[j]), sg[j], isg[j]);
+                if (r == 0 && g == 0) xisg[j][n] = isg[j];
+            }
+        };
         // the B operands of the U product, own k blocks 2r, 2r+1 in slots 0,
-        // 1 (from registers) and the other wave's in slots 2, 3 (from LDS)
+        // 1 (from registers) and the other wave's in slots 2, 3 (from LDS),
+        // all scaled by the columns' scales
         SplitOp sb[2][4];
         auto make_own = [&]() {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    sb[j][m] = split_pair(S[j][2 * m], S[j][2 * m + 1]);
+                    sb[j][m] = split_pair(S[j][2 * m] * sg[j], S[j][2 * m + 1] * sg[j]);
                     put_split(X.sb_hi[j][2 * r + m], X.sb_lo[j][2 * r + m], lane, sb[j][m]);
                 }
         };
+        set_scale(0);
         make_own();
         auto get_other = [&]() {
 #pragma unroll
@@ -1442,7 +1550,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     sb[j][2 + m] = get_split(X.sb_hi[j][2 * (1 - r) + m],
                                              X.sb_lo[j][2 * (1 - r) + m], lane);
         };
-        // row tile r of this half's U (accumulated at 2^8), split, to LDS
+        // row tile r of this half's U (accumulated at 2^8 times the column
+        // scales), split, to LDS
         auto u_tile = [&](const char* buf) {
             SplitOp w[4];
 #pragma unroll
@@ -1452,7 +1561,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[j] = *reinterpret_cast<const f32x4_t*>(buf + SBUF_UT + (2 * j + r) * 1024 +
-                                                           lane * 16) * kScW;
+                                                           lane * 16) * (kScW * sg[j]);
             prod4x2(w, sb, acc);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
@@ -1474,6 +1583,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             });
         };
         for (int cc = 0; cc < nch; ++cc) {
+            if (cc + 1 < nch) ld_utmax(cc + 1, mut_next);       // used at the chunk's end
             // ======== first half: tokens 0..31 of the chunk ========
             lds_sync();                                            // H0
             get_other();
@@ -1485,23 +1595,29 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(
                                        hbuf[0] + GAM_OFF + (16 * (4 * r + i) + 4 * g) * 4) * kSc;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) Sn[j][i] = gm * S[j][i];
+                for (int j = 0; j < 2; ++j) Sn[j][i] = gm * (S[j][i] * sg[j]);
             }
-            await_half(&xflag[1 - r], 2 * cc + 1);
+            stalled |= !await_half(&xflag[1 - r], 2 * cc + 1);
             s_update(hbuf[0], Sn);
 
             // ======== second half: tokens 32..63 ========
             lds_sync();                                            // H1
             u_tile(hbuf[1]);                              // the other blocks are still held
             publish_half(&xflag[r], 2 * cc + 2);
-            await_half(&xflag[1 - r], 2 * cc + 2);
+            stalled |= !await_half(&xflag[1 - r], 2 * cc + 2);
             s_update(hbuf[1], Sn);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * kInvSc;
-            make_own();                                   // the next chunk's split state
+                for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * (kInvSc * isg[j]);
+            if (cc + 1 < nch) {                           // the next chunk's scale and split state
+                mut[0] = mut_next[0];
+                mut[1] = mut_next[1];
+                set_scale(cc + 1);
+                make_own();
+            }
         }
+        if (stalled && lane == 0 && a.status) atomicOr(a.status, KDA_STATUS_STALLED);
         // typed store of the final state, once
 #pragma unroll
         for (int j = 0; j < 2; ++j)
@@ -1521,6 +1637,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
         // barrier
         f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         int orow0 = -1;
+        bool stalled = false;
         auto store_o = [&]() {
             if (orow0 < 0) return;
 #pragma unroll
@@ -1538,6 +1655,11 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             // ======== first half ========
             lds_sync();                                            // H0
             store_o();
+            // O comes out at 2^12 times the chunk's column scales; the query
+            // scale multiplies it here
+            float osc[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) osc[j] = a.q_scale * (kInvSc * xisg[j][n]);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1545,12 +1667,12 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     sb[j][kb] = get_split(X.sb_hi[j][kb], X.sb_lo[j][kb], lane);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[0], frag_q(r, kb), lane);
-            // O = (e(t,-1) q) S (accumulated at 2^12)
+            // O = (e(t,-1) q) S
             f32x4_t O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
             prod4x2(fq, sb, O);
             SplitOp fp0 = ld_frag(hbuf[0], frag_p(0, r, 0), lane);
-            await_half(&xflag[0], 2 * cc + 1);
-            await_half(&xflag[1], 2 * cc + 1);
+            stalled |= !await_half(&xflag[0], 2 * cc + 1);
+            stalled |= !await_half(&xflag[1], 2 * cc + 1);
             SplitOp ub0[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) ub0[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
@@ -1558,8 +1680,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
                 for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
             });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
+            Oprev[0] = O[0] * osc[0];
+            Oprev[1] = O[1] * osc[1];
             orow0 = cc * PC;
 
             // ======== second half ========
@@ -1575,8 +1697,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
                 for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
             });
-            await_half(&xflag[0], 2 * cc + 2);
-            await_half(&xflag[1], 2 * cc + 2);
+            stalled |= !await_half(&xflag[0], 2 * cc + 2);
+            stalled |= !await_half(&xflag[1], 2 * cc + 2);
             SplitOp ub1[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) ub1[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
@@ -1584,11 +1706,12 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
                 for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp1, ub1[j], O[j]);
             });
-            Oprev[0] = O[0] * kInvSc;
-            Oprev[1] = O[1] * kInvSc;
+            Oprev[0] = O[0] * osc[0];
+            Oprev[1] = O[1] * osc[1];
             orow0 = cc * PC + 32;
         }
         store_o();
+        if (stalled && lane == 0 && a.status) atomicOr(a.status, KDA_STATUS_STALLED);
     }
 
     // ring: the sequence's last min(3, len) raw tokens (the chunk kernel,

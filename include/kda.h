@@ -305,7 +305,18 @@ int kda_commit_recompute(const kda_shape *shape, const kda_params *params,
  * on Rubin (SM107): Modeling V2 target ...", section 3); FP32 recurrence
  * ("Extend ... isolated NVFP4 Kimi K3 targets", Description).  Chunkwise
  * WY/UT form with chunks of 64 tokens; the result equals the token-by-token
- * recurrence up to FP32 rounding.
+ * recurrence up to FP32-level rounding.  The chunk products run on the
+ * matrix cores with operands split into fp16 pairs (2^-22 of each value).
+ * Key-side operands are bounded; value-side operands (v, the writes U and
+ * the state) carry an exact power-of-two scale per value column and chunk,
+ * so any magnitude of v and of the stored state works, and any ratio between
+ * them, with one limit: within a chunk and value column, a write or state
+ * entry more than about 2^9 below the column's largest |U| or |S| keeps
+ * about 2^-25 of that largest value in absolute terms rather than 2^-22 of
+ * its own.  That matters only when a start state far larger than the
+ * chunk's values decays away inside the chunk; the error is then about
+ * 2^-25 x (start magnitude / result magnitude) relative to the result.
+ * q_scale multiplies the read-outs, never an operand.
  *   cu_seqlens [num_seqs + 1] int32 (device): sequence s owns tokens
  *            cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed inputs.
  *   total_tokens: rows of the packed inputs (host).

@@ -233,8 +233,8 @@ def commit(cfg: OracleCfg, S, hist, records, toks, accepted, store_bf16):
 # Whole-workload drivers.  They follow the mixer's three modes; positions
 # and slots are bookkeeping of the device pool and do not enter the math.
 
-def _cfg_of(case, gate="sigmoid"):
-    return OracleCfg(case.dk, case.dv, case.width, gate, gates=case.gates)
+def _cfg_of(case, gate="sigmoid", q_scale=1.0):
+    return OracleCfg(case.dk, case.dv, case.width, gate, q_scale, gates=case.gates)
 
 
 def decode_case(case, *, threads=None, gate="sigmoid", steps=None):
@@ -286,11 +286,11 @@ def verify_case(case, *, threads=None, gate="sigmoid"):
     return y, rec, S, hist
 
 
-def prefill_case(case, *, threads=None, gate="sigmoid", chunk=None):
+def prefill_case(case, *, threads=None, gate="sigmoid", chunk=None, q_scale=1.0):
     """Each sequence from its start state over its whole length, stored once.
 
     Returns (y [T,H,dv], S [B,H,dk,dv], hist [B,W-1,H,C])."""
-    cfg = _cfg_of(case, gate)
+    cfg = _cfg_of(case, gate, q_scale)
     B, H = case.batch, case.H
     S = _f64(case.S0).copy()
     hist = _f64(case.hist0).copy()

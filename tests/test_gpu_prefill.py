@@ -12,9 +12,9 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def run_prefill_gpu(case, ds=None, *, slots=None, max_seqlen=None, cu=None):
+def run_prefill_gpu(case, ds=None, *, slots=None, max_seqlen=None, cu=None, q_scale=1.0):
     torch = need_gpu()
-    ds = dev.make_state(case) if ds is None else ds
+    ds = dev.make_state(case, q_scale=q_scale) if ds is None else ds
     tok = dev.tokens_to_device(case.tokens, case.act)
     T = int(case.cu_seqlens[-1])
     y = torch.full((T, case.H, case.dv), float("nan"), device="cuda")
@@ -34,12 +34,12 @@ def run_prefill_gpu(case, ds=None, *, slots=None, max_seqlen=None, cu=None):
     return ds, y.cpu().numpy(), int(status.item())
 
 
-def check_prefill(case, *, full_outputs=True):
+def check_prefill(case, *, full_outputs=True, q_scale=1.0):
     print(f"case {case.name}: lens={case.lens} H={case.H} d={case.dk} act={case.act} "
-          f"state={case.state}", flush=True)
-    ds, y, status = run_prefill_gpu(case)
+          f"state={case.state} q_scale={q_scale}", flush=True)
+    ds, y, status = run_prefill_gpu(case, q_scale=q_scale)
     assert status == 0
-    y_ref, S_ref, h_ref = oracle.prefill_case(case)
+    y_ref, S_ref, h_ref = oracle.prefill_case(case, q_scale=q_scale)
     tol = tol_for(case.state)
     assert_parity(dev.read_states(ds), S_ref, tol, "final states")
     if full_outputs:
@@ -109,6 +109,64 @@ def test_prefill_strong_decay_stays_finite():
     case.tokens.alpha[:] = wl.round_f32(np.exp(-rng.uniform(0.0, 12.0,
                                                             case.tokens.alpha.shape)))
     check_prefill(case)
+
+
+@pytest.mark.parametrize("ev,es,state", [(-12, -12, "f32"), (12, 12, "f32"),
+                                         (-24, -24, "f32"), (24, 24, "f32"),
+                                         (12, -12, "f32"), (-3, 3, "f32"),
+                                         (12, 12, "bf16")])
+def test_prefill_value_and_state_magnitudes(ev, es, state):
+    """v (and the v channels of the stored history) scaled by 2^ev and the
+    stored start state by 2^es, exactly (powers of two).  The recurrence
+    takes them at any magnitude; the prefill's split matrix-core operands
+    keep FP32-level accuracy on the value side whatever the common
+    magnitude is, with a start state much smaller than the values, and with
+    one up to 2^6 larger (the stated domain allows about 2^9 between the
+    largest write of a chunk and the ones that set its result)."""
+    need_gpu()
+    case = wl.make_prefill(88, lens=[200, 64, 37], H=2, dk=128, dv=128, act="bf16",
+                           state=state, init="random", slice_len=32,
+                           name=f"prefill_magnitudes_v{ev}_s{es}_{state}")
+    case.tokens.v[:] *= 2.0 ** ev
+    case.hist0[..., 2 * case.dk:] *= 2.0 ** ev
+    case.S0[:] *= 2.0 ** es
+    if state == "bf16":
+        case.S0[:] = wl.round_bf16(case.S0)
+    check_prefill(case)
+
+
+def test_prefill_near_collinear_keys_full_writes():
+    """Keys of one sequence and head all close to one direction (head 0) or
+    to one direction with alternating sign (head 1), beta close to 1 and no
+    decay: A is close to a block of ones (or of alternating signs) under the
+    diagonal, the hardest case for the diagonal inverses T_bb and for W."""
+    need_gpu()
+    case = wl.make_prefill(89, lens=[192, 80, 17], H=2, dk=128, dv=128, act="f32",
+                           state="f32", init="random", slice_len=32,
+                           name="prefill_collinear_keys")
+    rng = np.random.default_rng(9)
+    k = case.tokens.k                         # [T, H, dk]
+    T = k.shape[0]
+    sign = np.where(np.arange(T) % 2 == 0, 1.0, -1.0)
+    for h in range(case.H):
+        base = rng.standard_normal(case.dk)
+        noise = 1e-3 * rng.standard_normal((T, case.dk))
+        k[:, h] = (sign[:, None] if h == 1 else 1.0) * base[None, :] + noise
+    case.tokens.k[:] = wl.round_f32(k)
+    case.tokens.beta[:] = wl.round_f32(np.full_like(case.tokens.beta, 0.999))
+    case.tokens.alpha[:] = 1.0
+    case.hist0[..., case.dk:2 * case.dk] = 0.0   # history keys do not spoil the first block
+    check_prefill(case)
+
+
+@pytest.mark.parametrize("q_scale", [0.08838834764831845, 40.0])
+def test_prefill_query_scale(q_scale):
+    """A query scale other than 1 (1/sqrt(dk), and a large one): the prefill
+    applies it to the read-outs, and the outputs match the oracle's."""
+    need_gpu()
+    case = wl.make_prefill(90, lens=[130, 7], H=2, dk=128, dv=128, act="bf16", state="f32",
+                           init="random", slice_len=32, name=f"prefill_q_scale_{q_scale:g}")
+    check_prefill(case, q_scale=q_scale)
 
 
 def test_prefill_many_sequences_several_items_per_workgroup():
