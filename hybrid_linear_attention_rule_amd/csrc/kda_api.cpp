@@ -89,6 +89,8 @@ const char* kda_status_str(int code) {
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_UNSUPPORTED: return "no kernel for these sizes";
         case KDA_ERR_HIP: return "HIP launch error";
+        case KDA_ERR_TOO_LARGE:
+            return "the call needs more scratch than the no-allocation prefill holds";
         case KDA_STATUS_BAD_SLOT: return "device status: a slot id is >= num_slots";
         case KDA_STATUS_BAD_POSITION: return "device status: a position is negative";
         case KDA_STATUS_BAD_ACCEPTED: return "device status: an accepted length is outside [0, n_draft]";
@@ -343,26 +345,37 @@ int kda_commit_accepted(const kda_shape* s, int32_t batch, int32_t n_draft,
     return kda::launch_commit(*s, a, batch, stream);
 }
 
-int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
-                const int32_t* cu_seqlens, int64_t total_tokens, int32_t max_seqlen,
-                int64_t num_slots, const int32_t* slot_ids, const int32_t* positions,
-                const void* q, const void* k, const void* v, const void* alpha,
-                const void* beta, const void* g, void* pool, void* ring, float* y,
-                void* workspace, size_t workspace_bytes, int32_t* status,
-                hipStream_t stream) {
+// Validation shared by both prefill entry points, before any launch.
+static int check_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
+                         const int32_t* cu_seqlens, int64_t total_tokens, int32_t max_seqlen,
+                         int64_t num_slots, const int32_t* slot_ids, const int32_t* positions,
+                         const void* q, const void* k, const void* v, const void* alpha,
+                         const void* beta, const void* g, void* pool, void* ring, float* y,
+                         bool& nothing_to_do) {
+    nothing_to_do = false;
     int rc = check_shape(s);
     if (rc != KDA_OK) return rc;
     if ((rc = check_params(p, s)) != KDA_OK) return rc;
     if (num_seqs < 0 || total_tokens < 0 || max_seqlen < 0 || num_slots < 0)
         return KDA_ERR_SHAPE;
-    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) return KDA_OK;
+    if (num_seqs == 0 || total_tokens == 0 || max_seqlen == 0) {
+        nothing_to_do = true;
+        return KDA_OK;
+    }
     // the finish kernel runs one 256-thread workgroup per token (grid x)
     if (total_tokens > 0x7fffffffLL || total_tokens * 256 >= (1LL << 32)) return KDA_ERR_SHAPE;
     if (!cu_seqlens || !slot_ids || !positions || !q || !k || !v || !alpha || !beta ||
         !g || !pool || !ring || !y)
         return KDA_ERR_NULL;
-    const size_t need = kda::prefill_workspace_bytes(*s, num_seqs, total_tokens);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    return KDA_OK;
+}
+
+static int run_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
+                       const int32_t* cu_seqlens, int64_t total_tokens, int32_t max_seqlen,
+                       int64_t num_slots, const int32_t* slot_ids, const int32_t* positions,
+                       const void* q, const void* k, const void* v, const void* alpha,
+                       const void* beta, const void* g, void* pool, void* ring, float* y,
+                       void* workspace, int32_t* status, hipStream_t stream) {
     kda::PrefillArgs a{};
     a.cu_seqlens = cu_seqlens;
     a.slot_ids = slot_ids;
@@ -395,6 +408,45 @@ int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
     set_scales(p, s, a.scale_q, a.scale_k, a.scale_v);
     set_row_strides(s, a.qkv_rs, a.g_rs);
     return kda::launch_prefill(*s, a, stream);
+}
+
+int kda_prefill(const kda_shape* s, const kda_params* p, int32_t num_seqs,
+                const int32_t* cu_seqlens, int64_t total_tokens, int32_t max_seqlen,
+                int64_t num_slots, const int32_t* slot_ids, const int32_t* positions,
+                const void* q, const void* k, const void* v, const void* alpha,
+                const void* beta, const void* g, void* pool, void* ring, float* y,
+                void* workspace, size_t workspace_bytes, int32_t* status,
+                hipStream_t stream) {
+    bool none;
+    int rc = check_prefill(s, p, num_seqs, cu_seqlens, total_tokens, max_seqlen, num_slots,
+                           slot_ids, positions, q, k, v, alpha, beta, g, pool, ring, y, none);
+    if (rc != KDA_OK || none) return rc;
+    if (s->head_k != 128 || s->head_v != 128) return KDA_ERR_UNSUPPORTED;
+    const size_t need = kda::prefill_workspace_bytes(*s, num_seqs, total_tokens);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    return run_prefill(s, p, num_seqs, cu_seqlens, total_tokens, max_seqlen, num_slots,
+                       slot_ids, positions, q, k, v, alpha, beta, g, pool, ring, y, workspace,
+                       status, stream);
+}
+
+int kda_prefill_noalloc(const kda_shape* s, const kda_params* p, int32_t num_seqs,
+                        const int32_t* cu_seqlens, int64_t total_tokens, int32_t max_seqlen,
+                        int64_t num_slots, const int32_t* slot_ids, const int32_t* positions,
+                        const void* q, const void* k, const void* v, const void* alpha,
+                        const void* beta, const void* g, void* pool, void* ring, float* y,
+                        int32_t* status, hipStream_t stream) {
+    bool none;
+    int rc = check_prefill(s, p, num_seqs, cu_seqlens, total_tokens, max_seqlen, num_slots,
+                           slot_ids, positions, q, k, v, alpha, beta, g, pool, ring, y, none);
+    if (rc != KDA_OK || none) return rc;
+    if (s->head_k != 128 || s->head_v != 128) return KDA_ERR_UNSUPPORTED;
+    if (kda::prefill_workspace_bytes(*s, num_seqs, total_tokens) > KDA_PREFILL_SCRATCH_BYTES)
+        return KDA_ERR_TOO_LARGE;
+    void* scratch = kda::prefill_scratch();
+    if (!scratch) return KDA_ERR_HIP;
+    return run_prefill(s, p, num_seqs, cu_seqlens, total_tokens, max_seqlen, num_slots,
+                       slot_ids, positions, q, k, v, alpha, beta, g, pool, ring, y, scratch,
+                       status, stream);
 }
 
 }  // extern "C"

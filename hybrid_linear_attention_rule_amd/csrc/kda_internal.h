@@ -121,5 +121,8 @@ size_t prefill_workspace_bytes(const kda_shape& s, int32_t num_seqs,
                                int64_t total_tokens);
 int launch_prefill(const kda_shape& s, const PrefillArgs& a,
                    hipStream_t stream);
+// Device address of the current device's fixed prefill scratch array
+// (KDA_PREFILL_SCRATCH_BYTES), resolved once per device; NULL on a HIP error.
+void* prefill_scratch();
 
 }  // namespace kda

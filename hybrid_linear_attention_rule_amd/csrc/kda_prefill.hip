@@ -46,6 +46,7 @@
 #include "kda_mfma.h"
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 namespace kda {
@@ -1828,6 +1829,28 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         hipLaunchKernelGGL((prefill_finish_kernel<ACT>), dim3((unsigned)a.total_tokens, hgroups),
                            dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// The fixed workspace of kda_prefill_noalloc: one array per GPU the library
+// runs on, placed when the code object loads and held until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies take the address prefill_scratch() resolves.
+static __device__ __align__(256) char scratch[KDA_PREFILL_SCRATCH_BYTES];
+
+void* prefill_scratch() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<void*> ptrs[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = ptrs[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    // once per device (a concurrent first call resolves the same address)
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();              // leave no error behind for the next call
+        return nullptr;
+    }
+    ptrs[dev].store(p, std::memory_order_release);
+    return p;
 }
 
 int launch_prefill(const kda_shape& s, const PrefillArgs& a, hipStream_t stream) {

@@ -24,6 +24,9 @@ STATUS_BAD_SLOT = 1
 STATUS_BAD_POSITION = 2
 STATUS_BAD_ACCEPTED = 4
 STATUS_BAD_SEQLENS = 8
+STATUS_STALLED = 16
+ERR_TOO_LARGE = -7
+PREFILL_SCRATCH_BYTES = 128 << 20      # KDA_PREFILL_SCRATCH_BYTES in kda.h
 
 _DT = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3}
 _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.float8_e4m3fn}
@@ -77,6 +80,8 @@ SIGNATURES = {
                              [_vp] * 6 + [_vp, _vp, _vp, _vp]),
     "kda_prefill": (ctypes.c_int, [_SP, _PP, _i32, _vp, _i64, _i32, _i64, _vp, _vp] +
                     [_vp] * 6 + [_vp, _vp, _vp, _vp, _sz, _vp, _vp]),
+    "kda_prefill_noalloc": (ctypes.c_int, [_SP, _PP, _i32, _vp, _i64, _i32, _i64, _vp, _vp] +
+                            [_vp] * 6 + [_vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -412,3 +417,24 @@ def prefill(shape, params, cu_seqlens, max_seqlen, slot_ids, positions, q, k, v,
                               _ptr(alpha), _ptr(beta), _ptr(g), _ptr(pool), _ptr(ring),
                               _ptr(y), _ptr(workspace), ws_bytes, _ptr(status),
                               _stream(stream)))
+
+
+def prefill_noalloc(shape, params, cu_seqlens, max_seqlen, slot_ids, positions, q, k, v,
+                    alpha, beta, g, pool, ring, y, status=None, stream=None):
+    """kda_prefill with the library's fixed scratch array as its workspace
+    (no allocation; calls needing more than PREFILL_SCRATCH_BYTES of
+    workspace raise KdaError with code ERR_TOO_LARGE)."""
+    B = slot_ids.numel()
+    T = q.shape[0]
+    _check_params(shape, params)
+    _expect(cu_seqlens, B + 1, torch.int32, "cu_seqlens")
+    _expect(slot_ids, B, torch.int32, "slot_ids")
+    _expect(positions, B, torch.int32, "positions")
+    _check_tokens(shape, T, q, k, v, alpha, beta, g)
+    _check_pool_ring(shape, pool, ring)
+    _expect(y, T * shape.num_heads * shape.head_v, torch.float32, "y")
+    _check(load().kda_prefill_noalloc(ctypes.byref(shape.c()), ctypes.byref(params.c()), B,
+                                      _ptr(cu_seqlens), T, int(max_seqlen), pool.shape[0],
+                                      _ptr(slot_ids), _ptr(positions), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(alpha), _ptr(beta), _ptr(g), _ptr(pool),
+                                      _ptr(ring), _ptr(y), _ptr(status), _stream(stream)))

@@ -89,7 +89,9 @@ enum {
     KDA_ERR_DTYPE = -3,       /* an unknown dtype or gate code */
     KDA_ERR_WORKSPACE = -4,   /* workspace missing or too small */
     KDA_ERR_UNSUPPORTED = -5, /* valid, but no kernel for these sizes */
-    KDA_ERR_HIP = -6          /* a HIP launch error */
+    KDA_ERR_HIP = -6,         /* a HIP launch error */
+    KDA_ERR_TOO_LARGE = -7    /* kda_prefill_noalloc: the call needs more
+                               * scratch than KDA_PREFILL_SCRATCH_BYTES */
 };
 
 /* Bits OR-ed into *status by the device.  kda_status_str() also names each
@@ -336,6 +338,35 @@ int kda_prefill(const kda_shape *shape, const kda_params *params,
                 const void *alpha, const void *beta, const void *g,
                 void *pool, void *ring, float *y, void *workspace,
                 size_t workspace_bytes, int32_t *status, hipStream_t stream);
+
+/* ----- chunked prefill without any allocation --------------------------- */
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * computation as kda_prefill with the same arguments, except that the
+ * workspace is a fixed array of KDA_PREFILL_SCRATCH_BYTES inside the library
+ * (one per GPU the library runs on, held until the process ends).
+ *   - Calls whose kda_prefill_workspace_bytes(shape, num_seqs, total_tokens)
+ *     exceeds KDA_PREFILL_SCRATCH_BYTES return KDA_ERR_TOO_LARGE before any
+ *     launch (128 MiB holds 910 (64-token chunk slot, head) pairs: for
+ *     example 1,728 tokens of one sequence at H = 32, or 29,056 at H = 2).
+ *   - The call allocates nothing and calls no allocating routine.  Its first
+ *     call on a device resolves that device's array address
+ *     (hipGetSymbolAddress), which may load the library's code object; make
+ *     that first call outside any graph capture.
+ *   - Every call on a GPU shares that GPU's array, and nothing in it needs
+ *     to start at zero.  Calls that overlap on one GPU (on different
+ *     streams, or from different threads without ordering) race on it and
+ *     give undefined results: order them on one stream. */
+#define KDA_PREFILL_SCRATCH_BYTES ((size_t)128 << 20)
+int kda_prefill_noalloc(const kda_shape *shape, const kda_params *params,
+                        int32_t num_seqs, const int32_t *cu_seqlens,
+                        int64_t total_tokens, int32_t max_seqlen,
+                        int64_t num_slots, const int32_t *slot_ids,
+                        const int32_t *positions, const void *q,
+                        const void *k, const void *v, const void *alpha,
+                        const void *beta, const void *g, void *pool,
+                        void *ring, float *y, int32_t *status,
+                        hipStream_t stream);
 
 #ifdef __cplusplus
 }

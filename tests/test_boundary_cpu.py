@@ -36,7 +36,7 @@ def shape(**kw):
 
 def test_every_declared_symbol_is_exported(lib):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
     assert sorted(kda.SIGNATURES) == names
@@ -205,6 +205,28 @@ def test_prefill_host_errors(lib):
     assert prefill(num_seqs=0, ptrs=[None] * 12) == OK
     # one 256-thread workgroup per token: 2^24 tokens is over the launch limit
     assert prefill(total=1 << 24, max_len=1 << 23) == E_SHAPE
+
+    # the no-allocation variant: same checks, then its fixed scratch size
+    def noalloc(num_seqs=2, total=100, max_len=60, ptrs=None, shp=sh):
+        p = [BOGUS] * 12 if ptrs is None else ptrs
+        return lib.kda_prefill_noalloc(ctypes.byref(shp.c()), ctypes.byref(_params()),
+                                       num_seqs, p[0], total, max_len, 8, *p[1:], None, None)
+    for i in range(12):
+        p = [BOGUS] * 12
+        p[i] = None
+        assert noalloc(ptrs=p) == E_NULL, i
+    assert noalloc(num_seqs=-1) == E_SHAPE
+    assert noalloc(num_seqs=0, ptrs=[None] * 12) == OK
+    assert noalloc(shp=shape(head_k=64, head_v=64)) == E_UNSUP
+    cap = kda.PREFILL_SCRATCH_BYTES
+    per_slot = kda.prefill_workspace_bytes(sh, 1, 64) // 2     # 1 chunk + 1 spare slot
+    slots_max = cap // per_slot                                 # chunk slots that fit
+    fits = (slots_max - 1) * 64                                 # one sequence
+    assert fits == 1728                                         # the figure kda.h states
+    assert kda.prefill_workspace_bytes(sh, 1, fits) <= cap
+    assert kda.prefill_workspace_bytes(sh, 1, fits + 64) > cap
+    assert noalloc(num_seqs=1, total=fits + 64, max_len=fits + 64) == kda.ERR_TOO_LARGE
+    assert lib.kda_status_str(kda.ERR_TOO_LARGE) != lib.kda_status_str(123)
 
 
 def test_state_io_host_errors(lib):
