@@ -25,9 +25,10 @@
 //
 // Thread map: the state of a head is stored [dk][dv] (dv contiguous).  A
 // thread owns VEC consecutive dv entries (16 bytes of storage) of RPT
-// consecutive key rows; LJ = dv / VEC lanes span a row and RG = 2 * VEC row
-// groups span dk (32 state elements per thread: 512 threads for
-// dk = dv = 128).  The dk-reductions run in-thread over the thread's RPT
+// consecutive key rows; LJ = dv / VEC lanes span a row and RG row groups
+// span dk (EPT = 32 state elements per thread: 512 threads for
+// dk = dv = 128; a one-token decode of a BF16 head takes EPT = 64, 256
+// threads).  The dk-reductions run in-thread over the thread's RPT
 // rows, then over the RG row groups through LDS in a fixed order, so every
 // result is bitwise reproducible.
 #include "kda_device.h"
@@ -602,13 +603,11 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitArgs a) {
 }
 
 // State elements per thread of a one-token decode: a 32 KiB BF16 head
-// (dk = dv = 128) is streamed by 256 threads with 128 bytes each, every other
-// case by DK * DV / 32 threads.
-#ifndef KDA_BF16_DECODE_EPT
-#define KDA_BF16_DECODE_EPT 32
-#endif
+// (dk = dv = 128) is streamed by 256 threads with 128 bytes each (measured
+// 0.3% faster than 512 threads with 64 bytes on the 256-row BF16-state
+// workload, same session, ABBA), every other case by DK * DV / 32 threads.
 template <int DK, int ST>
-constexpr int kDecodeEpt = (ST == kBF16 && DK == 128) ? KDA_BF16_DECODE_EPT : 32;
+constexpr int kDecodeEpt = (ST == kBF16 && DK == 128) ? 64 : 32;
 
 template <int DK, int DV, int ACT, int ST, bool STRIDED>
 static void launch_token_s(const TokenArgs& a, int32_t batch, int mode, hipStream_t stream) {
