@@ -163,3 +163,83 @@ def test_decode_is_bitwise_deterministic():
         outs.append((y, ds.pool.float().cpu().numpy()))
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("act,state", [("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32"),
+                                       ("fp8", "bf16")])
+def test_decode_many_rows_matches_small_calls(act, state):
+    """64 rows x 32 heads (2,048 row-head items) in one launch, with ragged
+    activity and rows starting at positions 0..7 (fresh sequences and short
+    histories).  The outputs, states and histories match the oracle, and
+    equal bit for bit what the same rows give when decoded four at a time:
+    the grid size changes nothing about a row's arithmetic."""
+    torch = need_gpu()
+    case = wl.make_decode(35, B=64, H=32, dk=128, dv=128, steps=3, act=act, state=state,
+                          init="random", active_per_step=48,
+                          name=f"many_rows_{act}_{state}")
+    device_S0 = case.S0.copy()
+    case.pos0 = (np.arange(64) % 8).astype(np.int64)
+    for b in range(64):
+        if case.pos0[b] == 0:
+            case.S0[b] = 0.0
+        for j in range(3):
+            if case.pos0[b] - 3 + j < 0:
+                case.hist0[b, j] = 0.0
+    ds = check_decode(case, device_S0=device_S0)
+    # the same steps, four rows per call
+    ds4 = dev.make_state(_with_S0(case, device_S0))
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    y4 = torch.full((case.steps, 64, 32, 128), float("nan"), device="cuda")
+    pos = case.pos0.copy()
+    for s in range(case.steps):
+        act_s = case.active[s]
+        for r0 in range(0, 64, 4):
+            rows = slice(r0, r0 + 4)
+            slot_t = torch.from_numpy(np.where(act_s[rows], ds4.slots[rows], -1)
+                                      .astype(np.int32)).cuda()
+            pos_t = torch.from_numpy(pos[rows].astype(np.int32)).cuda()
+            kda.decode(ds4.shape, ds4.params, slot_t, pos_t, tok["q"][s][rows].contiguous(),
+                       tok["k"][s][rows].contiguous(), tok["v"][s][rows].contiguous(),
+                       tok["alpha"][s][rows].contiguous(), tok["beta"][s][rows].contiguous(),
+                       tok["g"][s][rows].contiguous(), ds4.pool, ds4.ring, y4[s][rows])
+        pos += act_s
+    torch.cuda.synchronize()
+    y_all, _, _ = run_decode_gpu(case, dev.make_state(_with_S0(case, device_S0)))
+    np.testing.assert_array_equal(y4.cpu().numpy(), y_all)
+    assert torch.equal(ds4.pool.view(torch.uint8), ds.pool.view(torch.uint8))
+    assert torch.equal(ds4.ring.view(torch.uint8), ds.ring.view(torch.uint8))
+
+
+def test_decode_bad_rows_among_many():
+    """Bad slots and negative positions among 64 rows x 32 heads: reported,
+    those rows untouched, the others as the oracle has them."""
+    torch = need_gpu()
+    case = wl.make_decode(36, B=64, H=32, dk=128, dv=128, steps=1, act="bf16", state="bf16",
+                          init="random", name="many_rows_bad_rows")
+    ds = dev.make_state(case)
+    tok = dev.tokens_to_device(case.tokens, case.act)
+    pool0 = ds.pool.clone()
+    slots = ds.slots.astype(np.int32).copy()
+    pos = case.pos0.astype(np.int32).copy()
+    slots[5] = ds.num_slots + 1
+    slots[17] = -1
+    pos[40] = -3
+    y = torch.full((64, 32, 128), float("nan"), device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kda.decode(ds.shape, ds.params, torch.from_numpy(slots).cuda(),
+               torch.from_numpy(pos).cuda(), tok["q"][0], tok["k"][0], tok["v"][0],
+               tok["alpha"][0], tok["beta"][0], tok["g"][0], ds.pool, ds.ring, y, status)
+    torch.cuda.synchronize()
+    assert status.item() == kda.STATUS_BAD_SLOT | kda.STATUS_BAD_POSITION
+    y = y.cpu().numpy()
+    bad = [5, 17, 40]
+    assert np.isnan(y[bad]).all()
+    for b in bad:
+        if slots[b] >= 0 and slots[b] < ds.num_slots:
+            assert torch.equal(ds.pool[slots[b]].view(torch.uint8),
+                               pool0[slots[b]].view(torch.uint8))
+    good = np.setdiff1d(np.arange(64), bad)
+    y_ref, S_ref, _ = oracle.decode_case(case)
+    assert_parity(y[good], y_ref[0][good], tol_for(case.state), "y of the good rows")
+    assert_parity(dev.read_states(ds)[good], S_ref[good], tol_for(case.state),
+                  "states of the good rows")
