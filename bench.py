@@ -243,7 +243,7 @@ def rel_err(got, ref):
 # ------------------------------------------------------------ decode
 
 def run_decode_mode(torch, case, K, W, layers):
-    from hybrid_linear_attention_rule_amd import device as dev
+    from kda_inputs import device as dev
     from hybrid_linear_attention_rule_amd import kda
     import oracle
 
@@ -300,7 +300,7 @@ def run_decode_mode(torch, case, K, W, layers):
 # ------------------------------------------------------------ verify
 
 def run_verify_mode(torch, case, K, W, layers):
-    from hybrid_linear_attention_rule_amd import device as dev
+    from kda_inputs import device as dev
     from hybrid_linear_attention_rule_amd import kda
     import oracle
 
@@ -356,7 +356,7 @@ def run_verify_mode(torch, case, K, W, layers):
 def run_verify_recompute_mode(torch, case, K, W, layers):
     """The records-free alternative on the same workload: verify writes only
     y, and the commit runs the accepted tokens again from the stored state."""
-    from hybrid_linear_attention_rule_amd import device as dev
+    from kda_inputs import device as dev
     from hybrid_linear_attention_rule_amd import kda
     import oracle
 
@@ -414,7 +414,7 @@ def run_verify_recompute_mode(torch, case, K, W, layers):
 # ------------------------------------------------------------ prefill
 
 def run_prefill_mode(torch, case, K, W):
-    from hybrid_linear_attention_rule_amd import device as dev
+    from kda_inputs import device as dev
     from hybrid_linear_attention_rule_amd import kda
     import oracle
 
@@ -530,7 +530,7 @@ def main():
         sys.exit(2)
     import torch
     from hybrid_linear_attention_rule_amd import kda
-    from hybrid_linear_attention_rule_amd import workloads as wl
+    from kda_inputs import workloads as wl
 
     if not os.path.exists(kda.LIB_PATH):
         import __graft_entry__

@@ -14,7 +14,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-from . import kda
+from hybrid_linear_attention_rule_amd import kda
 from .workloads import FP8_SCALE, Case, gate_dtype
 
 RING = 4

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from hybrid_linear_attention_rule_amd import kda
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "tests", "c", "kda_c_caller.c")

@@ -3,9 +3,9 @@ import numpy as np
 import pytest
 
 from gpu_util import assert_parity, need_gpu, tol_for
-from hybrid_linear_attention_rule_amd import device as dev
+from kda_inputs import device as dev
 from hybrid_linear_attention_rule_amd import kda
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 import oracle
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +84,15 @@ def test_config1_batched_decode():
 def test_config3_bf16_state_ragged():
     need_gpu()
     check_decode(wl.config(3))
+
+
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+def test_two_head_large_batch_decode(state):
+    """The small per-GPU head count (two heads, 256 rows), with both storage
+    dtypes, as the benchmark's two-head mode launches it (one 256-row
+    launch per step, 512 workgroups)."""
+    need_gpu()
+    check_decode(wl.compact_heads(state))
 
 
 @pytest.mark.parametrize("act,state,d", [("f32", "f32", 128), ("bf16", "bf16", 64),

@@ -5,9 +5,9 @@ import numpy as np
 import pytest
 
 from gpu_util import assert_parity, need_gpu
-from hybrid_linear_attention_rule_amd import device as dev
+from kda_inputs import device as dev
 from hybrid_linear_attention_rule_amd import kda
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 from test_gpu_decode import check_decode
 from test_gpu_prefill import check_prefill
 from test_gpu_recompute import recompute, verify_no_records

@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from gpu_util import need_gpu
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 from test_gpu_decode import check_decode
 from test_gpu_prefill import check_prefill
 from test_gpu_verify import check_verify_commit

@@ -4,9 +4,9 @@ import numpy as np
 import pytest
 
 from gpu_util import assert_parity, need_gpu, tol_for
-from hybrid_linear_attention_rule_amd import device as dev
+from kda_inputs import device as dev
 from hybrid_linear_attention_rule_amd import kda
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 import oracle
 
 pytestmark = pytest.mark.gpu

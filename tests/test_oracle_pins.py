@@ -12,7 +12,7 @@ import pytest
 
 from oracle import ref
 from oracle.ref import OracleCfg
-from hybrid_linear_attention_rule_amd import workloads as wl
+from kda_inputs import workloads as wl
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
