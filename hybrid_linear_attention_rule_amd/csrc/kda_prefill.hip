@@ -28,18 +28,20 @@
 // queries.  Pairs inside one sub-block are formed elementwise in registers.
 //
 // Three kernels:
-//   chunk  (parallel over chunk x head): conv, L2 norms, decay products, A
-//          and P, the diagonal 16x16 inverses of (I + A), the blocked forward
-//          substitution for [W | Ut]; writes W (negated), exp-scaled Q and K
-//          and P as pre-split fp16 pairs in matrix-core fragment order, Ut in
-//          FP32, and the chunk's total decay;
-//   state  (per sequence x head x 64 value columns, sequential over the
-//          sequence's chunks): U, O and the next state on the matrix cores,
-//          the state slice in registers, each chunk's operands streamed into
-//          LDS in two halves by direct global-to-LDS loads, double-buffered;
-//          per 16-column slice one wave updates U and the state and another
-//          forms O; O is written unnormalised; the final state is stored
-//          once and the ring gets the sequence's last raw tokens;
+//   chunk  (persistent, one eight-wave workgroup per compute unit, items
+//          chunk x head): conv, L2 norms, decay products, A and P, the
+//          diagonal 16x16 inverses of (I + A), the blocked forward
+//          substitution for [W | Ut]; writes W (negated), decay-scaled Q and
+//          K and P as pre-split fp16 pairs in matrix-core fragment order, Ut
+//          in FP32, and the chunk's total decay;
+//   state  (four workgroups per sequence x head, 32 value columns each,
+//          sequential over the sequence's chunks): U, O and the next state
+//          on the matrix cores; two loader waves stream each half chunk's
+//          operands into LDS by direct global-to-LDS loads, double-buffered;
+//          two U/S waves form U and update the state slice they hold in
+//          registers, two O waves form O; O is written unnormalised; the
+//          final state is stored once and the ring gets the sequence's last
+//          raw tokens;
 //   finish (per token x head): the gated RMSNorm of O.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -174,99 +176,82 @@ __device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
     return v;
 }
 
-// Eight consecutive activations of one token, as loaded (16-byte aligned).
+// Four consecutive activations of one token, as loaded (aligned to their
+// size: 16 bytes FP32, 8 bytes BF16, 4 bytes FP8).
 template <int ACT>
-struct Raw8;
+struct Raw4;
 template <>
-struct Raw8<kF32> {
-    float4 a, b;
+struct Raw4<kF32> {
+    float4 a;
 };
 template <>
-struct Raw8<kBF16> {
-    uint4 u;
+struct Raw4<kBF16> {
+    uint2 u;
 };
 template <>
-struct Raw8<kFP8> {
-    uint2 u;                          // eight E4M3 bytes (8-byte aligned)
+struct Raw4<kFP8> {
+    uint32_t u;                       // four E4M3 bytes
 };
 
 template <int ACT>
-__device__ __forceinline__ Raw8<ACT> ld_raw8(const void* base, int64_t idx) {
-    Raw8<ACT> r;
-    if constexpr (ACT == kF32) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
-        r.a = p[0];
-        r.b = p[1];
-    } else if constexpr (ACT == kBF16) {
-        r.u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
-    } else {
-        r.u = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + idx);
-    }
+__device__ __forceinline__ Raw4<ACT> ld_raw4(const void* base, int64_t idx) {
+    Raw4<ACT> r;
+    if constexpr (ACT == kF32)
+        r.a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    else if constexpr (ACT == kBF16)
+        r.u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    else
+        r.u = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(base) + idx);
     return r;
 }
 
 // The same at byte offset `off` from `base`.
 template <int ACT>
-__device__ __forceinline__ Raw8<ACT> ld_raw8_at(const char* base, uint32_t off) {
-    Raw8<ACT> r;
-    if constexpr (ACT == kF32) {
-        const float4* p = reinterpret_cast<const float4*>(base + off);
-        r.a = p[0];
-        r.b = p[1];
-    } else if constexpr (ACT == kBF16) {
-        r.u = *reinterpret_cast<const uint4*>(base + off);
-    } else {
+__device__ __forceinline__ Raw4<ACT> ld_raw4_at(const char* base, uint32_t off) {
+    Raw4<ACT> r;
+    if constexpr (ACT == kF32)
+        r.a = *reinterpret_cast<const float4*>(base + off);
+    else if constexpr (ACT == kBF16)
         r.u = *reinterpret_cast<const uint2*>(base + off);
-    }
+    else
+        r.u = *reinterpret_cast<const uint32_t*>(base + off);
     return r;
 }
 
 // Zero unless ok, selected on the raw words.
 template <int ACT>
-__device__ __forceinline__ Raw8<ACT> keep_if(const Raw8<ACT>& r, bool ok) {
-    Raw8<ACT> o;
-    if constexpr (ACT == kF32) {
+__device__ __forceinline__ Raw4<ACT> keep_if(const Raw4<ACT>& r, bool ok) {
+    Raw4<ACT> o;
+    if constexpr (ACT == kF32)
         o.a = make_float4(ok ? r.a.x : 0.f, ok ? r.a.y : 0.f, ok ? r.a.z : 0.f, ok ? r.a.w : 0.f);
-        o.b = make_float4(ok ? r.b.x : 0.f, ok ? r.b.y : 0.f, ok ? r.b.z : 0.f, ok ? r.b.w : 0.f);
-    } else if constexpr (ACT == kBF16) {
-        o.u = make_uint4(ok ? r.u.x : 0u, ok ? r.u.y : 0u, ok ? r.u.z : 0u, ok ? r.u.w : 0u);
-    } else {
+    else if constexpr (ACT == kBF16)
         o.u = make_uint2(ok ? r.u.x : 0u, ok ? r.u.y : 0u);
-    }
+    else
+        o.u = ok ? r.u : 0u;
     return o;
 }
 
 // Widens to FP32.
 template <int ACT>
-__device__ __forceinline__ void unpack8(const Raw8<ACT>& r, float (&x)[8]) {
+__device__ __forceinline__ void unpack4(const Raw4<ACT>& r, float (&x)[4]) {
     if constexpr (ACT == kF32) {
         x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
-        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     } else if constexpr (ACT == kBF16) {
         x[0] = __uint_as_float(r.u.x << 16); x[1] = __uint_as_float(r.u.x & 0xffff0000u);
         x[2] = __uint_as_float(r.u.y << 16); x[3] = __uint_as_float(r.u.y & 0xffff0000u);
-        x[4] = __uint_as_float(r.u.z << 16); x[5] = __uint_as_float(r.u.z & 0xffff0000u);
-        x[6] = __uint_as_float(r.u.w << 16); x[7] = __uint_as_float(r.u.w & 0xffff0000u);
     } else {
-        float lo[4], hi[4];
-        e4m3x4_to_f32(r.u.x, lo);
-        e4m3x4_to_f32(r.u.y, hi);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            x[q] = lo[q];
-            x[4 + q] = hi[q];
-        }
+        e4m3x4_to_f32(r.u, x);
     }
 }
 
-// Raw channels [ch0, ch0 + 8) of one of q|k|v for local chunk token lt
+// Raw channels [ch0, ch0 + 4) of one of q|k|v for local chunk token lt
 // (-3 <= lt < 64): the packed input inside the sequence, the ring for
 // earlier positions >= 0; `ok` is false before position 0 and past the
 // chunk's end, where the value must count as zero.  Branch-free: the load
 // always goes to a valid address (the chunk's first token where `ok` is
 // false), so all of a lane's loads are in flight together.
 template <int ACT>
-__device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v, int h, int t0,
+__device__ __forceinline__ Raw4<ACT> raw4(const PrefillArgs& a, const SeqView& v, int h, int t0,
                                           int L, int lt, const void* src, int ch0, int ring_ch0,
                                           bool& ok) {
     const int gt = t0 + lt;
@@ -277,25 +262,25 @@ __device__ __forceinline__ Raw8<ACT> raw8(const PrefillArgs& a, const SeqView& v
     const int64_t idx_in = (int64_t)(v.lo + (ok && in_seq ? gt : t0)) * a.qkv_rs + h * PD + ch0;
     const int64_t idx_ring =
         (((int64_t)v.slot * kConvW + (p & (kConvW - 1))) * a.H + h) * (3 * PD) + ring_ch0;
-    return ld_raw8<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in);
+    return ld_raw4<ACT>(use_ring ? a.ring : src, use_ring ? idx_ring : idx_in);
 }
 
 // Conv of one of q|k|v for this lane's four tokens (tb..tb+3) and channels
-// [c0, c0 + 8), from the seven raw tokens tb-3..tb+3 and the channels' four
+// [c0, c0 + 4), from the seven raw tokens tb-3..tb+3 and the channels' four
 // taps; zero for tokens at or past L.  FP8 activations: times the tensor's
 // dequantisation scale `sc`, taken out of the sum.  Only the three raw
 // tokens before tb can lie before position 0 and must read as zero (`ok`);
 // a later raw token past the chunk's end feeds only outputs at or past L,
 // which are zeroed here whatever it holds.
 template <int ACT>
-__device__ __forceinline__ void conv4x8(const Raw8<ACT> (&r)[7], const bool (&ok)[3],
-                                        const float4 (&wt)[8], int tb, int L, float sc,
-                                        float (&c)[4][8]) {
-    float x[7][8];
+__device__ __forceinline__ void conv4x4(const Raw4<ACT> (&r)[7], const bool (&ok)[3],
+                                        const float4 (&wt)[4], int tb, int L, float sc,
+                                        float (&c)[4][4]) {
+    float x[7][4];
 #pragma unroll
-    for (int m = 0; m < 7; ++m) unpack8<ACT>(m < 3 ? keep_if<ACT>(r[m], ok[m]) : r[m], x[m]);
+    for (int m = 0; m < 7; ++m) unpack4<ACT>(m < 3 ? keep_if<ACT>(r[m], ok[m]) : r[m], x[m]);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
         const float4 w4 = wt[q];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -325,6 +310,13 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_mov<0x122>(x);   // row_ror:2
     x += dpp_mov<0x121>(x);   // row_ror:1
     return x;
+}
+
+// Sum over each half-wave of 32 lanes; every lane of the half gets the same
+// value (the two rows' sums meet through a swizzle of lane ^ 16).
+__device__ __forceinline__ float row32_sum(float x) {
+    x = row16_sum(x);
+    return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
 }
 
 __device__ __forceinline__ void ld4x2(const float* p0, const float* p1, float (&x)[8]) {
@@ -408,21 +400,21 @@ __device__ __forceinline__ ChunkItem next_item(const PrefillArgs& a, int n_slots
 // and beta (in the gate dtype) for its four tokens.
 template <int ACT>
 struct ChunkIn {
-    Raw8<ACT> rq[7], rk[7], rv[7];
-    Raw8<kGateAct<ACT>> ra[4];
+    Raw4<ACT> rq[7], rk[7], rv[7];
+    Raw4<kGateAct<ACT>> ra[4];
     uint32_t rb[4];                  // bits, widened where used (no wait here)
     bool okm[3];                     // raw tokens tb-3..tb-1: false where they count as zero
 };
 
 // Part PART of a lane's raw inputs: 0 q, 1 k, 2 v with alpha and beta.  The
 // three parts are issued at three points of a step, so that the loads of
-// the workgroup's four waves pass the address units in turn instead of all
+// the workgroup's eight waves pass the address units in turn instead of all
 // at once; `okm` is set by part 0.
 template <int ACT, int PART>
 __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const ChunkItem& it, int tb,
                                                 int c0, ChunkIn<ACT>& in) {
     const int h = it.h, t0 = it.t0, L = it.L;
-    Raw8<ACT>* dst = PART == 0 ? in.rq : (PART == 1 ? in.rk : in.rv);
+    Raw4<ACT>* dst = PART == 0 ? in.rq : (PART == 1 ? in.rk : in.rv);
     const void* src = PART == 0 ? a.q : (PART == 1 ? a.k : a.v);
     if (it.cc >= 1 && L == PC) {
         // Interior chunk: every conv token lies inside the sequence.  Each
@@ -435,7 +427,7 @@ __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const Chun
         const uint32_t off = (uint32_t)((size_t)tb * row_b + ((size_t)h * PD + c0) * ESZ);
         const char* xb = static_cast<const char*>(src) + row0 * row_b;
 #pragma unroll
-        for (int m = 0; m < 7; ++m) dst[m] = ld_raw8_at<ACT>(xb + m * row_b, off);
+        for (int m = 0; m < 7; ++m) dst[m] = ld_raw4_at<ACT>(xb + m * row_b, off);
         if constexpr (PART == 0) {
 #pragma unroll
             for (int m = 0; m < 3; ++m) in.okm[m] = true;
@@ -448,7 +440,7 @@ __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const Chun
             const uint32_t offb = (uint32_t)(((size_t)tb * a.H + h) * GESZ);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                in.ra[e] = ld_raw8_at<GACT>(ab + e * rowa_b, offa);
+                in.ra[e] = ld_raw4_at<GACT>(ab + e * rowa_b, offa);
                 in.rb[e] = GACT == kF32
                     ? *reinterpret_cast<const uint32_t*>(bb + e * a.H * GESZ + offb)
                     : *reinterpret_cast<const uint16_t*>(bb + e * a.H * GESZ + offb);
@@ -459,7 +451,7 @@ __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const Chun
 #pragma unroll
     for (int m = 0; m < 7; ++m) {
         bool ok;
-        dst[m] = raw8<ACT>(a, it.v, h, t0, L, tb - 3 + m, src, c0, PART * PD + c0, ok);
+        dst[m] = raw4<ACT>(a, it.v, h, t0, L, tb - 3 + m, src, c0, PART * PD + c0, ok);
         if (PART == 0 && m < 3) in.okm[m] = ok;
     }
     if constexpr (PART == 2) {
@@ -467,7 +459,7 @@ __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const Chun
         for (int e = 0; e < 4; ++e) {
             // past the chunk's end: alpha = 1, beta = 0 (loads clamped to a valid token)
             const int64_t row = (int64_t)(it.v.lo + t0 + min(tb + e, L - 1)) * a.H + h;
-            in.ra[e] = ld_raw8<kGateAct<ACT>>(a.alpha, row * PD + c0);
+            in.ra[e] = ld_raw4<kGateAct<ACT>>(a.alpha, row * PD + c0);
             in.rb[e] = ld_act_bits<kGateAct<ACT>>(a.beta, row);
         }
     }
@@ -481,11 +473,11 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
     load_chunk_part<ACT, 2>(a, it, tb, c0, in);
 }
 
-// The conv taps of channels [c0, c0 + 8) of head h, for q, k and v.
-__device__ __forceinline__ void load_taps(const PrefillArgs& a, int h, int c0, float4 (&wq)[8],
-                                          float4 (&wk)[8], float4 (&wv)[8]) {
+// The conv taps of channels [c0, c0 + 4) of head h, for q, k and v.
+__device__ __forceinline__ void load_taps(const PrefillArgs& a, int h, int c0, float4 (&wq)[4],
+                                          float4 (&wk)[4], float4 (&wv)[4]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 4; ++q) {
         const size_t wi = ((size_t)h * PD + c0 + q) * kConvW;
         wq[q] = *reinterpret_cast<const float4*>(a.wq + wi);
         wk[q] = *reinterpret_cast<const float4*>(a.wk + wi);
@@ -493,8 +485,13 @@ __device__ __forceinline__ void load_taps(const PrefillArgs& a, int h, int c0, f
     }
 }
 
+// Threads of a chunk workgroup: eight waves, two per SIMD, so that one
+// wave's LDS, matrix-core and memory latencies hide behind the other's
+// vector work.
+constexpr int kChunkThreads = 512;
+
 template <int ACT>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n_slots) {
+__global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArgs a, int n_slots) {
     // LDS regions (bytes), reused as the steps go:
     //   RA  kh * D4 [PC][LR]                    -> -W [PC][LR] (step 4)
     //   RB  qh * D4 [PC][LR]                    -> beta K_G transposed (step X)
@@ -529,16 +526,17 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     // Persistent: the workgroup takes items blockIdx.x, + gridDim.x, ...
     // The next item's inputs are requested in three parts during step 2b,
     // after the current item's convolutions have consumed theirs, and arrive
-    // during steps 2b-5.
-    constexpr bool kEarlyTaps = ACT != kF32;
+    // during steps 2b-5.  Lane l of wave w handles tokens 4 (2w + l / 32) ..
+    // + 3 and channels 4 (l % 32) .. + 3 in step 1.
+    constexpr bool kEarlyTaps = ACT == kFP8;
     ChunkItem it;
     ChunkIn<ACT> in;
-    float4 wtq[8], wtk[8], wtv[8];             // conv taps of the lane's channels
+    float4 wtq[4], wtk[4], wtv[4];             // conv taps of the lane's channels
     {
         const int tid = threadIdx.x, lane = tid & 63;
         // workgroup 0 validates every sequence once and reports the bad ones
         if (blockIdx.x == 0)
-            for (int sq = tid; sq < a.num_seqs; sq += 256) {
+            for (int sq = tid; sq < a.num_seqs; sq += kChunkThreads) {
                 SeqView sv;
                 seq_view(a, sq, true, sv);
             }
@@ -546,8 +544,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         none.idx = -1;
         it = next_item(a, n_slots, blockIdx.x, gridDim.x, none);
         if (it.idx < 0) return;
-        load_chunk_in<ACT>(a, it, 16 * (tid >> 6) + 4 * (lane >> 4), 8 * (lane & 15), in);
-        if constexpr (kEarlyTaps) load_taps(a, it.h, 8 * (lane & 15), wtq, wtk, wtv);
+        load_chunk_in<ACT>(a, it, 4 * (tid >> 5), 4 * (lane & 31), in);
+        if constexpr (kEarlyTaps) load_taps(a, it.h, 4 * (lane & 31), wtq, wtk, wtv);
     }
     for (;;) {
     // The thread index is passed through an empty assembly statement on each
@@ -558,54 +556,55 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     const int tid = tid_v, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, g = lane >> 4;
-    const int tb = 16 * wave + 4 * g;          // this lane's sub-block (step 1)
-    const int c0 = 8 * n;                      // and channels
+    const int tb = 4 * (tid >> 5);             // this lane's sub-block (step 1): tokens tb..tb+3
+    const int c0 = 4 * (lane & 31);            // and channels c0..c0+3
     const int h = it.h, L = it.L;
     const SeqView v = it.v;
     char* ws = static_cast<char*>(a.workspace) + ((size_t)chunk_slot(v.lo, it.s, it.cc) * H + h) * WS_B;
     ChunkItem nx;
 
-    // ---- 1. per lane: sub-block j = g of row block `wave` (tokens tb..tb+3),
-    // channels c0..c0+7: conv, L2 norms, decay products, in-sub-block pairs
-    float cv[4][8], bt[4];
+    // ---- 1. per lane: sub-block tb / 4 (tokens tb..tb+3; half-wave h32 of
+    // wave w holds sub-block 2w + h32), channels c0..c0+3: conv, L2 norms,
+    // decay products, in-sub-block pairs
+    float cv[4][4], bt[4];
     {
         if constexpr (!kEarlyTaps) load_taps(a, h, c0, wtq, wtk, wtv);
-        float qh[4][8], kh[4][8], al[4][8];
-        conv4x8<ACT>(in.rq, in.okm, wtq, tb, L, a.scale_q, qh);
+        float qh[4][4], kh[4][4], al[4][4];
+        conv4x4<ACT>(in.rq, in.okm, wtq, tb, L, a.scale_q, qh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sq = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
-            const float r = kSc / sqrtf(row16_sum(sq) + a.l2_eps);
+            for (int q = 0; q < 4; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
+            const float r = kSc / sqrtf(row32_sum(sq) + a.l2_eps);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) qh[e][q] *= r;
+            for (int q = 0; q < 4; ++q) qh[e][q] *= r;
         }
-        conv4x8<ACT>(in.rk, in.okm, wtk, tb, L, a.scale_k, kh);
+        conv4x4<ACT>(in.rk, in.okm, wtk, tb, L, a.scale_k, kh);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float sk = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sk = fmaf(kh[e][q], kh[e][q], sk);
-            const float r = kSc / sqrtf(row16_sum(sk) + a.l2_eps);
+            for (int q = 0; q < 4; ++q) sk = fmaf(kh[e][q], kh[e][q], sk);
+            const float r = kSc / sqrtf(row32_sum(sk) + a.l2_eps);
 #pragma unroll
-            for (int q = 0; q < 8; ++q) kh[e][q] *= r;
+            for (int q = 0; q < 4; ++q) kh[e][q] *= r;
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool live = tb + e < L;
-            unpack8<kGateAct<ACT>>(in.ra[e], al[e]);
+            unpack4<kGateAct<ACT>>(in.ra[e], al[e]);
             float bv = act_from_bits<kGateAct<ACT>>(in.rb[e]);
             if (a.gate_logits) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) al[e][q] = decay_from_logit(al[e][q]);
+                for (int q = 0; q < 4; ++q) al[e][q] = decay_from_logit(al[e][q]);
                 bv = write_from_logit(bv);
             }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) al[e][q] = live ? al[e][q] : 1.f;
+            for (int q = 0; q < 4; ++q) al[e][q] = live ? al[e][q] : 1.f;
             bt[e] = live ? bv : 0.f;
         }
-        conv4x8<ACT>(in.rv, in.okm, wtv, tb, L, a.scale_v, cv);
+        conv4x4<ACT>(in.rv, in.okm, wtv, tb, L, a.scale_v, cv);
 
         // every input of this item is consumed: find the next item (its
         // inputs are requested in three parts during step 2b)
@@ -617,28 +616,28 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             int ip = 0, ia = 0;
 #pragma unroll
             for (int ei = 0; ei < 4; ++ei) {
-                float d[8];
+                float d[4];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) d[q] = 1.f;
+                for (int q = 0; q < 4; ++q) d[q] = 1.f;
 #pragma unroll
                 for (int et = ei; et < 4; ++et) {
                     if (et > ei) {
 #pragma unroll
-                        for (int q = 0; q < 8; ++q) d[q] *= al[et][q];
+                        for (int q = 0; q < 4; ++q) d[q] *= al[et][q];
                     }
                     float sp = 0.f, sa = 0.f;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
+                    for (int q = 0; q < 4; ++q) {
                         const float kd = kh[ei][q] * d[q];
                         sp = fmaf(qh[et][q], kd, sp);
                         sa = fmaf(kh[et][q], kd, sa);
                     }
-                    pp[ip++] = row16_sum(sp);
-                    if (et > ei) pa[ia++] = row16_sum(sa);
+                    pp[ip++] = row32_sum(sp);
+                    if (et > ei) pa[ia++] = row32_sum(sa);
                 }
             }
         }
-        if (n == 0) {
+        if ((lane & 31) == 0) {
             // 4x4 sub-tiles on the diagonal, zeros above
             int ip = 0, ia = 0;
             float P4[4][4], A4[4][4];
@@ -667,64 +666,51 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         }
 
         // decay products inside the sub-block
-        float D4[4][8], E4[4][8];
+        float D4[4][4], E4[4][4];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < 4; ++q) {
             D4[0][q] = al[0][q];
             E4[3][q] = 1.f;
         }
 #pragma unroll
         for (int e = 1; e < 4; ++e)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) D4[e][q] = D4[e - 1][q] * al[e][q];
+            for (int q = 0; q < 4; ++q) D4[e][q] = D4[e - 1][q] * al[e][q];
 #pragma unroll
         for (int e = 2; e >= 0; --e)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) E4[e][q] = E4[e + 1][q] * al[e + 1][q];
+            for (int q = 0; q < 4; ++q) E4[e][q] = E4[e + 1][q] * al[e + 1][q];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float* kd = &KD[tb + e][c0];
-            float* qd = &QD[tb + e][c0];
-            float* ke = &KE[tb + e][c0];
-            *reinterpret_cast<float4*>(kd) = make_float4(kh[e][0] * D4[e][0], kh[e][1] * D4[e][1],
-                                                         kh[e][2] * D4[e][2], kh[e][3] * D4[e][3]);
-            *reinterpret_cast<float4*>(kd + 4) = make_float4(kh[e][4] * D4[e][4], kh[e][5] * D4[e][5],
-                                                             kh[e][6] * D4[e][6], kh[e][7] * D4[e][7]);
-            *reinterpret_cast<float4*>(qd) = make_float4(qh[e][0] * D4[e][0], qh[e][1] * D4[e][1],
-                                                         qh[e][2] * D4[e][2], qh[e][3] * D4[e][3]);
-            *reinterpret_cast<float4*>(qd + 4) = make_float4(qh[e][4] * D4[e][4], qh[e][5] * D4[e][5],
-                                                             qh[e][6] * D4[e][6], qh[e][7] * D4[e][7]);
-            *reinterpret_cast<float4*>(ke) = make_float4(kh[e][0] * E4[e][0], kh[e][1] * E4[e][1],
-                                                         kh[e][2] * E4[e][2], kh[e][3] * E4[e][3]);
-            *reinterpret_cast<float4*>(ke + 4) = make_float4(kh[e][4] * E4[e][4], kh[e][5] * E4[e][5],
-                                                             kh[e][6] * E4[e][6], kh[e][7] * E4[e][7]);
+            *reinterpret_cast<float4*>(&KD[tb + e][c0]) = make_float4(
+                kh[e][0] * D4[e][0], kh[e][1] * D4[e][1], kh[e][2] * D4[e][2], kh[e][3] * D4[e][3]);
+            *reinterpret_cast<float4*>(&QD[tb + e][c0]) = make_float4(
+                qh[e][0] * D4[e][0], qh[e][1] * D4[e][1], qh[e][2] * D4[e][2], qh[e][3] * D4[e][3]);
+            *reinterpret_cast<float4*>(&KE[tb + e][c0]) = make_float4(
+                kh[e][0] * E4[e][0], kh[e][1] * E4[e][1], kh[e][2] * E4[e][2], kh[e][3] * E4[e][3]);
         }
         *reinterpret_cast<float4*>(&T4[tb >> 2][c0]) =
             make_float4(D4[3][0], D4[3][1], D4[3][2], D4[3][3]);
-        *reinterpret_cast<float4*>(&T4[tb >> 2][c0 + 4]) =
-            make_float4(D4[3][4], D4[3][5], D4[3][6], D4[3][7]);
     }
     lds_sync();
 
-    // ---- 2a. wave w >= 1: suffix table AUX[o + j] = alpha over sub-blocks
-    // j+1 .. 4w-1, for j < 4w (the column factors of the tiles left of the
-    // diagonal block)
-    const int aux_o = 2 * wave * (wave - 1);
-    if (wave > 0) {
-        const int nj = 4 * wave;
+    // ---- 2a. suffix tables of row blocks rb = 1..3: AUX[2 rb (rb - 1) + j]
+    // = alpha over sub-blocks j+1 .. 4 rb - 1, for j < 4 rb (the column
+    // factors of the tiles left of the diagonal block).  Waves 1..6 take
+    // row block 1 + (w - 1) / 2, channel half (w - 1) % 2.
+    if (wave >= 1 && wave <= 6) {
+        const int rbk = 1 + ((wave - 1) >> 1);
+        const int aux_o = 2 * rbk * (rbk - 1), nj = 4 * rbk;
+        const int c = lane + 64 * ((wave - 1) & 1);
+        float t4v[12];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c = lane + 64 * half;
-            float t4v[12];
+        for (int jj = 0; jj < 12; ++jj) t4v[jj] = T4[jj][c];   // all reads in flight at once
+        float run = 1.f;
 #pragma unroll
-            for (int jj = 0; jj < 12; ++jj) t4v[jj] = T4[jj][c];   // all reads in flight at once
-            float run = 1.f;
-#pragma unroll
-            for (int jj = 11; jj >= 0; --jj) {
-                if (jj < nj) {
-                    AUX[aux_o + jj][c] = run;
-                    run *= t4v[jj];
-                }
+        for (int jj = 11; jj >= 0; --jj) {
+            if (jj < nj) {
+                AUX[aux_o + jj][c] = run;
+                run *= t4v[jj];
             }
         }
     }
@@ -737,12 +723,15 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     if (nx.idx >= 0) load_chunk_part<ACT, 0>(a, nx, tb, c0, in);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 2b. cross-sub-block entries of A and P on the matrix cores; wave w
-    // owns row block w.  Diagonal 16x16 block: adjacent sub-blocks through
-    // their common boundary ("adj"), sub-blocks two or three apart through
-    // the boundary before local sub-block 2 ("J2").  Tiles left of it:
-    // through the row block's first boundary.
-    {
+    // ---- 2b. cross-sub-block entries of A and P on the matrix cores.
+    // Waves 0-3: the diagonal 16x16 block of row block w.  Adjacent
+    // sub-blocks go through their common boundary ("adj"), sub-blocks two or
+    // three apart through the boundary before local sub-block 2 ("J2").
+    // Waves 4-7: the tiles left of the diagonal, through the row block's
+    // first boundary: wave 4 takes (2,0) and (2,1), wave 5 (3,0) and (3,1),
+    // wave 6 (3,2), wave 7 (1,0).  Every wave requests the next item's
+    // inputs in parts 1 and 2 between its products.
+    if (wave < 4) {
         const int t = 16 * wave + n;              // A-operand row of this lane
         const int i = 16 * wave + n;              // B-operand column of this lane
         f32x4_t aA1 = {0.f, 0.f, 0.f, 0.f}, aP1 = aA1, aA2 = aA1, aP2 = aA1;
@@ -793,12 +782,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 Am[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
                 Pm[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
             }
-        // Tiles left of the diagonal, spread so that no wave does more than
-        // two: wave 0 takes (2,0), (2,1); wave 1 (1,0); wave 2 (3,0); wave 3
-        // (3,1), (3,2).
-        const int rb = wave == 0 ? 2 : (wave == 1 ? 1 : 3);     // row block
-        const int bi0 = wave == 3 ? 1 : 0;
-        const int bi1 = wave == 0 ? 2 : (wave == 3 ? 3 : 1);   // exclusive
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
+    } else {
+        const int rb = wave == 4 ? 2 : (wave == 7 ? 1 : 3);     // row block
+        const int bi0 = wave == 6 ? 2 : 0;
+        const int bi1 = wave <= 5 ? 2 : (wave == 6 ? 3 : 1);    // exclusive
         {
             // row operand: scaled to the row block's first token
             const int tr0 = 16 * rb + n;
@@ -826,7 +815,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 xq[kb] = split_op(rq);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
+            if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
             __builtin_amdgcn_sched_barrier(0);
             for (int bi = bi0; bi < bi1; ++bi) {
                 const int ic = 16 * bi + n;
@@ -852,6 +841,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 }
             }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
     }
     lds_sync();
 
@@ -865,7 +856,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
             run *= T4[jj][tid];
         }
         reinterpret_cast<float*>(ws + GAM_OFF)[tid] = run;
-    } else {
+    } else if (tid < 2 * PD) {
         const int c = tid - PD;
         float run = 1.f;
 #pragma unroll
@@ -877,9 +868,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
     lds_sync();
 
     // ---- 3b. wave 0: T_bb = (I + A_bb)^-1 for the four diagonal blocks,
-    // in place (lane = block * 16 + column), then the P fragments and the
-    // last scaled-Q and scaled-K fragments.  Waves 1..3: the other scaled-Q
-    // and scaled-K fragments to the workspace.
+    // in place (lane = block * 16 + column).  Waves 1..7: the scaled-Q,
+    // scaled-K and P fragments to the workspace, five or six each.
     // (e(t,-1) * qh) rows, A operand
     auto q_frag = [&](int f) {
         const int tt = f >> 2, kb = f & 3;
@@ -903,6 +893,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         }
         st_frag(ws + kb * HALF_B + frag_k(ct) * FRAG_B, lane, split_op(x));
     };
+    // P rows, A operand: the two tiles of half 0 and the four of half 1
+    auto p_frag = [&](int p) {
+        const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
+        const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
+        float xp[8];
+        ld4x2(&Pm[t][cb], &Pm[t][cb + 16], xp);
+        st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(xp));
+    };
     if (wave == 0) {
         const int b = lane >> 4, ic = lane & 15;
         float x[16];
@@ -923,37 +921,34 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) Am[16 * b + t][16 * b + ic] = x[t];
-        // then the six P fragments (rows, A operand)
-#pragma unroll
-        for (int p = 0; p < 6; ++p) {
-            const int hh = p >= 2, u = hh ? (p - 2) >> 1 : p, kb = hh ? (p & 1) : 0;
-            const int tt = 2 * hh + u, t = 16 * tt + n, cb = 32 * kb + 4 * g;
-            float xp[8];
-            ld4x2(&Pm[t][cb], &Pm[t][cb + 16], xp);
-            st_frag(ws + hh * HALF_B + frag_p(hh, u, kb) * FRAG_B, lane, split_op(xp));
-        }
-        q_frag(15);
-        k_frag(15);
     } else {
-        // Static, unrolled loops (no branch between fragments) so that the
-        // LDS reads of later fragments overlap the work of earlier ones.
-        // Wave 1 + w1 takes fragments w1, w1 + 3, ..., w1 + 12 of each kind.
-        const int w1 = wave - 1;
-#pragma unroll
-        for (int i = 0; i < 5; ++i) q_frag(w1 + 3 * i);
-#pragma unroll
-        for (int i = 0; i < 5; ++i) k_frag(w1 + 3 * i);
+        // Wave w takes scaled-Q fragments w-1, w+6, w+13, scaled-K fragments
+        // (w+1) mod 7 + 0, 7, 14 (those below 16), and waves 3-5 two P
+        // fragments each: 5 or 6 fragments per wave.  The guards are
+        // uniform, and the first two of each kind are unconditional so that
+        // their LDS reads overlap.
+        const int wq = wave - 1, wk = (wave + 1) % 7;
+        q_frag(wq);
+        q_frag(wq + 7);
+        if (wq + 14 < 16) q_frag(wq + 14);
+        k_frag(wk);
+        k_frag(wk + 7);
+        if (wk + 14 < 16) k_frag(wk + 14);
+        if (wave >= 3 && wave <= 5) {
+            p_frag(2 * (wave - 3));
+            p_frag(2 * (wave - 3) + 1);
+        }
     }
     lds_sync();
 
     // ---- X. beta_t K_G = beta_t kh_t e(t,-1) and beta_t V, transposed to
     // [channel][token] (swizzled) so that the solve reads 4 tokens at once
     {
-        const int c = tid & (PD - 1), th = tid >> 7;
-        float kd[8][4], bq[8][4], pre[8];
+        const int c = tid & (PD - 1), th = tid >> 7;   // tokens 16 th .. 16 th + 15
+        float kd[4][4], bq[4][4], pre[4];
 #pragma unroll
-        for (int t4 = 0; t4 < 8; ++t4) {
-            const int t = 32 * th + 4 * t4;
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int t = 16 * th + 4 * t4;
             pre[t4] = AUX[t >> 2][c];
             const float4 b4 = *reinterpret_cast<const float4*>(&bet[t]);
             bq[t4][0] = b4.x; bq[t4][1] = b4.y; bq[t4][2] = b4.z; bq[t4][3] = b4.w;
@@ -965,8 +960,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
         // would otherwise wait for each read before the next write)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t4 = 0; t4 < 8; ++t4) {
-            const int t = 32 * th + 4 * t4;
+        for (int t4 = 0; t4 < 4; ++t4) {
+            const int t = 16 * th + 4 * t4;
             *reinterpret_cast<float4*>(&RWt[swz(c, t)]) =
                 make_float4(bq[t4][0] * kd[t4][0] * pre[t4], bq[t4][1] * kd[t4][1] * pre[t4],
                             bq[t4][2] * kd[t4][2] * pre[t4], bq[t4][3] * kd[t4][3] * pre[t4]);
@@ -975,29 +970,32 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
         for (int e = 0; e < 4; ++e) bs[e] = bt[e] * kSc;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < 4; ++q)
             *reinterpret_cast<float4*>(&VT[swz(c0 + q, tb)]) =
                 make_float4(bs[0] * cv[0][q], bs[1] * cv[1][q], bs[2] * cv[2][q], bs[3] * cv[3][q]);
     }
     lds_sync();
 
-    // the next item's conv taps (this item's were last used in step 1); FP32
-    // inputs take twice the registers, and there the taps are loaded in step 1
+    // the next item's conv taps (this item's were last used in step 1), with
+    // FP8 inputs only: with FP32 or BF16 inputs the raw tokens held for the
+    // next item leave too few of the 256 registers per lane that two waves
+    // per SIMD allow, and the taps are loaded at the start of step 1 instead
     if (kEarlyTaps && nx.idx >= 0) load_taps(a, nx.h, c0, wtq, wtk, wtv);
 
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
     // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns
-    // column tiles 4w..4w+3 of the 256 columns (waves 0-1: W, 2-3: Ut).
+    // column tiles 2w, 2w+1 of the 256 columns (waves 0-3: W, 4-7: Ut).
     {
-        const bool isW = wave < 2;
+        constexpr int NU = 2;                     // column tiles per wave
+        const bool isW = wave < 4;
         // Value columns: the solve runs on R scaled by the column's power-of-
         // two scale (largest |beta v| over the chunk in [1, 2)); X comes out
         // scaled by the same factor and is unscaled on its way out.
-        float sg[4] = {1.f, 1.f, 1.f, 1.f}, isg[4] = {1.f, 1.f, 1.f, 1.f};
+        float sg[NU] = {1.f, 1.f}, isg[NU] = {1.f, 1.f};
         if (!isW) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = 16 * ((4 * wave + u) & 7) + n;
+            for (int u = 0; u < NU; ++u) {
+                const int c = 16 * ((NU * wave + u) & 7) + n;
                 float m = 0.f;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -1008,14 +1006,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 pow2_scale(col_max4(m) * kInvSc, sg[u], isg[u]);
             }
         }
-        f32x4_t X[4][4];
-        SplitOp4 Xs[3][4];
+        f32x4_t X[4][NU];
+        SplitOp4 Xs[3][NU];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            f32x4_t acc[4];
+            f32x4_t acc[NU];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int c = 16 * ((4 * wave + u) & 7) + n;
+            for (int u = 0; u < NU; ++u) {
+                const int c = 16 * ((NU * wave + u) & 7) + n;
                 acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]) *
                          sg[u];
             }
@@ -1024,7 +1022,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 const float av[4] = {-a4.x * kSc, -a4.y * kSc, -a4.z * kSc, -a4.w * kSc};
                 const SplitOp4 sa = split_op4(av);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc[u] = mma3(sa, Xs[0][u], acc[u]);
+                for (int u = 0; u < NU; ++u) acc[u] = mma3(sa, Xs[0][u], acc[u]);
             } else if (b >= 2) {
                 float av[8];
                 ld4x2(&Am[16 * b + n][4 * g], &Am[16 * b + n][16 + 4 * g], av);
@@ -1032,7 +1030,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                 for (int q = 0; q < 8; ++q) av[q] = -av[q] * kSc;
                 const SplitOp sa = split_op(av);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < NU; ++u) {
                     SplitOp xb;
                     xb.hi = __builtin_shufflevector(Xs[0][u].hi, Xs[1][u].hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     xb.lo = __builtin_shufflevector(Xs[0][u].lo, Xs[1][u].lo, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -1043,14 +1041,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
                     const float a3[4] = {-a4.x * kSc, -a4.y * kSc, -a4.z * kSc, -a4.w * kSc};
                     const SplitOp4 sa3 = split_op4(a3);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[u] = mma3(sa3, Xs[2][u], acc[u]);
+                    for (int u = 0; u < NU; ++u) acc[u] = mma3(sa3, Xs[2][u], acc[u]);
                 }
             }
             const float4 t4 = *reinterpret_cast<const float4*>(&Am[16 * b + n][16 * b + 4 * g]);
             const float tv[4] = {t4.x * kScW, t4.y * kScW, t4.z * kScW, t4.w * kScW};
             const SplitOp4 st = split_op4(tv);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 X[b][u] = mma3(st, split_op4(acc[u] * kInvSc), f32x4_t{0.f, 0.f, 0.f, 0.f}) * kInvScW;
                 if (b < 3) Xs[b][u] = split_op4(X[b][u]);
             }
@@ -1059,15 +1057,15 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 #pragma unroll
             for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int c = 16 * (4 * wave + u) + n;
+                for (int u = 0; u < NU; ++u) {
+                    const int c = 16 * (NU * wave + u) + n;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) Wn[16 * b + 4 * g + r][c] = -X[b][u][r];
                 }
         } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int j16 = 4 * (wave - 2) + u;
+            for (int u = 0; u < NU; ++u) {
+                const int j16 = NU * (wave - 4) + u;
                 float m = 0.f;
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
@@ -1087,8 +1085,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, int n
 
     // ---- 5. -W fragments (A operand, k = key channel in pairing order)
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-        const int f = wave + 4 * k4;
+    for (int k4 = 0; k4 < 2; ++k4) {
+        const int f = wave + 8 * k4;
         const int tt = f >> 2, kb = f & 3;
         const int t = 16 * tt + n, cb = 32 * kb + 4 * g;
         float x[8];
@@ -1819,7 +1817,7 @@ static int launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
         // on some workgroups.
         int64_t grid = std::min<int64_t>(nchunk, chunk_grid());
         while (grid > 2 && !is_prime(grid)) --grid;
-        hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)grid), dim3(256), 0,
+        hipLaunchKernelGGL((prefill_chunk_kernel<ACT>), dim3((unsigned)grid), dim3(kChunkThreads), 0,
                            stream, a, (int)n_slots);
     }
     if (sgrid > 0)
