@@ -576,7 +576,7 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
             float sq = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) sq = fmaf(qh[e][q], qh[e][q], sq);
-            const float r = kSc / sqrtf(row32_sum(sq) + a.l2_eps);
+            const float r = kSc * __builtin_amdgcn_rsqf(row32_sum(sq) + a.l2_eps);
 #pragma unroll
             for (int q = 0; q < 4; ++q) qh[e][q] *= r;
         }
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
             float sk = 0.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) sk = fmaf(kh[e][q], kh[e][q], sk);
-            const float r = kSc / sqrtf(row32_sum(sk) + a.l2_eps);
+            const float r = kSc * __builtin_amdgcn_rsqf(row32_sum(sk) + a.l2_eps);
 #pragma unroll
             for (int q = 0; q < 4; ++q) kh[e][q] *= r;
         }
@@ -983,40 +983,34 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     if (kEarlyTaps && nx.idx >= 0) load_taps(a, nx.h, c0, wtq, wtk, wtv);
 
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
-    // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns
-    // column tiles 2w, 2w+1 of the 256 columns (waves 0-3: W, 4-7: Ut).
+    // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns one
+    // column tile of each: u = 0 the W tile of key channels 16w..16w+15, u = 1
+    // the Ut tile of value channels 16w..16w+15, so the two waves of a SIMD
+    // carry the same work.
     {
-        constexpr int NU = 2;                     // column tiles per wave
-        const bool isW = wave < 4;
+        constexpr int NU = 2;
+        const int cw = 16 * wave + n;             // the lane's column in both tiles
         // Value columns: the solve runs on R scaled by the column's power-of-
         // two scale (largest |beta v| over the chunk in [1, 2)); X comes out
         // scaled by the same factor and is unscaled on its way out.
-        float sg[NU] = {1.f, 1.f}, isg[NU] = {1.f, 1.f};
-        if (!isW) {
+        float sgv, isgv;
+        {
+            float m = 0.f;
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int c = 16 * ((NU * wave + u) & 7) + n;
-                float m = 0.f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(&VT[swz(c, 16 * b + 4 * g)]);
-                    m = fmaxf(m, fmaxf(fmaxf(fabsf(r4[0]), fabsf(r4[1])),
-                                       fmaxf(fabsf(r4[2]), fabsf(r4[3]))));
-                }
-                pow2_scale(col_max4(m) * kInvSc, sg[u], isg[u]);
+            for (int b = 0; b < 4; ++b) {
+                const f32x4_t r4 = *reinterpret_cast<const f32x4_t*>(&VT[swz(cw, 16 * b + 4 * g)]);
+                m = fmaxf(m, fmaxf(fmaxf(fabsf(r4[0]), fabsf(r4[1])),
+                                   fmaxf(fabsf(r4[2]), fabsf(r4[3]))));
             }
+            pow2_scale(col_max4(m) * kInvSc, sgv, isgv);
         }
         f32x4_t X[4][NU];
         SplitOp4 Xs[3][NU];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             f32x4_t acc[NU];
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int c = 16 * ((NU * wave + u) & 7) + n;
-                acc[u] = *reinterpret_cast<const f32x4_t*>(&(isW ? RWt : VT)[swz(c, 16 * b + 4 * g)]) *
-                         sg[u];
-            }
+            acc[0] = *reinterpret_cast<const f32x4_t*>(&RWt[swz(cw, 16 * b + 4 * g)]);
+            acc[1] = *reinterpret_cast<const f32x4_t*>(&VT[swz(cw, 16 * b + 4 * g)]) * sgv;
             if (b == 1) {
                 const float4 a4 = *reinterpret_cast<const float4*>(&Am[16 + n][4 * g]);
                 const float av[4] = {-a4.x * kSc, -a4.y * kSc, -a4.z * kSc, -a4.w * kSc};
@@ -1053,33 +1047,23 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
                 if (b < 3) Xs[b][u] = split_op4(X[b][u]);
             }
         }
-        if (isW) {
+        // the W tile to LDS (negated), the Ut tile to the workspace
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    const int c = 16 * (NU * wave + u) + n;
+            for (int r = 0; r < 4; ++r) Wn[16 * b + 4 * g + r][cw] = -X[b][0][r];
+        float m = 0.f;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) Wn[16 * b + 4 * g + r][c] = -X[b][u][r];
-                }
-        } else {
-#pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                const int j16 = NU * (wave - 4) + u;
-                float m = 0.f;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int hh = b >> 1, uu = b & 1;
-                    const f32x4_t x = X[b][u] * isg[u];
-                    *reinterpret_cast<f32x4_t*>(ws + UT_OFF +
-                                                ((((hh * 8 + j16) * 2 + uu) * 64 + lane) * 16)) = x;
-                    m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
-                }
-                // the column's largest |Ut| over the chunk, for the state pass's scale
-                m = col_max4(m);
-                if (g == 0) reinterpret_cast<float*>(ws + UTMAX_OFF)[16 * j16 + n] = m;
-            }
+        for (int b = 0; b < 4; ++b) {
+            const int hh = b >> 1, uu = b & 1;
+            const f32x4_t x = X[b][1] * isgv;
+            *reinterpret_cast<f32x4_t*>(ws + UT_OFF +
+                                        ((((hh * 8 + wave) * 2 + uu) * 64 + lane) * 16)) = x;
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
         }
+        // the column's largest |Ut| over the chunk, for the state pass's scale
+        m = col_max4(m);
+        if (g == 0) reinterpret_cast<float*>(ws + UTMAX_OFF)[cw] = m;
     }
     lds_sync();
 
