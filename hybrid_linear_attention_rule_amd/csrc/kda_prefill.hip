@@ -1320,9 +1320,10 @@ __device__ __forceinline__ void put_half_split(f16x8_t* hi, f16x8_t* lo, int lan
     reinterpret_cast<f16x4_t*>(&lo[lane])[r] = x.lo;
 }
 
-// acc[j] += sum over four 32-deep k blocks of fa[kb] * b[j][kb] for two
-// column tiles j, one accumulator per (pass, tile): six independent chains.
-// The hi*hi pass starts from acc.
+// acc[j] += sum over the 32-deep k blocks K0..K0+NK-1 of fa[kb] * b[j][kb]
+// for two column tiles j, one accumulator per (pass, tile): six independent
+// chains.  The hi*hi pass starts from acc.
+template <int K0 = 0, int NK = 4>
 __device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&b)[2][4],
                                         f32x4_t (&acc)[2]) {
     f32x4_t pa[3][2];
@@ -1333,7 +1334,7 @@ __device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&
         pa[2][j] = acc[j];
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = K0; kb < K0 + NK; ++kb)
         three_passes([&](auto P) {
             constexpr int pp = decltype(P)::value;
 #pragma unroll
@@ -1374,19 +1375,20 @@ constexpr int kStateThreads = 384;
 // O wave r computes row tile r of O = Qg S + P U for both column tiles and
 // stores it.  One barrier per half keeps the buffers in step.
 //
-// Value columns carry a power-of-two scale per chunk (pow2_scale of the
-// column's largest magnitude over the chunk's start state and its Ut): the
-// U/S waves trade their halves' column maxima through LDS before splitting
-// the state, and the O waves read the scale after the chunk's first barrier.
-// S is held unscaled between chunks.
+// Value columns carry power-of-two scales (pow2_scale).  Each U/S wave
+// splits its channel half of the chunk's start state scaled by its own
+// column maxima, and leaves those maxima in LDS beside the split blocks.
+// After the chunk's first barrier every wave forms the chunk's common column
+// scale from both halves' maxima and the chunk's largest |Ut|: U and O are
+// accumulated at that scale, each state half's partial product brought to it
+// by an exact power of two.  S is held unscaled between chunks.
 template <int ACT, int ST>
 __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char hbuf[2][SBUF_B];
     __shared__ StateX X;
     __shared__ int xflag[2];                      // per row tile: last half published
-    __shared__ int mflag[2];                      // per U/S wave: last chunk scale published
-    __shared__ float xmax[2][2][16];              // [U/S wave][column tile][column]
-    __shared__ float xisg[2][16];                 // 1 / scale of the chunk's columns
+    __shared__ float xmax[2][2][16];              // [U/S wave][column tile][column]: largest
+                                                  // |S| over the wave's channel half
     __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1395,7 +1397,6 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
     const int r = wave & 1;                       // row tile (U/S channel half; loader index)
     const int H = a.H;
     if (tid < 2) xflag[tid] = 0;
-    if (tid >= 2 && tid < 4) mflag[tid - 2] = 0;
     lds_sync();                                   // the flags before any wave uses them
     // The half buffers are filled only by assembly loads; this store, which
     // never runs (num_seqs >= 1), keeps the compiler from treating them as
@@ -1478,20 +1479,10 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     }
         }
         bool stalled = false;
-        // the chunk's largest |Ut| in each of the lane's two value columns
-        auto ld_utmax = [&](int c, float (&m)[2]) {
-            const float* p = reinterpret_cast<const float*>(cws(c) + UTMAX_OFF);
-            m[0] = p[jc[0]];
-            m[1] = p[jc[1]];
-        };
-        float mut[2], mut_next[2];
-        ld_utmax(0, mut);
-        // the chunk's column scales: both U/S waves take the largest |S| over
-        // their channel halves, trade them through LDS, and combine them with
-        // the chunk's largest |Ut| into the same power of two
-        float sg[2], isg[2];
-        auto set_scale = [&](int cc) {
-            float m[2];
+        // own split scale: the largest |S| of each value column over this
+        // wave's channel half, left in LDS for the other waves
+        float so[2], iso[2];
+        auto own_scale = [&]() {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float x = 0.f;
@@ -1499,31 +1490,25 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) x = fmaxf(x, fabsf(S[j][i][e]));
-                m[j] = col_max4(x);
-                if (g == 0) xmax[r][j][n] = m[j];
-            }
-            publish_half(&mflag[r], cc + 1);
-            stalled |= !await_half(&mflag[1 - r], cc + 1);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                pow2_scale(fmaxf(fmaxf(m[j], xmax[1 - r][j][n]), mut[j]), sg[j], isg[j]);
-                if (r == 0 && g == 0) xisg[j][n] = isg[j];
+                x = col_max4(x);
+                if (g == 0) xmax[r][j][n] = x;
+                pow2_scale(x, so[j], iso[j]);
             }
         };
-        // the B operands of the U product, own k blocks 2r, 2r+1 in slots 0,
-        // 1 (from registers) and the other wave's in slots 2, 3 (from LDS),
-        // all scaled by the columns' scales
+        // the B operands of the U product: own k blocks 2r, 2r+1 in slots 0,
+        // 1 (from registers, at the own scale) and the other wave's in slots
+        // 2, 3 (from LDS, at its scale)
         SplitOp sb[2][4];
         auto make_own = [&]() {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
-                    sb[j][m] = split_pair(S[j][2 * m] * sg[j], S[j][2 * m + 1] * sg[j]);
+                    sb[j][m] = split_pair(S[j][2 * m] * so[j], S[j][2 * m + 1] * so[j]);
                     put_split(X.sb_hi[j][2 * r + m], X.sb_lo[j][2 * r + m], lane, sb[j][m]);
                 }
         };
-        set_scale(0);
+        own_scale();
         make_own();
         auto get_other = [&]() {
 #pragma unroll
@@ -1533,6 +1518,22 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     sb[j][2 + m] = get_split(X.sb_hi[j][2 * (1 - r) + m],
                                              X.sb_lo[j][2 * (1 - r) + m], lane);
         };
+        // the chunk's common column scale sg (largest of both halves' |S| and
+        // the chunk's |Ut|) and the factors that bring each half's partial
+        // products to it (powers of two, at most 1)
+        float sg[2], isg[2], rown[2], roth[2];
+        auto set_scale = [&]() {
+            const float* utm = reinterpret_cast<const float*>(hbuf[0] + UTMAX_OFF);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float mo = xmax[1 - r][j][n], mu = utm[jc[j]];
+                float s1, is1;
+                pow2_scale(mo, s1, is1);
+                pow2_scale(fmaxf(fmaxf(xmax[r][j][n], mo), mu), sg[j], isg[j]);
+                rown[j] = sg[j] * iso[j];
+                roth[j] = sg[j] * is1;
+            }
+        };
         // row tile r of this half's U (accumulated at 2^8 times the column
         // scales), split, to LDS
         auto u_tile = [&](const char* buf) {
@@ -1540,15 +1541,16 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 w[m] = ld_frag(buf, frag_w(r, m < 2 ? 2 * r + m : 2 * (1 - r) + m - 2), lane);
-            f32x4_t acc[2];
+            f32x4_t acc[2], ao[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, at[2] = {ao[0], ao[1]};
+            prod4x2<0, 2>(w, sb, ao);
+            prod4x2<2, 2>(w, sb, at);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j) {
                 acc[j] = *reinterpret_cast<const f32x4_t*>(buf + SBUF_UT + (2 * j + r) * 1024 +
-                                                           lane * 16) * (kScW * sg[j]);
-            prod4x2(w, sb, acc);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
+                                                           lane * 16) * (kScW * sg[j]) +
+                         ao[j] * rown[j] + at[j] * roth[j];
                 put_half_split(X.ub_hi[j], X.ub_lo[j], lane, r, split_op4(acc[j] * kInvScW));
+            }
         };
         // channel tiles 4r.. of S += Kc^T U for both column tiles (at 2^12)
         auto s_update = [&](const char* buf, f32x4_t (&Sn)[2][4]) {
@@ -1566,9 +1568,9 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             });
         };
         for (int cc = 0; cc < nch; ++cc) {
-            if (cc + 1 < nch) ld_utmax(cc + 1, mut_next);       // used at the chunk's end
             // ======== first half: tokens 0..31 of the chunk ========
             lds_sync();                                            // H0
+            set_scale();
             get_other();
             u_tile(hbuf[0]);
             publish_half(&xflag[r], 2 * cc + 1);
@@ -1593,10 +1595,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * (kInvSc * isg[j]);
-            if (cc + 1 < nch) {                           // the next chunk's scale and split state
-                mut[0] = mut_next[0];
-                mut[1] = mut_next[1];
-                set_scale(cc + 1);
+            if (cc + 1 < nch) {                           // the next chunk's split state
+                own_scale();
                 make_own();
             }
         }
@@ -1638,11 +1638,32 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             // ======== first half ========
             lds_sync();                                            // H0
             store_o();
-            // O comes out at 2^12 times the chunk's column scales; the query
-            // scale multiplies it here
-            float osc[2];
+            // O comes out at 2^12 times the chunk's common column scales; the
+            // query scale multiplies it here.  The state blocks of U/S wave 0
+            // (k blocks 0, 1) and wave 1 (2, 3) carry their own scales.
+            float osc[2], r0[2], r1[2];
+            {
+                const float* utm = reinterpret_cast<const float*>(hbuf[0] + UTMAX_OFF);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) osc[j] = a.q_scale * (kInvSc * xisg[j][n]);
+                for (int j = 0; j < 2; ++j) {
+                    const float m0 = xmax[0][j][n], m1 = xmax[1][j][n];
+                    float s0, is0, s1, is1, su, isu;
+                    pow2_scale(m0, s0, is0);
+                    pow2_scale(m1, s1, is1);
+                    pow2_scale(fmaxf(fmaxf(m0, m1), utm[jc[j]]), su, isu);
+                    osc[j] = a.q_scale * (kInvSc * isu);
+                    r0[j] = su * is0;
+                    r1[j] = su * is1;
+                }
+            }
+            // O = (e(t,-1) q) S, both halves brought to the common scale
+            auto qs = [&](f32x4_t (&O)[2]) {
+                f32x4_t o0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, o1[2] = {o0[0], o0[1]};
+                prod4x2<0, 2>(fq, sb, o0);
+                prod4x2<2, 2>(fq, sb, o1);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) O[j] = o0[j] * r0[j] + o1[j] * r1[j];
+            };
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1650,9 +1671,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     sb[j][kb] = get_split(X.sb_hi[j][kb], X.sb_lo[j][kb], lane);
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[0], frag_q(r, kb), lane);
-            // O = (e(t,-1) q) S
-            f32x4_t O[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            prod4x2(fq, sb, O);
+            f32x4_t O[2];
+            qs(O);
             SplitOp fp0 = ld_frag(hbuf[0], frag_p(0, r, 0), lane);
             stalled |= !await_half(&xflag[0], 2 * cc + 1);
             stalled |= !await_half(&xflag[1], 2 * cc + 1);
@@ -1674,8 +1694,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[1], frag_q(r, kb), lane);
             fp0 = ld_frag(hbuf[1], frag_p(1, r, 0), lane);
             SplitOp fp1 = ld_frag(hbuf[1], frag_p(1, r, 1), lane);
-            O[0] = O[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            prod4x2(fq, sb, O);
+            qs(O);
             three_passes([&](auto P) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
