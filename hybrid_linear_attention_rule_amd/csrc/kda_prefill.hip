@@ -170,9 +170,16 @@ __device__ __forceinline__ bool seq_view(const PrefillArgs& a, int s, bool repor
 // stores to global memory, where the compiler would make a vector load
 // (assuming a store may alias it) and wait behind every outstanding vector
 // access, stores included.
+// Every caller passes a uniform address; it is read through readfirstlane so
+// that it sits in scalar registers even where the compiler keeps it in
+// vector ones.
 __device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    const int32_t* q = reinterpret_cast<const int32_t*>(lo | (hi << 32));
     int32_t v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p));
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q));
     return v;
 }
 
@@ -357,12 +364,25 @@ struct ChunkItem {
 // grow with s when cu_seqlens is monotone); its bounds are then checked.
 // `prev` (a checked item, or idx < 0) answers slots of its own sequence
 // without any load.
+// Workgroup-uniform values, stated as such: the direct-to-LDS loads' inline
+// assembly elsewhere in the chunk kernel otherwise leads the compiler to keep
+// the item search in vector registers.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uni(int64_t x) {
+    const uint64_t lo = (uint32_t)uni((int)(uint32_t)x), hi = (uint32_t)uni((int)(uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(lo | (hi << 32));
+}
+__device__ __forceinline__ ChunkItem uni(const ChunkItem& it) {
+    return ChunkItem{uni(it.idx), uni(it.cc), uni(it.s), uni(it.h), uni(it.t0), uni(it.L),
+                     SeqView{uni(it.v.lo), uni(it.v.len), uni(it.v.slot), uni(it.v.pos)}};
+}
+
 __device__ __forceinline__ ChunkItem next_item(const PrefillArgs& a, int n_slots, int64_t i,
                                                int64_t step, const ChunkItem& prev) {
     const int64_t total = (int64_t)n_slots * a.H;
     ChunkItem it;
     it.idx = -1;
-    for (; i < total; i += step) {
+    for (i = uni(i); i < total; i = uni(i + step)) {
         const int slot = n_slots - 1 - (int)(i / a.H);
         const int h = (int)(i % a.H);
         if (prev.idx >= 0) {
@@ -473,15 +493,22 @@ __device__ __forceinline__ void load_chunk_in(const PrefillArgs& a, const ChunkI
     load_chunk_part<ACT, 2>(a, it, tb, c0, in);
 }
 
-// The conv taps of channels [c0, c0 + 4) of head h, for q, k and v.
-__device__ __forceinline__ void load_taps(const PrefillArgs& a, int h, int c0, float4 (&wq)[4],
-                                          float4 (&wk)[4], float4 (&wv)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const size_t wi = ((size_t)h * PD + c0 + q) * kConvW;
-        wq[q] = *reinterpret_cast<const float4*>(a.wq + wi);
-        wk[q] = *reinterpret_cast<const float4*>(a.wk + wi);
-        wv[q] = *reinterpret_cast<const float4*>(a.wv + wi);
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// The conv taps of head h (q, k and v, 128 channels of four FP32 taps each:
+// 6 KB) into LDS at dst as [tensor][channel] float4.  Waves 0-5 move 1 KB
+// each, lane l 16 bytes, straight from global memory to LDS (M0 holds the
+// wave's LDS destination); the caller waits for them (s_waitcnt vmcnt(0))
+// before a barrier publishes them.
+__device__ __forceinline__ void dma_taps(const PrefillArgs& a, int h, char* dst, int wave,
+                                         int lane) {
+    if (wave < 6) {
+        const float* w = wave < 2 ? a.wq : (wave < 4 ? a.wk : a.wv);
+        const char* src = reinterpret_cast<const char*>(w + ((size_t)h * PD + 64 * (wave & 1)) * kConvW);
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src + lane * 16), "{m0}"((lds_char_t*)(dst + 1024 * wave))
+                     : "memory");
     }
 }
 
@@ -502,7 +529,8 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     //   operand scale, which step 1 puts into the norm factors of q and k)
     //   RF  alpha product over each sub-block [NSB][PD]
     //   RG  step 2: per-wave suffix tables; from step 3a: prefix | suffix
-    //       products over whole sub-blocks [2 NSB][PD]
+    //       products over whole sub-blocks [2 NSB][PD]; from step X to the
+    //       next item's step 1: that item's conv taps [3][PD] float4
     //   RH  beta [PC]
     // D4 = alpha over the sub-block start..t, E4 = alpha over t+1..sub-block end.
     constexpr int RA = 0, RB = RA + PC * LR * 4, RC = RB + PC * LR * 4;
@@ -528,10 +556,10 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     // after the current item's convolutions have consumed theirs, and arrive
     // during steps 2b-5.  Lane l of wave w handles tokens 4 (2w + l / 32) ..
     // + 3 and channels 4 (l % 32) .. + 3 in step 1.
-    constexpr bool kEarlyTaps = ACT == kFP8;
+    // The conv taps of an item go into RG by direct loads after the previous
+    // item's step X (for the first item, here) and are read in step 1.
     ChunkItem it;
     ChunkIn<ACT> in;
-    float4 wtq[4], wtk[4], wtv[4];             // conv taps of the lane's channels
     {
         const int tid = threadIdx.x, lane = tid & 63;
         // workgroup 0 validates every sequence once and reports the bad ones
@@ -542,10 +570,12 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
             }
         ChunkItem none;
         none.idx = -1;
-        it = next_item(a, n_slots, blockIdx.x, gridDim.x, none);
+        it = uni(next_item(a, n_slots, blockIdx.x, gridDim.x, none));
         if (it.idx < 0) return;
         load_chunk_in<ACT>(a, it, 4 * (tid >> 5), 4 * (lane & 31), in);
-        if constexpr (kEarlyTaps) load_taps(a, it.h, 4 * (lane & 31), wtq, wtk, wtv);
+        dma_taps(a, it.h, lds + RG, __builtin_amdgcn_readfirstlane(tid >> 6), lane);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_sync();
     }
     for (;;) {
     // The thread index is passed through an empty assembly statement on each
@@ -568,7 +598,16 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     // decay products, in-sub-block pairs
     float cv[4][4], bt[4];
     {
-        if constexpr (!kEarlyTaps) load_taps(a, h, c0, wtq, wtk, wtv);
+        float4 wtq[4], wtk[4], wtv[4];           // conv taps of the lane's channels
+        {
+            const float4* tp = reinterpret_cast<const float4*>(lds + RG);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                wtq[q] = tp[c0 + q];
+                wtk[q] = tp[PD + c0 + q];
+                wtv[q] = tp[2 * PD + c0 + q];
+            }
+        }
         float qh[4][4], kh[4][4], al[4][4];
         conv4x4<ACT>(in.rq, in.okm, wtq, tb, L, a.scale_q, qh);
 #pragma unroll
@@ -608,7 +647,7 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
 
         // every input of this item is consumed: find the next item (its
         // inputs are requested in three parts during step 2b)
-        nx = next_item(a, n_slots, it.idx + gridDim.x, gridDim.x, it);
+        nx = uni(next_item(a, n_slots, it.idx + gridDim.x, gridDim.x, it));
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
         float pp[10], pa[6];
@@ -976,11 +1015,9 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     }
     lds_sync();
 
-    // the next item's conv taps (this item's were last used in step 1), with
-    // FP8 inputs only: with FP32 or BF16 inputs the raw tokens held for the
-    // next item leave too few of the 256 registers per lane that two waves
-    // per SIMD allow, and the taps are loaded at the start of step 1 instead
-    if (kEarlyTaps && nx.idx >= 0) load_taps(a, nx.h, c0, wtq, wtk, wtv);
+    // the next item's conv taps into RG (free until the next item's step
+    // 2a); waited for in step 4, before its stores
+    if (nx.idx >= 0) dma_taps(a, nx.h, lds + RG, wave, lane);
 
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
     // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns one
@@ -1047,7 +1084,11 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
                 if (b < 3) Xs[b][u] = split_op4(X[b][u]);
             }
         }
-        // the W tile to LDS (negated), the Ut tile to the workspace
+        // the W tile to LDS (negated), the Ut tile to the workspace.  First
+        // the wait for the taps' direct loads, issued before this step, so
+        // that it never waits behind this step's stores; the loop's last
+        // barrier then publishes them.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -1102,139 +1143,12 @@ __device__ __forceinline__ void three_passes(F&& body) {
     body(std::integral_constant<int, 2>{});
 }
 
-typedef __attribute__((address_space(3))) char lds_char_t;
-
-// One half of a chunk's fragments into LDS: 56 pieces of 1 KB, wave w of
-// the NW copies pieces w, w+NW, ...; lane l moves 16 bytes straight from
-// global memory to LDS (M0 holds the wave's LDS destination).  Issued as
-// inline assembly: the compiler would otherwise wait for these loads before
-// every LDS read of the other buffer.  The caller waits for them explicitly
-// (s_waitcnt vmcnt(0)) before the barrier that publishes the buffer.
-template <int NW>
-__device__ __forceinline__ void dma_half(const char* src, char* dst, int wave, int lane) {
-    static_assert((HALF_B / 1024) % NW == 0, "pieces per wave");
-#pragma unroll
-    for (int q = 0; q < HALF_B / 1024 / NW; ++q) {
-        const int piece = wave + NW * q;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src + piece * 1024 + lane * 16),
-                       "{m0}"((lds_char_t*)(dst + piece * 1024))
-                     : "memory");
-    }
-}
-
-// Pulls a later half into the L2 ahead of its DMA: one 4-byte load per
-// 128-byte line of the half's fragments (448 lines) and of the workgroup's
-// 4 KB of Ut (32 lines), two loads per lane over four waves, aimed at a small
-// LDS sink whose contents are never read.  The half's DMA into a working
-// buffer then finds its lines in the L2 instead of waiting on HBM.
-__device__ __forceinline__ void prefetch_lines(const char* frag, const char* ut, char* sink,
-                                               int wave, int lane) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int line = wave * 64 + lane + 256 * r;               // 0..511
-        const char* src = line < HALF_B / 128 ? frag + line * 128
-                                              : ut + min(line - HALF_B / 128, 31) * 128;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
-                     :
-                     : "v"(src), "{m0}"((lds_char_t*)(sink + wave * 256))
-                     : "memory");
-    }
-}
-
-// One 1 KB piece from global memory to LDS (the wave's 64 lanes, 16 bytes
-// each), the same kind of load.
-__device__ __forceinline__ void dma_1k(const char* src, char* dst, int lane) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src + lane * 16), "{m0}"((lds_char_t*)dst)
-                 : "memory");
-}
-
-// Split operands a column slice's U/S wave hands to its O wave through LDS:
-// the chunk's start state as the B operand (k = key channel, four 32-deep
-// blocks) and the current half's U (k = token).
-struct SliceX {
-    f16x8_t sb_hi[2][4][64], sb_lo[2][4][64];    // by chunk parity
-    f16x8_t ub_hi[64], ub_lo[64];
-};
-
 __device__ __forceinline__ void put_split(f16x8_t* hi, f16x8_t* lo, int lane, const SplitOp& x) {
     hi[lane] = x.hi;
     lo[lane] = x.lo;
 }
 __device__ __forceinline__ SplitOp get_split(const f16x8_t* hi, const f16x8_t* lo, int lane) {
     return SplitOp{hi[lane], lo[lane]};
-}
-
-// Every operand a product step reads from LDS is requested first and then
-// pinned by one empty assembly statement, so the wave waits once for all of
-// them instead of once per fragment (the compiler otherwise places each read
-// right before its first matrix instruction and waits for it there).
-__device__ __forceinline__ void pin(SplitOp (&f)[8]) {
-    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
-                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
-                      "+v"(f[4].hi), "+v"(f[4].lo), "+v"(f[5].hi), "+v"(f[5].lo),
-                      "+v"(f[6].hi), "+v"(f[6].lo), "+v"(f[7].hi), "+v"(f[7].lo));
-}
-__device__ __forceinline__ void pin(SplitOp (&f)[8], SplitOp (&b)[4]) {
-    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
-                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
-                      "+v"(f[4].hi), "+v"(f[4].lo), "+v"(f[5].hi), "+v"(f[5].lo),
-                      "+v"(f[6].hi), "+v"(f[6].lo), "+v"(f[7].hi), "+v"(f[7].lo),
-                      "+v"(b[0].hi), "+v"(b[0].lo), "+v"(b[1].hi), "+v"(b[1].lo),
-                      "+v"(b[2].hi), "+v"(b[2].lo), "+v"(b[3].hi), "+v"(b[3].lo));
-}
-__device__ __forceinline__ void pin(SplitOp (&f)[4]) {
-    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
-                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo));
-}
-__device__ __forceinline__ void pin(SplitOp (&f)[4], SplitOp (&b)[4]) {
-    asm volatile("" : "+v"(f[0].hi), "+v"(f[0].lo), "+v"(f[1].hi), "+v"(f[1].lo),
-                      "+v"(f[2].hi), "+v"(f[2].lo), "+v"(f[3].hi), "+v"(f[3].lo),
-                      "+v"(b[0].hi), "+v"(b[0].lo), "+v"(b[1].hi), "+v"(b[1].lo),
-                      "+v"(b[2].hi), "+v"(b[2].lo), "+v"(b[3].hi), "+v"(b[3].lo));
-}
-__device__ __forceinline__ void pin(SplitOp& x, SplitOp& y, SplitOp& z) {
-    asm volatile("" : "+v"(x.hi), "+v"(x.lo), "+v"(y.hi), "+v"(y.lo), "+v"(z.hi), "+v"(z.lo));
-}
-
-// acc[t] += sum over four 32-deep k blocks of fa[2 kb + t] * b[kb] for two
-// row tiles t, with one accumulator per (pass, tile): six independent chains
-// keep the matrix pipe busy.  The hi*hi pass starts from acc.
-__device__ __forceinline__ void prod2x4(const SplitOp (&fa)[8], const SplitOp (&b)[4],
-                                        f32x4_t (&acc)[2]) {
-    f32x4_t pa[3][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        pa[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        pa[1][t] = pa[0][t];
-        pa[2][t] = acc[t];
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        three_passes([&](auto P) {
-            constexpr int pp = decltype(P)::value;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) pa[pp][t] = mma_pass<pp>(fa[2 * kb + t], b[kb], pa[pp][t]);
-        });
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[t] = pa[2][t] + pa[1][t] + pa[0][t];
-}
-
-// acc += sum over four 32-deep k blocks of fa[kb] * b[kb] for one row tile,
-// one accumulator per pass.  The hi*hi pass starts from acc.
-__device__ __forceinline__ void prod1x4(const SplitOp (&fa)[4], const SplitOp (&b)[4],
-                                        f32x4_t& acc) {
-    f32x4_t pa[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, acc};
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-        three_passes([&](auto P) {
-            constexpr int pp = decltype(P)::value;
-            pa[pp] = mma_pass<pp>(fa[kb], b[kb], pa[pp]);
-        });
-    acc = pa[2] + pa[1] + pa[0];
 }
 
 // One-way hand-off of a half's U from a slice's U/S wave to its O wave: the
