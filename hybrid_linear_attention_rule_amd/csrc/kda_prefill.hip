@@ -90,11 +90,15 @@ __device__ __forceinline__ void pow2_scale(float m, float& s, float& is) {
     is = __uint_as_float(ef << 23);
 }
 
-// Largest magnitude over the 16 lanes n, n + 16, n + 32, n + 48 (one matrix
-// column); every one of them gets the result.
+// Largest value over the four lanes n, n + 16, n + 32, n + 48 (one matrix
+// column); every one of them gets the result.  The lane swaps of gfx950
+// (v_permlane16_swap, v_permlane32_swap) pair each lane with lane ^ 16 and
+// then lane ^ 32 in the vector unit, without a round trip through LDS.
 __device__ __forceinline__ float col_max4(float m) {
-    m = fmaxf(m, __shfl_xor(m, 16));
-    return fmaxf(m, __shfl_xor(m, 32));
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    m = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 // Workspace per (chunk slot, head), in bytes.  A fragment is one 16x16x32
