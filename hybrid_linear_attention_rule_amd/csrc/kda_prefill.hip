@@ -1192,40 +1192,63 @@ __device__ __forceinline__ SplitOp ld_frag_g(const char* half, int f, int lane) 
     return o;
 }
 
-// Pulls a later half into the L2: one 4-byte load per 128-byte line of its
-// fragments (448 lines) and of the workgroup's 4 KB of Ut (32 lines), four
-// loads per lane of the two loader waves, aimed at a small LDS sink whose
-// contents are never read.
-__device__ __forceinline__ void prefetch_half_lines(const char* half, const char* ut, char* sink,
-                                                    int lw, int lane) {
+// A chunk's operands of the state chain in LDS: the -W and scaled-K
+// fragments of both halves and the chunk's total decay and largest |Ut|,
+// 65 pieces of 1 KB.  Layout: [half h][-W (16 KB) | scaled K (16 KB)] for
+// h = 0, 1, then the 1 KB of decay and |Ut| maxima.
+constexpr int CB_PIECES = 65;
+constexpr int CB_B = CB_PIECES * 1024;
+constexpr int CB_G = 64 * 1024;                   // decay [PD] FP32, then |Ut| maxima [PD]
+__device__ __forceinline__ int cb_w(int h) { return h * 32768; }
+__device__ __forceinline__ int cb_k(int h) { return h * 32768 + 16384; }
+
+// Workspace byte offset of LDS piece p of a chunk (see the layout above):
+// -W is fragments 0-7 of a half, scaled K fragments 16-23, and the decay and
+// maxima sit at GAM_OFF of half 0.
+__device__ __forceinline__ int cb_src(int p) {
+    if (p == 64) return GAM_OFF;
+    const int h = p >> 5, q = p & 31;
+    return h * HALF_B + (q < 16 ? q * 1024 : 32768 + (q - 16) * 1024);
+}
+
+// One chunk's chain operands into an LDS buffer, loader wave lw (0, 1)
+// taking every other piece; lane l moves 16 bytes straight from global
+// memory to LDS.  Issued as inline assembly: the compiler would otherwise
+// wait for these loads before every LDS read of the other buffer.  The
+// loaders wait for them with counted s_waitcnt vmcnt before the barrier
+// that publishes the buffer.
+__device__ __forceinline__ void dma_chunk(const char* ws, char* dst, int lw, int lane) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int line = lw * 64 + lane + 128 * q;               // 0..511
-        const char* src = line < HALF_B / 128 ? half + line * 128
-                                              : ut + min(line - HALF_B / 128, 31) * 128;
+    for (int q = 0; q < (CB_PIECES + 1) / 2; ++q) {
+        const int piece = lw + 2 * q;
+        if (piece < CB_PIECES)
+            asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(ws + cb_src(piece) + lane * 16),
+                           "{m0}"((lds_char_t*)(dst + piece * 1024))
+                         : "memory");
+    }
+}
+// Loads issued by loader wave lw in dma_chunk: 33 for lw = 0, 32 for lw = 1.
+
+// Pulls a later chunk into the L2: one 4-byte load per 128-byte line of its
+// fragments (both halves, 896 lines) and of the workgroup's 8 KB of Ut (64
+// lines), eight loads per lane of the two loader waves, aimed at a small LDS
+// sink whose contents are never read.  The DMA of the chain operands and
+// the O waves' and U/S waves' direct loads then find their lines in the L2.
+// ut is the workgroup's Ut of half 0 (4 KB); half 1's lies 16 KB further.
+constexpr int kPrefetchLoads = 8;
+__device__ __forceinline__ void prefetch_chunk_lines(const char* ws, const char* ut, char* sink,
+                                                     int lw, int lane) {
+#pragma unroll
+    for (int q = 0; q < kPrefetchLoads; ++q) {
+        const int line = lw * 64 + lane + 128 * q;               // 0..1023
+        const int fl = 2 * HALF_B / 128;                          // 896 fragment lines
+        const int ul = min(line - fl, 63);                        // Ut lines: 32 per half
+        const char* src = line < fl ? ws + line * 128 : ut + (ul >> 5) * 16384 + (ul & 31) * 128;
         asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off"
                      :
                      : "v"(src), "{m0}"((lds_char_t*)(sink + lw * 256))
-                     : "memory");
-    }
-}
-
-// One half of a chunk into an LDS buffer: its 56 fragment pieces of 1 KB
-// (same layout as in the workspace) then the workgroup's 4 KB of Ut, 60
-// pieces, loader wave lw (0, 1) taking every other one; lane l moves 16
-// bytes straight from global memory to LDS.
-constexpr int SBUF_PIECES = HALF_B / 1024 + 4;
-constexpr int SBUF_B = SBUF_PIECES * 1024;
-constexpr int SBUF_UT = HALF_B;                   // Ut's offset in the buffer
-__device__ __forceinline__ void dma_state_half(const char* half, const char* ut, char* dst, int lw,
-                                               int lane) {
-#pragma unroll
-    for (int q = 0; q < SBUF_PIECES / 2; ++q) {
-        const int piece = lw + 2 * q;
-        const char* src = piece < HALF_B / 1024 ? half + piece * 1024 : ut + (piece - HALF_B / 1024) * 1024;
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src + lane * 16), "{m0}"((lds_char_t*)(dst + piece * 1024))
                      : "memory");
     }
 }
@@ -1264,47 +1287,52 @@ __device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&
 
 // Split operands the state pass's waves share through LDS, for the
 // workgroup's two 16-column tiles: the chunk's start state as the B operand
-// (k = key channel, four 32-deep blocks) and the current half's U (k =
-// token).
+// (k = key channel, four 32-deep blocks) and both halves' U (k = token).
 struct StateX {
     f16x8_t sb_hi[2][4][64], sb_lo[2][4][64];     // [column tile][k block]
-    f16x8_t ub_hi[2][64], ub_lo[2][64];           // [column tile]
+    f16x8_t ub_hi[2][2][64], ub_lo[2][2][64];     // [half][column tile]
 };
 
 constexpr int kStateThreads = 384;
 
 // State pass.  Four workgroups per (sequence, head), 32 value columns (two
 // 16-column tiles) each, six waves: two U/S waves, two O waves and two
-// loader waves.
+// loader waves, one barrier per chunk.
 //
-// The loader waves alone touch global memory for operands: they stream each
-// half of a chunk (all its fragments and the workgroup's Ut) into one of two
-// LDS buffers by direct loads, a half ahead of its use, and pull the half
-// after that into the L2.  The waves that compute never wait on a vector
-// memory issue queue.
+// The loader waves stream each chunk's chain operands (-W and scaled K of
+// both halves, the decay, the |Ut| maxima) into one of two LDS buffers by
+// direct loads, a chunk ahead of its use, and pull the chunk after that into
+// the L2.  The O waves and U/S waves read their other operands (scaled Q and
+// P fragments, Ut) straight from the workspace, where those prefetches have
+// put them in the L2.
 //
-// U/S wave r (0, 1) computes row tile r of U = Ut - W S for both column
-// tiles and holds the state's channels 64r..64r+63 (channel tiles 4r..4r+3)
-// of both, updating them by S <- Diag(gamma) S + Kc^T U.  Its own channel
-// blocks of S feed its U product from registers; the other wave's come
-// through LDS.  Each U/S wave publishes its row tile of the split U and sets
-// its flag; the state update and the O waves' P U product wait for both.
+// U/S wave r (0, 1) computes row tile r of U = Ut - W S for both halves of
+// the chunk and both column tiles, from the chunk's start state, and holds
+// the state's channels 64r..64r+63 (channel tiles 4r..4r+3) of both column
+// tiles, updating them once per chunk by S <- Diag(gamma) S + Kc^T U over
+// the chunk's 64 tokens.  Its own channel blocks of S feed its U products
+// from registers; the other wave's come through LDS.  Each U/S wave
+// publishes its row tiles of the split U and sets its flag; the state update
+// and the O waves' P U products wait for both.
 //
-// O wave r computes row tile r of O = Qg S + P U for both column tiles and
-// stores it.  One barrier per half keeps the buffers in step.
+// O wave r computes row tile r of both halves' O = Qg S + P U for both
+// column tiles and stores it, one chunk late.  It publishes a flag once it
+// has read the chunk's split start state and scales, and the U/S waves wait
+// for it before they overwrite them with the next chunk's.
 //
 // Value columns carry power-of-two scales (pow2_scale).  Each U/S wave
 // splits its channel half of the chunk's start state scaled by its own
 // column maxima, and leaves those maxima in LDS beside the split blocks.
-// After the chunk's first barrier every wave forms the chunk's common column
-// scale from both halves' maxima and the chunk's largest |Ut|: U and O are
+// After the chunk's barrier every wave forms the chunk's common column scale
+// from both halves' maxima and the chunk's largest |Ut|: U and O are
 // accumulated at that scale, each state half's partial product brought to it
 // by an exact power of two.  S is held unscaled between chunks.
 template <int ACT, int ST>
 __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArgs a) {
-    __shared__ __attribute__((aligned(16))) char hbuf[2][SBUF_B];
+    __shared__ __attribute__((aligned(16))) char cbuf[2][CB_B];
     __shared__ StateX X;
-    __shared__ int xflag[2];                      // per row tile: last half published
+    __shared__ int xflag[2];                      // per U/S wave: last chunk whose U is published
+    __shared__ int oflag[2];                      // per O wave: last chunk whose split state is read
     __shared__ float xmax[2][2][16];              // [U/S wave][column tile][column]: largest
                                                   // |S| over the wave's channel half
     __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
@@ -1312,14 +1340,15 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
     const int n = lane & 15, g = lane >> 4;
-    const int r = wave & 1;                       // row tile (U/S channel half; loader index)
+    const int r = wave & 1;                       // row tile (U/S channel half; O row tile; loader index)
     const int H = a.H;
     if (tid < 2) xflag[tid] = 0;
+    if (tid >= 2 && tid < 4) oflag[tid - 2] = 0;
     lds_sync();                                   // the flags before any wave uses them
-    // The half buffers are filled only by assembly loads; this store, which
+    // The chunk buffers are filled only by assembly loads; this store, which
     // never runs (num_seqs >= 1), keeps the compiler from treating them as
     // never written.
-    if (a.num_seqs < 0) hbuf[0][tid] = hbuf[1][tid] = 0;
+    if (a.num_seqs < 0) cbuf[0][tid] = cbuf[1][tid] = 0;
     // the column groups of one (sequence, head) sit eight workgroups apart,
     // so they land on the same XCD and share its L2
     const int G = a.num_seqs * H;
@@ -1341,37 +1370,33 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
         return static_cast<const char*>(a.workspace) +
                ((size_t)chunk_slot(v.lo, s, c) * H + h) * WS_B;
     };
-    // half hh of chunk c, and this workgroup's Ut pieces of it (two column
-    // tiles x two row tiles, 4 KB)
-    auto half_src = [&](int hg) -> const char* { return cws(hg >> 1) + (hg & 1) * HALF_B; };
-    auto ut_src = [&](int hg) -> const char* {
-        return cws(hg >> 1) + UT_OFF + ((((hg & 1) * 8 + 2 * grp) * 2) * 64) * 16;
+    // this workgroup's Ut of chunk c: half hh, column tile j, row tile rt
+    auto ut_tile = [&](int c, int hh, int j, int rt) -> const char* {
+        return cws(c) + UT_OFF + ((((hh * 8 + 2 * grp + j) * 2 + rt) * 64) * 16);
     };
 
     if (wave >= 4) {
         // ---------------------------------------------------------- loaders
-        const int nh = 2 * nch;                   // halves, in order
-        dma_state_half(half_src(0), ut_src(0), hbuf[0], r, lane);
-        int npf = 0;                              // prefetch loads issued after the DMA
-        for (int hx = 1; hx <= 2 && hx < nh; ++hx) {
-            prefetch_half_lines(half_src(hx), ut_src(hx), pf_sink, r, lane);
-            npf += 4;
+        const int lw = r;
+        dma_chunk(cws(0), cbuf[0], lw, lane);
+        int npf = 0;                              // prefetch loads issued after the last DMA
+        if (nch > 1) {
+            prefetch_chunk_lines(cws(1), ut_tile(1, 0, 0, 0), pf_sink, lw, lane);
+            npf = kPrefetchLoads;
         }
-        for (int hg = 0; hg < nh; ++hg) {
-            // the DMA of half hg has landed; prefetches issued after it
+        for (int cc = 0; cc < nch; ++cc) {
+            // the DMA of chunk cc has landed; prefetches issued after it
             // (loads complete in order) may stay in flight
-            if (npf >= 8)
+            if (npf == kPrefetchLoads)
                 asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else if (npf == 4)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            lds_sync();                           // half hg may be read
-            if (hg + 1 < nh) dma_state_half(half_src(hg + 1), ut_src(hg + 1), hbuf[(hg + 1) & 1], r, lane);
+            lds_sync();                           // chunk cc may be read
+            if (cc + 1 < nch) dma_chunk(cws(cc + 1), cbuf[(cc + 1) & 1], lw, lane);
             npf = 0;
-            if (hg + 3 < nh) {
-                prefetch_half_lines(half_src(hg + 3), ut_src(hg + 3), pf_sink, r, lane);
-                npf = 4;
+            if (cc + 2 < nch) {
+                prefetch_chunk_lines(cws(cc + 2), ut_tile(cc + 2, 0, 0, 0), pf_sink, lw, lane);
+                npf = kPrefetchLoads;
             }
         }
     } else if (wave < 2) {
@@ -1413,7 +1438,7 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 pow2_scale(x, so[j], iso[j]);
             }
         };
-        // the B operands of the U product: own k blocks 2r, 2r+1 in slots 0,
+        // the B operands of the U products: own k blocks 2r, 2r+1 in slots 0,
         // 1 (from registers, at the own scale) and the other wave's in slots
         // 2, 3 (from LDS, at its scale)
         SplitOp sb[2][4];
@@ -1440,8 +1465,8 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
         // the chunk's |Ut|) and the factors that bring each half's partial
         // products to it (powers of two, at most 1)
         float sg[2], isg[2], rown[2], roth[2];
-        auto set_scale = [&]() {
-            const float* utm = reinterpret_cast<const float*>(hbuf[0] + UTMAX_OFF);
+        auto set_scale = [&](const char* buf) {
+            const float* utm = reinterpret_cast<const float*>(buf + CB_G) + PD;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const float mo = xmax[1 - r][j][n], mu = utm[jc[j]];
@@ -1452,70 +1477,99 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 roth[j] = sg[j] * is1;
             }
         };
-        // row tile r of this half's U (accumulated at 2^8 times the column
-        // scales), split, to LDS
-        auto u_tile = [&](const char* buf) {
-            SplitOp w[4];
+        // the chunk's Ut of this row tile: [half][column tile], loaded a
+        // chunk ahead
+        f32x4_t ut[2][2], utn[2][2];
+        auto ld_ut = [&](int c, f32x4_t (&u)[2][2]) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                w[m] = ld_frag(buf, frag_w(r, m < 2 ? 2 * r + m : 2 * (1 - r) + m - 2), lane);
-            f32x4_t acc[2], ao[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, at[2] = {ao[0], ao[1]};
-            prod4x2<0, 2>(w, sb, ao);
-            prod4x2<2, 2>(w, sb, at);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                acc[j] = *reinterpret_cast<const f32x4_t*>(buf + SBUF_UT + (2 * j + r) * 1024 +
-                                                           lane * 16) * (kScW * sg[j]) +
-                         ao[j] * rown[j] + at[j] * roth[j];
-                put_half_split(X.ub_hi[j], X.ub_lo[j], lane, r, split_op4(acc[j] * kInvScW));
-            }
-        };
-        // channel tiles 4r.. of S += Kc^T U for both column tiles (at 2^12)
-        auto s_update = [&](const char* buf, f32x4_t (&Sn)[2][4]) {
-            SplitOp kf[4], ub[2];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) kf[i] = ld_frag(buf, frag_k(4 * r + i), lane);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) ub[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
-            three_passes([&](auto P) {
+            for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
+                    u[hh][j] = *reinterpret_cast<const f32x4_t*>(ut_tile(c, hh, j, r) + lane * 16);
+        };
+        ld_ut(0, ut);
+        // row tile r of both halves' U (accumulated at 2^8 times the column
+        // scales), split, to LDS.  Both halves' -W fragments are read first
+        // so that the second half's reads pass under the first half's
+        // products.
+        auto u_tiles = [&](const char* buf) {
+            SplitOp w[2][4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Sn[j][i] = mma_pass<decltype(P)::value>(kf[i], ub[j], Sn[j][i]);
-            });
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    w[hh][m] = ld_frag(buf + cb_w(hh),
+                                       frag_w(r, m < 2 ? 2 * r + m : 2 * (1 - r) + m - 2), lane);
+            f32x4_t ao[2][2], at[2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int j = 0; j < 2; ++j) ao[hh][j] = at[hh][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                prod4x2<0, 2>(w[hh], sb, ao[hh]);
+                prod4x2<2, 2>(w[hh], sb, at[hh]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x4_t acc = ut[hh][j] * (kScW * sg[j]) + ao[hh][j] * rown[j] + at[hh][j] * roth[j];
+                    put_half_split(X.ub_hi[hh][j], X.ub_lo[hh][j], lane, r, split_op4(acc * kInvScW));
+                }
+        };
+        // channel tiles 4r.. of S += Kc^T U over both halves, both column
+        // tiles (at 2^12); all operands are read before the products
+        auto s_update = [&](const char* buf, f32x4_t (&Sn)[2][4]) {
+            SplitOp kf[2][4], ub[2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    kf[hh][i] = ld_frag(buf + cb_k(hh), frag_k(4 * r + i) - 16, lane);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) ub[hh][j] = get_split(X.ub_hi[hh][j], X.ub_lo[hh][j], lane);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                three_passes([&](auto P) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            Sn[j][i] = mma_pass<decltype(P)::value>(kf[hh][i], ub[hh][j], Sn[j][i]);
+                });
         };
         for (int cc = 0; cc < nch; ++cc) {
-            // ======== first half: tokens 0..31 of the chunk ========
-            lds_sync();                                            // H0
-            set_scale();
+            const char* buf = cbuf[cc & 1];
+            lds_sync();                                            // chunk cc's operands
+            if (cc + 1 < nch) ld_ut(cc + 1, utn);                 // used next chunk
+            set_scale(buf);
             get_other();
-            u_tile(hbuf[0]);
-            publish_half(&xflag[r], 2 * cc + 1);
+            u_tiles(buf);
+            publish_half(&xflag[r], cc + 1);
             f32x4_t Sn[2][4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(
-                                       hbuf[0] + GAM_OFF + (16 * (4 * r + i) + 4 * g) * 4) * kSc;
+                                       buf + CB_G + (16 * (4 * r + i) + 4 * g) * 4) * kSc;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) Sn[j][i] = gm * (S[j][i] * sg[j]);
             }
-            stalled |= !await_half(&xflag[1 - r], 2 * cc + 1);
-            s_update(hbuf[0], Sn);
-
-            // ======== second half: tokens 32..63 ========
-            lds_sync();                                            // H1
-            u_tile(hbuf[1]);                              // the other blocks are still held
-            publish_half(&xflag[r], 2 * cc + 2);
-            stalled |= !await_half(&xflag[1 - r], 2 * cc + 2);
-            s_update(hbuf[1], Sn);
+            stalled |= !await_half(&xflag[1 - r], cc + 1);
+            s_update(buf, Sn);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * (kInvSc * isg[j]);
             if (cc + 1 < nch) {                           // the next chunk's split state
+                // the O waves have read this chunk's split state and scales
+                stalled |= !await_half(&oflag[0], cc + 1);
+                stalled |= !await_half(&oflag[1], cc + 1);
                 own_scale();
                 make_own();
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) ut[hh][j] = utn[hh][j];
             }
         }
         if (stalled && lane == 0 && a.status) atomicOr(a.status, KDA_STATUS_STALLED);
@@ -1534,34 +1588,48 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 }
     } else {
         // ---------------------------------------------------------- O wave
-        // row tile r of O of the previous half, stored after the next half's
-        // barrier
-        f32x4_t Oprev[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        // row tile r of O of the previous chunk's two halves, stored after the
+        // next chunk's barrier
+        f32x4_t Oprev[2][2] = {{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}},
+                               {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}};
         int orow0 = -1;
         bool stalled = false;
         auto store_o = [&]() {
             if (orow0 < 0) return;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tl = orow0 + 16 * r + 4 * g + e;
-                if (tl < v.len) {
-                    float* yrow = a.y + ((int64_t)(v.lo + tl) * H + h) * PD;
-                    yrow[jc[0]] = Oprev[0][e];
-                    yrow[jc[1]] = Oprev[1][e];
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tl = orow0 + 32 * hh + 16 * r + 4 * g + e;
+                    if (tl < v.len) {
+                        float* yrow = a.y + ((int64_t)(v.lo + tl) * H + h) * PD;
+                        yrow[jc[0]] = Oprev[hh][0][e];
+                        yrow[jc[1]] = Oprev[hh][1][e];
+                    }
                 }
-            }
         };
-        SplitOp sb[2][4], fq[4];
+        SplitOp sb[2][4];
         for (int cc = 0; cc < nch; ++cc) {
-            // ======== first half ========
-            lds_sync();                                            // H0
+            const char* buf = cbuf[cc & 1];
+            const char* ws = cws(cc);
+            lds_sync();                                            // chunk cc's operands
+            // this chunk's scaled-Q and P fragments of row tile r, straight
+            // from the workspace (in the L2 by the loaders' prefetch)
+            SplitOp fq[2][4], fp[3];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) fq[hh][kb] = ld_frag_g(ws + hh * HALF_B, frag_q(r, kb), lane);
+            fp[0] = ld_frag_g(ws, frag_p(0, r, 0), lane);
+            fp[1] = ld_frag_g(ws + HALF_B, frag_p(1, r, 0), lane);
+            fp[2] = ld_frag_g(ws + HALF_B, frag_p(1, r, 1), lane);
             store_o();
             // O comes out at 2^12 times the chunk's common column scales; the
             // query scale multiplies it here.  The state blocks of U/S wave 0
             // (k blocks 0, 1) and wave 1 (2, 3) carry their own scales.
             float osc[2], r0[2], r1[2];
             {
-                const float* utm = reinterpret_cast<const float*>(hbuf[0] + UTMAX_OFF);
+                const float* utm = reinterpret_cast<const float*>(buf + CB_G) + PD;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float m0 = xmax[0][j][n], m1 = xmax[1][j][n];
@@ -1574,61 +1642,45 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                     r1[j] = su * is1;
                 }
             }
-            // O = (e(t,-1) q) S, both halves brought to the common scale
-            auto qs = [&](f32x4_t (&O)[2]) {
-                f32x4_t o0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, o1[2] = {o0[0], o0[1]};
-                prod4x2<0, 2>(fq, sb, o0);
-                prod4x2<2, 2>(fq, sb, o1);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) O[j] = o0[j] * r0[j] + o1[j] * r1[j];
-            };
 #pragma unroll
             for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
                     sb[j][kb] = get_split(X.sb_hi[j][kb], X.sb_lo[j][kb], lane);
+            publish_half(&oflag[r], cc + 1);              // split state and scales read
+            // O = (e(t,-1) q) S for both halves, each state half brought to the
+            // common scale
+            f32x4_t O[2][2];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[0], frag_q(r, kb), lane);
-            f32x4_t O[2];
-            qs(O);
-            SplitOp fp0 = ld_frag(hbuf[0], frag_p(0, r, 0), lane);
-            stalled |= !await_half(&xflag[0], 2 * cc + 1);
-            stalled |= !await_half(&xflag[1], 2 * cc + 1);
-            SplitOp ub0[2];
+            for (int hh = 0; hh < 2; ++hh) {
+                f32x4_t o0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, o1[2] = {o0[0], o0[1]};
+                prod4x2<0, 2>(fq[hh], sb, o0);
+                prod4x2<2, 2>(fq[hh], sb, o1);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) ub0[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
+                for (int j = 0; j < 2; ++j) O[hh][j] = o0[j] * r0[j] + o1[j] * r1[j];
+            }
+            stalled |= !await_half(&xflag[0], cc + 1);
+            stalled |= !await_half(&xflag[1], cc + 1);
+            SplitOp ub0[2], ub1[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                ub0[j] = get_split(X.ub_hi[0][j], X.ub_lo[0][j], lane);
+                ub1[j] = get_split(X.ub_hi[1][j], X.ub_lo[1][j], lane);
+            }
             three_passes([&](auto P) {
+                constexpr int pp = decltype(P)::value;
 #pragma unroll
-                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
+                for (int j = 0; j < 2; ++j) {
+                    O[0][j] = mma_pass<pp>(fp[0], ub0[j], O[0][j]);
+                    O[1][j] = mma_pass<pp>(fp[1], ub0[j], O[1][j]);
+                    O[1][j] = mma_pass<pp>(fp[2], ub1[j], O[1][j]);
+                }
             });
-            Oprev[0] = O[0] * osc[0];
-            Oprev[1] = O[1] * osc[1];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) Oprev[hh][j] = O[hh][j] * osc[j];
             orow0 = cc * PC;
-
-            // ======== second half ========
-            lds_sync();                                            // H1
-            store_o();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) fq[kb] = ld_frag(hbuf[1], frag_q(r, kb), lane);
-            fp0 = ld_frag(hbuf[1], frag_p(1, r, 0), lane);
-            SplitOp fp1 = ld_frag(hbuf[1], frag_p(1, r, 1), lane);
-            qs(O);
-            three_passes([&](auto P) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp0, ub0[j], O[j]);
-            });
-            stalled |= !await_half(&xflag[0], 2 * cc + 2);
-            stalled |= !await_half(&xflag[1], 2 * cc + 2);
-            SplitOp ub1[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) ub1[j] = get_split(X.ub_hi[j], X.ub_lo[j], lane);
-            three_passes([&](auto P) {
-#pragma unroll
-                for (int j = 0; j < 2; ++j) O[j] = mma_pass<decltype(P)::value>(fp1, ub1[j], O[j]);
-            });
-            Oprev[0] = O[0] * osc[0];
-            Oprev[1] = O[1] * osc[1];
-            orow0 = cc * PC + 32;
         }
         store_o();
         if (stalled && lane == 0 && a.status) atomicOr(a.status, KDA_STATUS_STALLED);
