@@ -35,13 +35,13 @@
 //          K and P as pre-split fp16 pairs in matrix-core fragment order, Ut
 //          in FP32, and the chunk's total decay;
 //   state  (four workgroups per sequence x head, 32 value columns each,
-//          sequential over the sequence's chunks): U, O and the next state
-//          on the matrix cores; two loader waves stream each half chunk's
-//          operands into LDS by direct global-to-LDS loads, double-buffered;
-//          two U/S waves form U and update the state slice they hold in
-//          registers, two O waves form O; O is written unnormalised; the
-//          final state is stored once and the ring gets the sequence's last
-//          raw tokens;
+//          sequential over the sequence's chunks, one barrier per chunk):
+//          U, O and the next state on the matrix cores; two loader waves
+//          stream each chunk's chain operands into LDS by direct
+//          global-to-LDS loads, a chunk ahead, double-buffered; two U/S
+//          waves form U and update the state slice they hold in registers,
+//          two O waves form O; O is written unnormalised; the final state
+//          is stored once and the ring gets the sequence's last raw tokens;
 //   finish (per token x head): the gated RMSNorm of O.
 #include "kda_device.h"
 #include "kda_internal.h"
