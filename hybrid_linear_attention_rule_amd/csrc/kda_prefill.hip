@@ -39,9 +39,10 @@
 //          U, O and the next state on the matrix cores; two loader waves
 //          stream each chunk's chain operands into LDS by direct
 //          global-to-LDS loads, a chunk ahead, double-buffered; two U/S
-//          waves form U and update the state slice they hold in registers,
-//          two O waves form O; O is written unnormalised; the final state
-//          is stored once and the ring gets the sequence's last raw tokens;
+//          waves, one per 16-column tile, form U and update the state tile
+//          they hold in registers, independently of each other; two O waves
+//          form O; O is written unnormalised; the final state is stored
+//          once and the ring gets the sequence's last raw tokens;
 //   finish (per token x head): the gated RMSNorm of O.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -1155,13 +1156,15 @@ __device__ __forceinline__ SplitOp get_split(const f16x8_t* hi, const f16x8_t* l
     return SplitOp{hi[lane], lo[lane]};
 }
 
-// One-way hand-off of a half's U from a slice's U/S wave to its O wave: the
-// U/S wave writes the split U to LDS, waits for those writes, then stores
-// the half's number (never 0) in the slice's flag; the O wave polls the flag
-// before reading U.  The U/S wave never waits for the O wave here (the
-// barriers at each half's start keep both in step), so the hand-off cannot
-// block.  The poll is bounded all the same: await_half returns false when
-// the flag never arrived, and the kernel then reports KDA_STATUS_STALLED.
+// One-way hand-offs between the state pass's waves through LDS flags: a U/S
+// wave publishes a chunk's split U and the O waves poll before reading it;
+// an O wave publishes once it has read the chunk's split state, and the U/S
+// waves poll before overwriting it.  The writer writes, waits for those
+// writes, then stores the chunk's number plus one (never 0) in its flag.
+// Each wait is for work its own workgroup does in the same chunk, between
+// the same two barriers, so no hand-off can block.  The poll is bounded all
+// the same: await_half returns false when the flag never arrived, and the
+// kernel then reports KDA_STATUS_STALLED.
 // The flag is accessed through an LDS-typed pointer: through a generic one
 // the volatile access becomes a flat store, which also counts as a vector
 // memory operation and makes the compiler wait for every outstanding load.
@@ -1306,14 +1309,14 @@ constexpr int kStateThreads = 384;
 // P fragments, Ut) straight from the workspace, where those prefetches have
 // put them in the L2.
 //
-// U/S wave r (0, 1) computes row tile r of U = Ut - W S for both halves of
-// the chunk and both column tiles, from the chunk's start state, and holds
-// the state's channels 64r..64r+63 (channel tiles 4r..4r+3) of both column
-// tiles, updating them once per chunk by S <- Diag(gamma) S + Kc^T U over
-// the chunk's 64 tokens.  Its own channel blocks of S feed its U products
-// from registers; the other wave's come through LDS.  Each U/S wave
-// publishes its row tiles of the split U and sets its flag; the state update
-// and the O waves' P U products wait for both.
+// U/S wave j (0, 1) holds value-column tile j of the state for all 128 key
+// channels and updates it once per chunk: U = Ut - W S for all 64 tokens of
+// the chunk from the chunk's start state, then S <- Diag(gamma) S + Kc^T U.
+// The MFMA output layout of a half's two U row tiles is, lane for lane and
+// in order, the B operand the update takes (the scaled-K fragments are
+// stored in that pairing order), so U stays in registers and the two U/S
+// waves exchange nothing.  Each U/S wave leaves its split U in LDS for the
+// O waves and sets its flag.
 //
 // O wave r computes row tile r of both halves' O = Qg S + P U for both
 // column tiles and stores it, one chunk late.  It publishes a flag once it
@@ -1321,26 +1324,24 @@ constexpr int kStateThreads = 384;
 // for it before they overwrite them with the next chunk's.
 //
 // Value columns carry power-of-two scales (pow2_scale).  Each U/S wave
-// splits its channel half of the chunk's start state scaled by its own
-// column maxima, and leaves those maxima in LDS beside the split blocks.
-// After the chunk's barrier every wave forms the chunk's common column scale
-// from both halves' maxima and the chunk's largest |Ut|: U and O are
-// accumulated at that scale, each state half's partial product brought to it
-// by an exact power of two.  S is held unscaled between chunks.
+// splits the chunk's start state scaled by its column maxima, and leaves
+// those maxima in LDS beside the split blocks.  U and O are accumulated at
+// the chunk's column scale (the larger of the state's maxima and the
+// chunk's largest |Ut|), the state products brought to it by an exact power
+// of two.  S is held unscaled between chunks.
 template <int ACT, int ST>
 __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArgs a) {
     __shared__ __attribute__((aligned(16))) char cbuf[2][CB_B];
     __shared__ StateX X;
     __shared__ int xflag[2];                      // per U/S wave: last chunk whose U is published
     __shared__ int oflag[2];                      // per O wave: last chunk whose split state is read
-    __shared__ float xmax[2][2][16];              // [U/S wave][column tile][column]: largest
-                                                  // |S| over the wave's channel half
+    __shared__ float xmax[2][16];                 // [column tile][column]: largest |S|
     __shared__ __attribute__((aligned(16))) char pf_sink[2 * 256];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: role branches are scalar
     const int n = lane & 15, g = lane >> 4;
-    const int r = wave & 1;                       // row tile (U/S channel half; O row tile; loader index)
+    const int r = wave & 1;                       // U/S column tile; O row tile; loader index
     const int H = a.H;
     if (tid < 2) xflag[tid] = 0;
     if (tid >= 2 && tid < 4) oflag[tid - 2] = 0;
@@ -1401,165 +1402,140 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
         }
     } else if (wave < 2) {
         // ---------------------------------------------------------- U/S wave
-        // S[j][i]: column tile j, channel tile 4r + i (channels 16 (4r+i) + 4g + e)
-        f32x4_t S[2][4];
+        // U/S wave jw owns value-column tile jw (the lane's column jc[jw]) of
+        // the state over all 128 key channels: S[i] is channel tile i
+        // (channels 16 i + 4 g + e).  Its U of both row tiles of a half lands
+        // in the lanes and order the update's B operand takes, so the two
+        // U/S waves exchange nothing.
+        const int jw = r;
+        f32x4_t S[8];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[j][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; ++i) S[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         if (v.pos > 0) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const size_t el =
-                            head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc[j];
-                        S[j][i][e] = ST == kF32
-                                         ? static_cast<const float*>(a.pool)[el]
+                for (int e = 0; e < 4; ++e) {
+                    const size_t el = head_off + (size_t)(16 * i + 4 * g + e) * PD + jc[jw];
+                    S[i][e] = ST == kF32 ? static_cast<const float*>(a.pool)[el]
                                          : bf16_to_f32(static_cast<const uint16_t*>(a.pool)[el]);
-                    }
+                }
         }
         bool stalled = false;
-        // own split scale: the largest |S| of each value column over this
-        // wave's channel half, left in LDS for the other waves
-        float so[2], iso[2];
+        // the split scale: the largest |S| of each value column, left in LDS
+        // for the O waves
+        float xo, so, iso;
         auto own_scale = [&]() {
+            float x = 0.f;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                float x = 0.f;
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) x = fmaxf(x, fabsf(S[j][i][e]));
-                x = col_max4(x);
-                if (g == 0) xmax[r][j][n] = x;
-                pow2_scale(x, so[j], iso[j]);
-            }
+                for (int e = 0; e < 4; ++e) x = fmaxf(x, fabsf(S[i][e]));
+            x = col_max4(x);
+            xo = x;
+            if (g == 0) xmax[jw][n] = x;
+            pow2_scale(x, so, iso);
         };
-        // the B operands of the U products: own k blocks 2r, 2r+1 in slots 0,
-        // 1 (from registers, at the own scale) and the other wave's in slots
-        // 2, 3 (from LDS, at its scale)
-        SplitOp sb[2][4];
+        // the B operands of the U products (k block kb: channel tiles 2 kb,
+        // 2 kb + 1), also left in LDS for the O waves
+        SplitOp sb[4];
         auto make_own = [&]() {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    sb[j][m] = split_pair(S[j][2 * m] * so[j], S[j][2 * m + 1] * so[j]);
-                    put_split(X.sb_hi[j][2 * r + m], X.sb_lo[j][2 * r + m], lane, sb[j][m]);
-                }
+            for (int kb = 0; kb < 4; ++kb) {
+                sb[kb] = split_pair(S[2 * kb] * so, S[2 * kb + 1] * so);
+                put_split(X.sb_hi[jw][kb], X.sb_lo[jw][kb], lane, sb[kb]);
+            }
         };
         own_scale();
         make_own();
-        auto get_other = [&]() {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    sb[j][2 + m] = get_split(X.sb_hi[j][2 * (1 - r) + m],
-                                             X.sb_lo[j][2 * (1 - r) + m], lane);
-        };
-        // the chunk's common column scale sg (largest of both halves' |S| and
-        // the chunk's |Ut|) and the factors that bring each half's partial
-        // products to it (powers of two, at most 1)
-        float sg[2], isg[2], rown[2], roth[2];
+        // the chunk's column scale sg (the largest of |S| and the chunk's
+        // |Ut|) and the factor that brings the state products to it (a power
+        // of two, at most 1)
+        float sg, isg, rown;
         auto set_scale = [&](const char* buf) {
             const float* utm = reinterpret_cast<const float*>(buf + CB_G) + PD;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const float mo = xmax[1 - r][j][n], mu = utm[jc[j]];
-                float s1, is1;
-                pow2_scale(mo, s1, is1);
-                pow2_scale(fmaxf(fmaxf(xmax[r][j][n], mo), mu), sg[j], isg[j]);
-                rown[j] = sg[j] * iso[j];
-                roth[j] = sg[j] * is1;
-            }
+            pow2_scale(fmaxf(xo, utm[jc[jw]]), sg, isg);
+            rown = sg * iso;
         };
-        // the chunk's Ut of this row tile: [half][column tile], loaded a
+        // the chunk's Ut of this column tile: [half][row tile], loaded a
         // chunk ahead
         f32x4_t ut[2][2], utn[2][2];
         auto ld_ut = [&](int c, f32x4_t (&u)[2][2]) {
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    u[hh][j] = *reinterpret_cast<const f32x4_t*>(ut_tile(c, hh, j, r) + lane * 16);
+                for (int rt = 0; rt < 2; ++rt)
+                    u[hh][rt] = *reinterpret_cast<const f32x4_t*>(ut_tile(c, hh, jw, rt) + lane * 16);
         };
         ld_ut(0, ut);
-        // row tile r of both halves' U (accumulated at 2^8 times the column
-        // scales), split, to LDS.  Both halves' -W fragments are read first
-        // so that the second half's reads pass under the first half's
-        // products.
-        auto u_tiles = [&](const char* buf) {
-            SplitOp w[2][4];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    w[hh][m] = ld_frag(buf + cb_w(hh),
-                                       frag_w(r, m < 2 ? 2 * r + m : 2 * (1 - r) + m - 2), lane);
-            f32x4_t ao[2][2], at[2][2];
+        // One chunk of the chain: U of both halves (accumulated at 2^8 times
+        // the column scale) from the chunk's start state, split (the update's
+        // B operand, and in LDS for the O waves), then S += Kc^T U over both
+        // halves and all 128 channels (at 2^12; Sn holds the decayed start
+        // state).  Both halves' U products are issued before either half is
+        // finished, and the first half's update before the second half's U
+        // is finished, so that vector work runs under matrix instructions.
+        auto chain = [&](const char* buf, f32x4_t (&Sn)[8], int epoch) {
+            f32x4_t pa[2][3][2];                  // [half][pass][row tile]
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
+                SplitOp w[2][4];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) ao[hh][j] = at[hh][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                prod4x2<0, 2>(w[hh], sb, ao[hh]);
-                prod4x2<2, 2>(w[hh], sb, at[hh]);
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) w[u][kb] = ld_frag(buf + cb_w(hh), frag_w(u, kb), lane);
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    pa[hh][0][u] = pa[hh][1][u] = pa[hh][2][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+                    three_passes([&](auto P) {
+                        constexpr int pp = decltype(P)::value;
+#pragma unroll
+                        for (int u = 0; u < 2; ++u)
+                            pa[hh][pp][u] = mma_pass<pp>(w[u][kb], sb[kb], pa[hh][pp][u]);
+                    });
             }
+            SplitOp ub[2];
+            auto finish_u = [&](int hh) {
+                f32x4_t uu[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+                for (int u = 0; u < 2; ++u)
+                    uu[u] = (ut[hh][u] * (kScW * sg) +
+                             (pa[hh][2][u] + pa[hh][1][u] + pa[hh][0][u]) * rown) * kInvScW;
+                ub[hh] = split_pair(uu[0], uu[1]);
+                put_split(X.ub_hi[hh][jw], X.ub_lo[hh][jw], lane, ub[hh]);
+            };
+            auto update = [&](int hh) {
+                SplitOp kf[8];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const f32x4_t acc = ut[hh][j] * (kScW * sg[j]) + ao[hh][j] * rown[j] + at[hh][j] * roth[j];
-                    put_half_split(X.ub_hi[hh][j], X.ub_lo[hh][j], lane, r, split_op4(acc * kInvScW));
-                }
-        };
-        // channel tiles 4r.. of S += Kc^T U over both halves, both column
-        // tiles (at 2^12); all operands are read before the products
-        auto s_update = [&](const char* buf, f32x4_t (&Sn)[2][4]) {
-            SplitOp kf[2][4], ub[2][2];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    kf[hh][i] = ld_frag(buf + cb_k(hh), frag_k(4 * r + i) - 16, lane);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) ub[hh][j] = get_split(X.ub_hi[hh][j], X.ub_lo[hh][j], lane);
-            }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
+                for (int i = 0; i < 8; ++i) kf[i] = ld_frag(buf + cb_k(hh), frag_k(i) - 16, lane);
                 three_passes([&](auto P) {
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            Sn[j][i] = mma_pass<decltype(P)::value>(kf[hh][i], ub[hh][j], Sn[j][i]);
+                    for (int i = 0; i < 8; ++i) Sn[i] = mma_pass<decltype(P)::value>(kf[i], ub[hh], Sn[i]);
                 });
+            };
+            finish_u(0);
+            update(0);
+            finish_u(1);
+            publish_half(&xflag[jw], epoch);
+            update(1);
         };
         for (int cc = 0; cc < nch; ++cc) {
             const char* buf = cbuf[cc & 1];
             lds_sync();                                            // chunk cc's operands
             if (cc + 1 < nch) ld_ut(cc + 1, utn);                 // used next chunk
             set_scale(buf);
-            get_other();
-            u_tiles(buf);
-            publish_half(&xflag[r], cc + 1);
-            f32x4_t Sn[2][4];
+            f32x4_t Sn[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4_t gm = *reinterpret_cast<const f32x4_t*>(
-                                       buf + CB_G + (16 * (4 * r + i) + 4 * g) * 4) * kSc;
-#pragma unroll
-                for (int j = 0; j < 2; ++j) Sn[j][i] = gm * (S[j][i] * sg[j]);
+            for (int i = 0; i < 8; ++i) {
+                const f32x4_t gm =
+                    *reinterpret_cast<const f32x4_t*>(buf + CB_G + (16 * i + 4 * g) * 4) * kSc;
+                Sn[i] = gm * (S[i] * sg);
             }
-            stalled |= !await_half(&xflag[1 - r], cc + 1);
-            s_update(buf, Sn);
+            chain(buf, Sn, cc + 1);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[j][i] = Sn[j][i] * (kInvSc * isg[j]);
+            for (int i = 0; i < 8; ++i) S[i] = Sn[i] * (kInvSc * isg);
             if (cc + 1 < nch) {                           // the next chunk's split state
                 // the O waves have read this chunk's split state and scales
                 stalled |= !await_half(&oflag[0], cc + 1);
@@ -1569,23 +1545,21 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) ut[hh][j] = utn[hh][j];
+                    for (int rt = 0; rt < 2; ++rt) ut[hh][rt] = utn[hh][rt];
             }
         }
         if (stalled && lane == 0 && a.status) atomicOr(a.status, KDA_STATUS_STALLED);
         // typed store of the final state, once
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const size_t el = head_off + (size_t)(16 * (4 * r + i) + 4 * g + e) * PD + jc[j];
-                    if (ST == kF32)
-                        static_cast<float*>(a.pool)[el] = S[j][i][e];
-                    else
-                        static_cast<uint16_t*>(a.pool)[el] = (uint16_t)f32_to_bf16_rne(S[j][i][e]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                const size_t el = head_off + (size_t)(16 * i + 4 * g + e) * PD + jc[jw];
+                if (ST == kF32)
+                    static_cast<float*>(a.pool)[el] = S[i][e];
+                else
+                    static_cast<uint16_t*>(a.pool)[el] = (uint16_t)f32_to_bf16_rne(S[i][e]);
+            }
     } else {
         // ---------------------------------------------------------- O wave
         // row tile r of O of the previous chunk's two halves, stored after the
@@ -1623,23 +1597,20 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
             fp[0] = ld_frag_g(ws, frag_p(0, r, 0), lane);
             fp[1] = ld_frag_g(ws + HALF_B, frag_p(1, r, 0), lane);
             fp[2] = ld_frag_g(ws + HALF_B, frag_p(1, r, 1), lane);
-            store_o();
-            // O comes out at 2^12 times the chunk's common column scales; the
-            // query scale multiplies it here.  The state blocks of U/S wave 0
-            // (k blocks 0, 1) and wave 1 (2, 3) carry their own scales.
-            float osc[2], r0[2], r1[2];
+            // O comes out at 2^12 times the chunk's column scales; the query
+            // scale multiplies it here.  The split state carries its own
+            // column scale (the largest |S|), which rs brings to the chunk's.
+            float osc[2], rs[2];
             {
                 const float* utm = reinterpret_cast<const float*>(buf + CB_G) + PD;
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
-                    const float m0 = xmax[0][j][n], m1 = xmax[1][j][n];
-                    float s0, is0, s1, is1, su, isu;
-                    pow2_scale(m0, s0, is0);
-                    pow2_scale(m1, s1, is1);
-                    pow2_scale(fmaxf(fmaxf(m0, m1), utm[jc[j]]), su, isu);
+                    const float m = xmax[j][n];
+                    float ss, iss, su, isu;
+                    pow2_scale(m, ss, iss);
+                    pow2_scale(fmaxf(m, utm[jc[j]]), su, isu);
                     osc[j] = a.q_scale * (kInvSc * isu);
-                    r0[j] = su * is0;
-                    r1[j] = su * is1;
+                    rs[j] = su * iss;
                 }
             }
 #pragma unroll
@@ -1648,16 +1619,16 @@ __global__ __launch_bounds__(kStateThreads) void prefill_state_kernel(PrefillArg
                 for (int kb = 0; kb < 4; ++kb)
                     sb[j][kb] = get_split(X.sb_hi[j][kb], X.sb_lo[j][kb], lane);
             publish_half(&oflag[r], cc + 1);              // split state and scales read
-            // O = (e(t,-1) q) S for both halves, each state half brought to the
-            // common scale
+            store_o();
+            // O = (e(t,-1) q) S for both halves, brought to the chunk's
+            // column scale
             f32x4_t O[2][2];
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                f32x4_t o0[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}}, o1[2] = {o0[0], o0[1]};
-                prod4x2<0, 2>(fq[hh], sb, o0);
-                prod4x2<2, 2>(fq[hh], sb, o1);
+                f32x4_t o[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                prod4x2(fq[hh], sb, o);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) O[hh][j] = o0[j] * r0[j] + o1[j] * r1[j];
+                for (int j = 0; j < 2; ++j) O[hh][j] = o[j] * rs[j];
             }
             stalled |= !await_half(&xflag[0], cc + 1);
             stalled |= !await_half(&xflag[1], cc + 1);
