@@ -1256,18 +1256,9 @@ __device__ __forceinline__ void prefetch_chunk_lines(const char* ws, const char*
     }
 }
 
-// The lane's half (row tile r) of a split U operand: slots 4r..4r+3 of the
-// 16-byte hi and lo words.
-__device__ __forceinline__ void put_half_split(f16x8_t* hi, f16x8_t* lo, int lane, int r,
-                                               const SplitOp4& x) {
-    reinterpret_cast<f16x4_t*>(&hi[lane])[r] = x.hi;
-    reinterpret_cast<f16x4_t*>(&lo[lane])[r] = x.lo;
-}
-
-// acc[j] += sum over the 32-deep k blocks K0..K0+NK-1 of fa[kb] * b[j][kb]
-// for two column tiles j, one accumulator per (pass, tile): six independent
-// chains.  The hi*hi pass starts from acc.
-template <int K0 = 0, int NK = 4>
+// acc[j] += sum over the four 32-deep k blocks of fa[kb] * b[j][kb] for two
+// column tiles j, one accumulator per (pass, tile): six independent chains.
+// The hi*hi pass starts from acc.
 __device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&b)[2][4],
                                         f32x4_t (&acc)[2]) {
     f32x4_t pa[3][2];
@@ -1278,7 +1269,7 @@ __device__ __forceinline__ void prod4x2(const SplitOp (&fa)[4], const SplitOp (&
         pa[2][j] = acc[j];
     }
 #pragma unroll
-    for (int kb = K0; kb < K0 + NK; ++kb)
+    for (int kb = 0; kb < 4; ++kb)
         three_passes([&](auto P) {
             constexpr int pp = decltype(P)::value;
 #pragma unroll
