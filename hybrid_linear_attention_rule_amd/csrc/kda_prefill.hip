@@ -432,9 +432,10 @@ struct ChunkIn {
 };
 
 // Part PART of a lane's raw inputs: 0 q, 1 k, 2 v with alpha and beta.  The
-// three parts are issued at three points of a step, so that the loads of
-// the workgroup's eight waves pass the address units in turn instead of all
-// at once; `okm` is set by part 0.
+// three parts go out before three different steps, so that the loads pass
+// the address units in turn, and only part of the next item's inputs
+// occupies registers during step 2b, where the current item's products
+// need the most; `okm` is set by part 0.
 template <int ACT, int PART>
 __device__ __forceinline__ void load_chunk_part(const PrefillArgs& a, const ChunkItem& it, int tb,
                                                 int c0, ChunkIn<ACT>& in) {
@@ -557,9 +558,9 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     const int H = a.H;
 
     // Persistent: the workgroup takes items blockIdx.x, + gridDim.x, ...
-    // The next item's inputs are requested in three parts during step 2b,
-    // after the current item's convolutions have consumed theirs, and arrive
-    // during steps 2b-5.  Lane l of wave w handles tokens 4 (2w + l / 32) ..
+    // The next item's inputs are requested in three parts (before steps 2b,
+    // X and 4), after the current item's convolutions have consumed theirs,
+    // and arrive by the next item's step 1.  Lane l of wave w handles tokens 4 (2w + l / 32) ..
     // + 3 and channels 4 (l % 32) .. + 3 in step 1.
     // The conv taps of an item go into RG by direct loads after the previous
     // item's step X (for the first item, here) and are read in step 1.
@@ -651,7 +652,7 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
         conv4x4<ACT>(in.rv, in.okm, wtv, tb, L, a.scale_v, cv);
 
         // every input of this item is consumed: find the next item (its
-        // inputs are requested in three parts during step 2b)
+        // inputs are requested in three parts, from step 2b on)
         nx = uni(next_item(a, n_slots, it.idx + gridDim.x, gridDim.x, it));
 
         // pairs inside the sub-block: e(t, i) = alpha over i+1..t
@@ -760,8 +761,8 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     }
     lds_sync();
 
-    // The next item's inputs, in three parts over step 2b (FP32 inputs: the
-    // q part here, the others later; see step X).  Requested here rather
+    // The next item's inputs go out in three parts: q here, k before step X,
+    // v, alpha and beta before step 4.  The first is requested here rather
     // than right after the convolutions: by now the previous item's
     // workspace stores have drained, and the loads still have steps 2b-5 to
     // arrive.
@@ -774,8 +775,7 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     // three apart through the boundary before local sub-block 2 ("J2").
     // Waves 4-7: the tiles left of the diagonal, through the row block's
     // first boundary: wave 4 takes (2,0) and (2,1), wave 5 (3,0) and (3,1),
-    // wave 6 (3,2), wave 7 (1,0).  Every wave requests the next item's
-    // inputs in parts 1 and 2 between its products.
+    // wave 6 (3,2), wave 7 (1,0).
     if (wave < 4) {
         const int t = 16 * wave + n;              // A-operand row of this lane
         const int i = 16 * wave + n;              // B-operand column of this lane
@@ -805,10 +805,6 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
             aP2 = mma3(split_op(rq2), sck2, aP2);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ACT != kF32) {
-            if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
-        }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int tl = 4 * g + r, jtl = g, jil = n >> 2;
@@ -830,9 +826,6 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
                 Pm[16 * wave + 4 * g + r][16 * bi + n] = 0.f;
             }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ACT != kF32) {
-            if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
-        }
     } else {
         const int rb = wave == 4 ? 2 : (wave == 7 ? 1 : 3);     // row block
         const int bi0 = wave == 6 ? 2 : 0;
@@ -864,10 +857,6 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
                 xq[kb] = split_op(rq);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (ACT != kF32) {
-                if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
-            }
-            __builtin_amdgcn_sched_barrier(0);
             for (int bi = bi0; bi < bi1; ++bi) {
                 const int ic = 16 * bi + n;
                 const int ji = ic >> 2;
@@ -893,9 +882,6 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ACT != kF32) {
-            if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
-        }
     }
     lds_sync();
 
@@ -994,13 +980,10 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     }
     lds_sync();
 
-    // FP32 inputs take twice the registers of BF16 ones: their k part is
-    // requested here and their v, alpha and beta part before step 4, out of
-    // step 2b's register peak (12 spilled registers instead of 45; the call
-    // is about 10% faster).
-    if constexpr (ACT == kF32) {
-        if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
-    }
+    // The next item's k inputs (its q inputs went out before step 2b, its
+    // v, alpha and beta go out before step 4): requested outside step 2b's
+    // register peak.
+    if (nx.idx >= 0) load_chunk_part<ACT, 1>(a, nx, tb, c0, in);
     // ---- X. beta_t K_G = beta_t kh_t e(t,-1) and beta_t V, transposed to
     // [channel][token] (swizzled) so that the solve reads 4 tokens at once
     {
@@ -1040,9 +1023,8 @@ __global__ __launch_bounds__(kChunkThreads) void prefill_chunk_kernel(PrefillArg
     // 2a); waited for in step 4, before its stores
     if (nx.idx >= 0) dma_taps(a, nx.h, lds + RG, wave, lane);
 
-    if constexpr (ACT == kF32) {
-        if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
-    }
+    // the next item's v, alpha and beta inputs
+    if (nx.idx >= 0) load_chunk_part<ACT, 2>(a, nx, tb, c0, in);
     // ---- 4. [W | Ut] = T (diag(beta) [K_G | V]) by block forward
     // substitution: X_b = T_bb (R_b - sum_{a<b} A_ba X_a).  Wave w owns one
     // column tile of each: u = 0 the W tile of key channels 16w..16w+15, u = 1
