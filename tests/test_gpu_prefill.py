@@ -182,6 +182,19 @@ def test_prefill_many_sequences_several_items_per_workgroup():
     check_prefill(case, full_outputs=True)
 
 
+@pytest.mark.parametrize("act", ["f32", "fp8"])
+def test_prefill_several_items_per_workgroup_other_inputs(act):
+    """FP32 and FP8 inputs with more chunk items than workgroups: each
+    workgroup requests the next item's inputs (q, k and v/alpha/beta at
+    three different steps) while it works on the current one."""
+    need_gpu()
+    rng = np.random.default_rng(41)
+    lens = [int(x) for x in rng.integers(1, 301, 24)]
+    case = wl.make_prefill(95, lens=lens, H=8, dk=128, dv=128, act=act, state="f32",
+                           init="random", slice_len=64, name=f"prefill_many_seqs_{act}")
+    check_prefill(case, full_outputs=True)
+
+
 def test_prefill_inactive_and_bad_rows_among_many():
     """Inactive sequences scattered among active ones are untouched, a bad
     slot is reported once and skipped, and the others still match."""
